@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check in __graft_entry__ and the benchmark's CPU-baseline leg may import
+this package. It is independent of the HIP library: it shares no code with it and never
+imports it. The arithmetic lives in attention.c (plain definition of attention in double
+precision); this module only marshals numpy arrays through ctypes.
+
+Parity pins (tests/test_oracle_*.py): a library routine (torch's CPU scaled-dot-product
+attention in float64 with band masks built from tril), 50-digit mpmath brute force on tiny
+inputs, closed forms (Q = 0 gives the mean of the visible V rows and LSE = ln(count)),
+invariants (rows sum to one, shift and permutation invariance, split-and-merge of keys) and
+one-hot edge probes of every mask boundary.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+
+class Oracle:
+    """ctypes handle on a built oracle library (the default one, or another build of the
+    same source, as the mutation tests use)."""
+
+    def __init__(self, path):
+        lib = ctypes.CDLL(path)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_attention_rows.argtypes = [
+            f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_long, ctypes.c_long, i64p,
+            ctypes.c_long, f64p, f64p]
+        lib.oracle_attention_rows.restype = ctypes.c_int
+        lib.oracle_decode_paged.argtypes = [
+            f32p, f32p, f32p, i32p, i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_double, f64p, f64p]
+        lib.oracle_decode_paged.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self):
+        return int(self.lib.oracle_num_threads())
+
+    def attention(self, q, k, v, scale, mask_mode=0, window=0, n_global=0, rows=None):
+        """Exact attention in fp64.
+
+        q: [B,H,Nq,d], k/v: [B,H,Nkv,d] (any float dtype; taken as exact float32 values).
+        scale: the float32 scale the device receives (upcast exactly).
+        rows: optional 1-D array of flat query-row indices ((b*H+h)*Nq + i).
+        Returns (o, lse): o [B,H,Nq,d] (or [len(rows), d]) float64, lse [B,H,Nq] (or [len]).
+        """
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        assert k.shape == (B, H, Nkv, d) and v.shape == (B, H, Nkv, d)
+        scale = float(np.float32(scale))
+        if rows is None:
+            n = B * H * Nq
+            rp = None
+        else:
+            rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+            n = rows.size
+            rp = _p(rows, ctypes.c_int64)
+        o = np.empty((n, d), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        rc = self.lib.oracle_attention_rows(
+            _p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float), B, H, Nq,
+            Nkv, d, scale, int(mask_mode), int(window), int(n_global), rp, n,
+            _p(o, ctypes.c_double), _p(lse, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_attention_rows rejected its arguments")
+        if rows is None:
+            return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+        return o, lse
+
+    def decode_paged(self, q, k_pages, v_pages, page_table, seq_lens, scale):
+        """Single-token decode against a paged cache, fp64.
+
+        q: [S,H,d]; k_pages/v_pages: [num_pages, page_size, H, d]; page_table:
+        [S, max_pages] int32; seq_lens: [S] int32. Returns (o [S,H,d], lse [S,H]) float64.
+        """
+        q, kp, vp = _f32(q), _f32(k_pages), _f32(v_pages)
+        pt = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
+        sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        S, H, d = q.shape
+        num_pages, page_size = kp.shape[0], kp.shape[1]
+        assert kp.shape == (num_pages, page_size, H, d) and vp.shape == kp.shape
+        assert pt.shape[0] == S and sl.shape == (S,)
+        o = np.empty((S, H, d), dtype=np.float64)
+        lse = np.empty((S, H), dtype=np.float64)
+        rc = self.lib.oracle_decode_paged(
+            _p(q, ctypes.c_float), _p(kp, ctypes.c_float), _p(vp, ctypes.c_float),
+            _p(pt, ctypes.c_int32), _p(sl, ctypes.c_int32), S, H, d, page_size, pt.shape[1],
+            num_pages, float(np.float32(scale)), _p(o, ctypes.c_double),
+            _p(lse, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_decode_paged rejected its arguments")
+        return o, lse
+
+
+def _f32(a):
+    """Exact float32 view of the values the device receives (fp16/bf16/fp32 all fit)."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu", torch.float32).numpy()
+    except ImportError:
+        pass
+    a = np.asarray(a)
+    if a.dtype != np.float32:
+        a = a.astype(np.float32)
+    return np.ascontiguousarray(a)
+
+
+def _p(a, t):
+    return a.ctypes.data_as(ctypes.POINTER(t))
+
+
+_default = None
+
+
+def default():
+    """The oracle built from attention.c (rebuilt when the source is newer)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def num_threads():
+    return default().num_threads()
+
+
+def attention(*args, **kw):
+    return default().attention(*args, **kw)
+
+
+def decode_paged(*args, **kw):
+    return default().decode_paged(*args, **kw)

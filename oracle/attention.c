@@ -1,0 +1,216 @@
+/*
+ * oracle/attention.c -- TEST INFRASTRUCTURE ONLY. Plain, slow, fp64 CPU reference for exact
+ * attention. Only the tests, the smoke check and the benchmark's CPU-baseline leg may load it;
+ * the product path never does. It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (the plain, materialised definition of attention, written out):
+ *   s_ij = scale * sum_c q_ic * k_jc            for every key j the mask allows, else -inf
+ *   m_i  = max_j s_ij
+ *   O_i  = sum_j exp(s_ij - m_i) v_j / sum_j exp(s_ij - m_i)
+ *   LSE_i = m_i + ln(sum_j exp(s_ij - m_i))     (natural log)
+ * Source: "ops-transformer" article on gitcode.csdn.net, section 二.1 "FlashAttention算子",
+ * the listing of conventional attention (scores = Q K^T / sqrt(d_k), softmax over keys, then
+ * the product with V). The tiled method on the same pages reaches this same result (it only
+ * avoids storing the N x N score matrix), so the oracle is this definition and not the
+ * tiled recurrence. The running-max subtraction is the numerically stable form of the same
+ * softmax (zwxr.cn article, section 6.1, "softmax_stable" remedy for score overflow).
+ *
+ * Readings where the pages are silent or ambiguous (each one is also listed in the design
+ * notes of the repository):
+ *   - layout [B, H, N, d], contiguous; LSE [B, H, Nq];
+ *   - causal keeps the diagonal (j <= i), aligned bottom-right when Nq != Nkv:
+ *     query row i sits at absolute position i' = i + (Nkv - Nq);
+ *   - sliding window + global keys ("ascend-transformer-boost" article, 场景三, sparse_config
+ *     with window_size and global_tokens): causal window of W keys including the query's own
+ *     position (i' - j < W) plus the first G key positions, still causal;
+ *   - a row with no visible key gives O = 0 and LSE = -inf.
+ *
+ * Inputs are float32 arrays that hold exactly the values the device sees (fp16 and bf16
+ * values are exactly representable in float32); every product, sum and exponential is done
+ * in double precision. No -ffast-math, no contraction into FMA (see oracle/build.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Mask predicate: is key position j visible from a query at absolute position ip?
+ * mode 0: all keys; mode 1: causal (j <= ip); mode 2: causal window of `window` keys
+ * ending at ip, plus the first `n_global` positions (still causal). */
+static int key_visible(long ip, long j, int mode, long window, long n_global)
+{
+    if (mode == 0)
+        return 1;
+    if (mode == 1)
+        return j <= ip;
+    if (mode == 2)
+        return j <= ip && ((ip - j) < window || j < n_global);
+    return 0;
+}
+
+/* One query row against `nkv` key/value rows given by pointers. `s` is scratch of nkv
+ * doubles. Writes d outputs and the row's LSE. */
+static void attend_row(const float *q, const float *const *krow, const float *const *vrow,
+                       long nkv, int d, double scale, long ip, int mode, long window,
+                       long n_global, double *s, double *out, double *lse)
+{
+    double m = -INFINITY;
+    long j;
+    int c;
+
+    for (j = 0; j < nkv; ++j) {
+        double dot = 0.0;
+        if (!key_visible(ip, j, mode, window, n_global)) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        for (c = 0; c < d; ++c)
+            dot += (double)q[c] * (double)krow[j][c];
+        s[j] = scale * dot;
+        if (s[j] > m)
+            m = s[j];
+    }
+
+    for (c = 0; c < d; ++c)
+        out[c] = 0.0;
+    if (m == -INFINITY) {
+        *lse = -INFINITY;
+        return;
+    }
+
+    {
+        double l = 0.0;
+        for (j = 0; j < nkv; ++j) {
+            double e;
+            if (!key_visible(ip, j, mode, window, n_global))
+                continue;
+            e = exp(s[j] - m);
+            l += e;
+            for (c = 0; c < d; ++c)
+                out[c] += e * (double)vrow[j][c];
+        }
+        for (c = 0; c < d; ++c)
+            out[c] /= l;
+        *lse = m + log(l);
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Attention over contiguous [B,H,N,d] tensors for a list of query rows.
+ * rows: flat indices ((b*H + h)*Nq + i); if NULL, every row in order.
+ * o: nrows x d doubles; lse: nrows doubles. Returns 0, or -1 on bad arguments / no memory.
+ */
+int oracle_attention_rows(const float *q, const float *k, const float *v, int B, int H,
+                          long Nq, long Nkv, int d, double scale, int mode, long window,
+                          long n_global, const int64_t *rows, long nrows, double *o,
+                          double *lse)
+{
+    int failed = 0;
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || mode < 0 || mode > 2)
+        return -1;
+    if (rows == NULL)
+        nrows = (long)B * H * Nq;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)Nkv);
+        const float **kp = (const float **)malloc(sizeof(float *) * (size_t)Nkv);
+        const float **vp = (const float **)malloc(sizeof(float *) * (size_t)Nkv);
+        long r;
+        if (s == NULL || kp == NULL || vp == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (r = 0; r < nrows; ++r) {
+                int64_t flat = rows ? rows[r] : (int64_t)r;
+                long i = (long)(flat % Nq);
+                long bh = (long)(flat / Nq);
+                const float *kb = k + (size_t)bh * Nkv * d;
+                const float *vb = v + (size_t)bh * Nkv * d;
+                long j;
+                for (j = 0; j < Nkv; ++j) {
+                    kp[j] = kb + (size_t)j * d;
+                    vp[j] = vb + (size_t)j * d;
+                }
+                attend_row(q + (size_t)flat * d, kp, vp, Nkv, d, scale, i + (Nkv - Nq), mode,
+                           window, n_global, s, o + (size_t)r * d, lse + r);
+            }
+        }
+        free(s);
+        free((void *)kp);
+        free((void *)vp);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * Single-token decode against a paged K/V cache ("ascend-transformer-boost" article, 场景二:
+ * the cache is cut into fixed pages of page_size tokens; a sequence's pages need not be
+ * contiguous). Pages are [num_pages, page_size, H, d]; logical token j of sequence s lives
+ * in physical page page_table[s*max_pages + j/page_size], slot j % page_size. The query is
+ * the newest token, so it sees all L_s keys. q: [S,H,d]; o: [S,H,d]; lse: [S,H].
+ * Returns 0, or -1 on bad arguments (including a page id outside [0, num_pages)).
+ */
+int oracle_decode_paged(const float *q, const float *k_pages, const float *v_pages,
+                        const int32_t *page_table, const int32_t *seq_lens, int S, int H, int d,
+                        int page_size, int max_pages, long num_pages, double scale, double *o,
+                        double *lse)
+{
+    int failed = 0;
+    long r;
+    if (S < 1 || H < 1 || d < 1 || page_size < 1 || max_pages < 1 || num_pages < 1)
+        return -1;
+    for (r = 0; r < S; ++r) {
+        long L = seq_lens[r], p;
+        if (L < 1 || L > (long)max_pages * page_size)
+            return -1;
+        for (p = 0; p < (L + page_size - 1) / page_size; ++p) {
+            int32_t id = page_table[r * max_pages + p];
+            if (id < 0 || id >= num_pages)
+                return -1;
+        }
+    }
+
+#pragma omp parallel
+    {
+        long Lmax = (long)max_pages * page_size;
+        double *s = (double *)malloc(sizeof(double) * (size_t)Lmax);
+        const float **kp = (const float **)malloc(sizeof(float *) * (size_t)Lmax);
+        const float **vp = (const float **)malloc(sizeof(float *) * (size_t)Lmax);
+        long t;
+        if (s == NULL || kp == NULL || vp == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (t = 0; t < (long)S * H; ++t) {
+                long sq = t / H, h = t % H, L = seq_lens[sq], j;
+                for (j = 0; j < L; ++j) {
+                    long page = page_table[sq * max_pages + j / page_size];
+                    size_t off = (((size_t)page * page_size + (size_t)(j % page_size)) * H + h) * d;
+                    kp[j] = k_pages + off;
+                    vp[j] = v_pages + off;
+                }
+                attend_row(q + (size_t)t * d, kp, vp, L, d, scale, L - 1, 1, 0, 0, s,
+                           o + (size_t)t * d, lse + t);
+            }
+        }
+        free(s);
+        free((void *)kp);
+        free((void *)vp);
+    }
+    return failed ? -1 : 0;
+}

@@ -1,0 +1,353 @@
+"""Pins of the fp64 oracle to facts other than itself.
+
+Each pin takes an oracle handle (oracle.default() or a deliberately broken build of the same
+source) and raises AssertionError when the oracle disagrees with:
+  * a library routine: torch's CPU scaled_dot_product_attention and logsumexp in float64,
+    with the masks built from torch.tril band offsets rather than from an index predicate;
+  * 50-digit mpmath brute force over explicitly enumerated key sets on tiny inputs;
+  * closed forms: Q = 0 makes every visible score equal, so O is the mean of the visible V
+    rows (computed from prefix sums) and LSE = ln(count), with count from its own formula;
+  * invariants: rows sum to one (V = 1 gives O = 1), a common score shift moves LSE only,
+    jointly permuting keys and values changes nothing (no mask), attention over a key split
+    merged by log-sum-exp equals attention over all keys (the multimodal split in the
+    "ascend-transformer-boost" article, 场景四, is stated to be numerically identical);
+  * one-hot probes that put a dominant score on one key and check which V row comes out, at
+    every mask edge: the causal diagonal, the key after it, the first and last key of the
+    window, the last global key and the key after it.
+Masks: 0 none, 1 causal (diagonal kept, aligned bottom-right), 2 causal window of W keys
+ending at the query plus the first G keys.
+"""
+import math
+
+import numpy as np
+import torch
+
+RNG_SEED = 1234
+
+
+def _rand(shape, seed, dtype=np.float32):
+    return np.random.default_rng(seed).standard_normal(shape).astype(dtype)
+
+
+def band_mask(Nq, Nkv, mode, W=0, G=0):
+    """Boolean [Nq, Nkv] visibility built from tril band offsets (True = visible)."""
+    delta = Nkv - Nq
+    ones = torch.ones(Nq, Nkv, dtype=torch.bool)
+    if mode == 0:
+        return ones
+    causal = torch.tril(ones, diagonal=delta)
+    if mode == 1:
+        return causal
+    window = causal & ~torch.tril(ones, diagonal=delta - W)
+    glob = causal.clone()
+    glob[:, G:] = False
+    return window | glob
+
+
+def library_attention(q, k, v, scale, mode, W=0, G=0):
+    """torch SDPA + logsumexp in float64 on the CPU (rows with no visible key excluded)."""
+    qt = torch.from_numpy(np.asarray(q, dtype=np.float64))
+    kt = torch.from_numpy(np.asarray(k, dtype=np.float64))
+    vt = torch.from_numpy(np.asarray(v, dtype=np.float64))
+    m = band_mask(qt.shape[-2], kt.shape[-2], mode, W, G)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    s = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) * scale
+    s = s.masked_fill(~m, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy(), m.numpy()
+
+
+def visible_keys(ip, Nkv, mode, W, G):
+    """Explicit visible key set for a query at absolute position ip (range arithmetic)."""
+    if mode == 0:
+        return list(range(Nkv))
+    hi = min(ip, Nkv - 1)
+    if hi < 0:
+        return []
+    if mode == 1:
+        return list(range(0, hi + 1))
+    win = set(range(max(0, ip - W + 1), hi + 1))
+    glob = set(range(0, min(G, hi + 1)))
+    return sorted(win | glob)
+
+
+def visible_count(ip, Nkv, mode, W, G):
+    """Closed-form count of visible keys (no enumeration)."""
+    if mode == 0:
+        return Nkv
+    if ip < 0:
+        return 0
+    top = min(ip, Nkv - 1) + 1
+    if mode == 1:
+        return top
+    start = max(0, ip - W + 1)
+    in_win = max(0, top - start)
+    return in_win + max(0, min(G, start, top))
+
+
+def mp_attention_row(q, krows, vrows, scale, keys):
+    import mpmath as mp
+    with mp.workdps(50):
+        sc = mp.mpf(float(scale))
+        s = {j: sc * mp.fsum(mp.mpf(float(a)) * mp.mpf(float(b)) for a, b in zip(q, krows[j]))
+             for j in keys}
+        m = max(s.values())
+        e = {j: mp.exp(s[j] - m) for j in keys}
+        l = mp.fsum(e.values())
+        o = [mp.fsum(e[j] * mp.mpf(float(vrows[j][c])) for j in keys) / l
+             for c in range(len(q))]
+        return [float(x) for x in o], float(m + mp.log(l))
+
+
+# --------------------------------------------------------------------------- pins
+
+def pin_library(orc):
+    cases = [(1, 1, 9, 9, 8, 0, 0, 0), (2, 3, 17, 17, 16, 1, 0, 0), (1, 2, 33, 33, 8, 2, 5, 3),
+             (1, 2, 40, 40, 4, 2, 1, 0), (1, 1, 12, 30, 8, 1, 0, 0), (1, 1, 12, 30, 8, 2, 7, 2),
+             (1, 2, 25, 25, 64, 2, 30, 40), (2, 1, 20, 20, 8, 0, 0, 0)]
+    for n, (B, H, Nq, Nkv, d, mode, W, G) in enumerate(cases):
+        q = _rand((B, H, Nq, d), RNG_SEED + 3 * n)
+        k = _rand((B, H, Nkv, d), RNG_SEED + 3 * n + 1)
+        v = _rand((B, H, Nkv, d), RNG_SEED + 3 * n + 2)
+        scale = float(np.float32(1 / math.sqrt(d)))
+        o, lse = orc.attention(q, k, v, scale, mode, W, G)
+        ro, rl, _ = library_attention(q, k, v, scale, mode, W, G)
+        assert np.allclose(o, ro, rtol=1e-12, atol=1e-13), f"library O mismatch case {n}"
+        assert np.allclose(lse, rl, rtol=1e-12, atol=1e-13), f"library LSE mismatch case {n}"
+
+
+def pin_mpmath(orc):
+    cases = [(1, 1, 1, 1, 0, 0, 0), (3, 3, 4, 1, 0, 0), (7, 7, 4, 2, 2, 1), (7, 7, 4, 2, 5, 3),
+             (4, 7, 2, 1, 0, 0), (5, 5, 1, 0, 0, 0), (6, 6, 8, 2, 1, 0), (16, 16, 4, 2, 5, 3)]
+    for n, case in enumerate(cases):
+        Nq, Nkv, d, mode, W, G = case[0], case[1], case[2], case[3], case[4], case[5]
+        q = _rand((1, 1, Nq, d), 77 + n) * 2
+        k = _rand((1, 1, Nkv, d), 177 + n) * 2
+        v = _rand((1, 1, Nkv, d), 277 + n)
+        scale = 0.7
+        o, lse = orc.attention(q, k, v, scale, mode, W, G)
+        for i in range(Nq):
+            keys = visible_keys(i + Nkv - Nq, Nkv, mode, W, G)
+            ro, rl = mp_attention_row(q[0, 0, i], k[0, 0], v[0, 0], np.float32(scale), keys)
+            assert np.allclose(o[0, 0, i], ro, rtol=1e-12, atol=1e-14), (n, i)
+            assert abs(lse[0, 0, i] - rl) <= 1e-12 * max(1.0, abs(rl)), (n, i)
+
+
+def pin_q_zero(orc):
+    for n, (Nq, Nkv, mode, W, G) in enumerate([(50, 50, 0, 0, 0), (50, 50, 1, 0, 0),
+                                               (20, 50, 1, 0, 0), (60, 60, 2, 8, 5),
+                                               (60, 60, 2, 1, 0), (40, 70, 2, 16, 20),
+                                               (30, 30, 2, 40, 2)]):
+        d = 8
+        q = np.zeros((1, 2, Nq, d), np.float32)
+        k = _rand((1, 2, Nkv, d), 500 + n)
+        v = _rand((1, 2, Nkv, d), 600 + n).astype(np.float64).astype(np.float32)
+        o, lse = orc.attention(q, k, v, 0.3, mode, W, G)
+        pre = np.concatenate([np.zeros((1, 2, 1, d)), np.cumsum(v.astype(np.float64), axis=2)],
+                             axis=2)
+        for i in range(Nq):
+            ip = i + Nkv - Nq
+            cnt = visible_count(ip, Nkv, mode, W, G)
+            assert abs(lse[0, :, i] - math.log(cnt)).max() < 1e-12, (n, i)
+            if mode == 0:
+                tot = pre[0, :, Nkv]
+            elif mode == 1:
+                tot = pre[0, :, ip + 1]
+            else:
+                start = max(0, ip - W + 1)
+                g_end = min(G, start)
+                tot = pre[0, :, ip + 1] - pre[0, :, start] + pre[0, :, g_end]
+            assert np.allclose(o[0, :, i], tot / cnt, rtol=1e-12, atol=1e-13), (n, i)
+
+
+def pin_causal_row0(orc):
+    for n, mode in enumerate([1, 2]):
+        q = _rand((2, 2, 30, 16), 700 + n)
+        k = _rand((2, 2, 30, 16), 710 + n)
+        v = _rand((2, 2, 30, 16), 720 + n)
+        scale = 0.25
+        o, lse = orc.attention(q, k, v, scale, mode, 4, 2)
+        assert np.array_equal(o[:, :, 0], v[:, :, 0].astype(np.float64)), "row 0 != V[0]"
+        dot = np.einsum("bhc,bhc->bh", q[:, :, 0].astype(np.float64), k[:, :, 0].astype(np.float64))
+        assert np.allclose(lse[:, :, 0], scale * dot, rtol=1e-13, atol=1e-14)
+
+
+def onehot_case(N, d, W, G, probes, c=8.0, alpha=8.0):
+    """K rows c*e_j (orthogonal, needs N <= d); Q rows alpha*e_{j*} for each probe (i, j*)."""
+    assert N <= d
+    k = np.zeros((1, 1, N, d), np.float32)
+    for j in range(N):
+        k[0, 0, j, j] = c
+    q = np.zeros((1, 1, N, d), np.float32)
+    for i, js in probes:
+        q[0, 0, i, js] = alpha
+    v = _rand((1, 1, N, d), 900)
+    return q, k, v
+
+
+def pin_onehot_edges(orc):
+    N, d, W, G = 48, 64, 8, 4
+    probes = {
+        # row: (probe key, expected visible?)
+        20: (20, True),          # causal diagonal
+        21: (22, False),         # the key after the diagonal
+        30: (30 - W + 1, True),  # first key inside the window
+        31: (31 - W, False),     # the key just outside the window (not global)
+        40: (G - 1, True),       # last global key, far outside the window
+        41: (G, False),          # first non-global key, outside the window
+        10: (10 - W + 1, True),
+        2: (2, True),
+    }
+    q, k, v = onehot_case(N, d, W, G, [(i, js) for i, (js, _) in probes.items()])
+    scale = 1.0 / 8.0  # alpha*c*scale = 8 per dominant score -> mass on one key >= 1-1e-...
+    q *= 5  # dominant score 40 (e^-40 ~ 4e-18 leakage)
+    o, lse = orc.attention(q, k, v, scale, 2, W, G)
+    for i, (js, vis) in probes.items():
+        keys = visible_keys(i, N, 2, W, G)
+        if vis:
+            assert js in keys
+            assert np.allclose(o[0, 0, i], v[0, 0, js], rtol=0, atol=1e-12), (i, js)
+            assert abs(lse[0, 0, i] - (40.0 + math.log1p((len(keys) - 1) * math.exp(-40.0)))) < 1e-12
+        else:
+            assert js not in keys
+            mean = v[0, 0, keys].astype(np.float64).mean(axis=0)
+            assert np.allclose(o[0, 0, i], mean, rtol=1e-12, atol=1e-13), (i, js)
+            assert abs(lse[0, 0, i] - math.log(len(keys))) < 1e-12
+    # causal mode: the diagonal is visible, the key after it is not
+    q2, k2, v2 = onehot_case(N, d, W, G, [(5, 5), (6, 7)])
+    q2 *= 5
+    o2, _ = orc.attention(q2, k2, v2, scale, 1)
+    assert np.allclose(o2[0, 0, 5], v2[0, 0, 5], atol=1e-12)
+    assert np.allclose(o2[0, 0, 6], v2[0, 0, :7].astype(np.float64).mean(axis=0), atol=1e-12)
+    # no mask: a dominant key past the diagonal is still selected
+    o3, _ = orc.attention(q2, k2, v2, scale, 0)
+    assert np.allclose(o3[0, 0, 6], v2[0, 0, 7], atol=1e-12)
+
+
+def pin_rows_sum_to_one(orc):
+    for mode in (0, 1, 2):
+        q = _rand((1, 3, 40, 16), 1000 + mode) * 3
+        k = _rand((1, 3, 40, 16), 1010 + mode) * 3
+        v = np.ones((1, 3, 40, 16), np.float32)
+        o, _ = orc.attention(q, k, v, 0.5, mode, 5, 3)
+        assert np.allclose(o, 1.0, rtol=0, atol=1e-14)
+
+
+def pin_shift(orc):
+    d, N = 16, 25
+    q = _rand((1, 2, N, d), 1100)
+    k = _rand((1, 2, N, d), 1101)
+    v = _rand((1, 2, N, d), 1102)
+    scale = 0.25
+    for mode in (0, 1, 2):
+        o0, l0 = orc.attention(q, k, v, scale, mode, 6, 2)
+        for c in (-800.0, 800.0):
+            qe = np.float32(c / scale)
+            q2 = np.concatenate([q, np.full((1, 2, N, 1), qe, np.float32)], axis=-1)
+            k2 = np.concatenate([k, np.ones((1, 2, N, 1), np.float32)], axis=-1)
+            v2 = np.concatenate([v, np.zeros((1, 2, N, 1), np.float32)], axis=-1)
+            o1, l1 = orc.attention(q2, k2, v2, scale, mode, 6, 2)
+            shift = scale * float(qe)
+            assert np.all(np.isfinite(o1)) and np.all(np.isfinite(l1))
+            assert np.allclose(o1[..., :d], o0, rtol=1e-10, atol=1e-10)
+            assert np.allclose(l1 - shift, l0, rtol=0, atol=1e-9)
+
+
+def pin_permutation(orc):
+    q = _rand((2, 2, 19, 8), 1200)
+    k = _rand((2, 2, 31, 8), 1201)
+    v = _rand((2, 2, 31, 8), 1202)
+    perm = np.random.default_rng(5).permutation(31)
+    o0, l0 = orc.attention(q, k, v, 0.4, 0)
+    o1, l1 = orc.attention(q, k[:, :, perm], v[:, :, perm], 0.4, 0)
+    assert np.allclose(o0, o1, rtol=1e-13, atol=1e-14)
+    assert np.allclose(l0, l1, rtol=1e-13, atol=1e-14)
+
+
+def pin_split_merge(orc):
+    q = _rand((1, 2, 13, 8), 1300) * 2
+    k = _rand((1, 2, 40, 8), 1301) * 2
+    v = _rand((1, 2, 40, 8), 1302)
+    o, l = orc.attention(q, k, v, 0.6, 0)
+    oa, la = orc.attention(q, k[:, :, :17], v[:, :, :17], 0.6, 0)
+    ob, lb = orc.attention(q, k[:, :, 17:], v[:, :, 17:], 0.6, 0)
+    lm = np.logaddexp(la, lb)
+    om = np.exp(la - lm)[..., None] * oa + np.exp(lb - lm)[..., None] * ob
+    assert np.allclose(lm, l, rtol=1e-13, atol=1e-13)
+    assert np.allclose(om, o, rtol=1e-12, atol=1e-13)
+
+
+def pin_mask_reductions(orc):
+    q = _rand((1, 2, 24, 8), 1400)
+    k = _rand((1, 2, 24, 8), 1401)
+    v = _rand((1, 2, 24, 8), 1402)
+    oc, lc = orc.attention(q, k, v, 0.35, 1)
+    for W, G in ((24, 0), (1000, 3), (1, 24), (5, 1000)):
+        ow, lw = orc.attention(q, k, v, 0.35, 2, W, G)
+        assert np.array_equal(ow, oc) and np.array_equal(lw, lc), (W, G)
+    o1, l1 = orc.attention(q, k[:, :, :1], v[:, :, :1], 0.35, 0)
+    assert np.array_equal(o1, np.broadcast_to(v[:, :, :1].astype(np.float64), o1.shape))
+    # window of one key and no global keys: every row sees only itself
+    ow, _ = orc.attention(q, k, v, 0.35, 2, 1, 0)
+    assert np.array_equal(ow, v.astype(np.float64))
+
+
+def pin_empty_rows(orc):
+    # more queries than keys with bottom-right causal: the first Nq-Nkv rows see nothing
+    q = _rand((1, 1, 10, 8), 1500)
+    k = _rand((1, 1, 4, 8), 1501)
+    v = _rand((1, 1, 4, 8), 1502)
+    o, l = orc.attention(q, k, v, 0.35, 1)
+    assert np.all(o[0, 0, :6] == 0) and np.all(np.isneginf(l[0, 0, :6]))
+    assert np.array_equal(o[0, 0, 6], v[0, 0, 0].astype(np.float64))
+    assert np.all(np.isfinite(l[0, 0, 6:]))
+
+
+def make_paged(k, v, page_size, seed, spare=2):
+    """Scatter contiguous per-sequence K/V [S][L_s,H,d] into a permuted page pool."""
+    rng = np.random.default_rng(seed)
+    S = len(k)
+    H, d = k[0].shape[1], k[0].shape[2]
+    npg = [(x.shape[0] + page_size - 1) // page_size for x in k]
+    total = sum(npg) + spare
+    perm = rng.permutation(total)
+    kp = np.full((total, page_size, H, d), np.nan, np.float32)
+    vp = np.full((total, page_size, H, d), np.nan, np.float32)
+    pt = np.full((S, max(npg)), -1, np.int32)
+    n = 0
+    for s in range(S):
+        for p in range(npg[s]):
+            pid = perm[n]
+            n += 1
+            pt[s, p] = pid
+            seg_k = k[s][p * page_size:(p + 1) * page_size]
+            kp[pid, :seg_k.shape[0]] = seg_k
+            vp[pid, :seg_k.shape[0]] = v[s][p * page_size:(p + 1) * page_size]
+    return kp, vp, pt
+
+
+def pin_decode(orc):
+    H, d, ps = 3, 8, 16
+    lens = [1, 16, 17, 40, 64]
+    q = _rand((len(lens), H, d), 1600)
+    ks = [_rand((L, H, d), 1610 + i) for i, L in enumerate(lens)]
+    vs = [_rand((L, H, d), 1620 + i) for i, L in enumerate(lens)]
+    kp, vp, pt = make_paged(ks, vs, ps, 7)
+    o, l = orc.decode_paged(q, kp, vp, pt, np.array(lens, np.int32), 0.3)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    for s, L in enumerate(lens):
+        # contiguous [1,H,L,d] against the same query: same result as the paged lookup
+        kc = np.ascontiguousarray(ks[s].transpose(1, 0, 2))[None]
+        vc = np.ascontiguousarray(vs[s].transpose(1, 0, 2))[None]
+        ro, rl, _ = library_attention(q[s][None, :, None, :], kc, vc, float(np.float32(0.3)), 0)
+        assert np.allclose(o[s], ro[0, :, 0], rtol=1e-12, atol=1e-13), s
+        assert np.allclose(l[s], rl[0, :, 0], rtol=1e-12, atol=1e-13), s
+    # a different physical placement gives bit-identical results
+    kp2, vp2, pt2 = make_paged(ks, vs, ps, 8, spare=5)
+    o2, l2 = orc.decode_paged(q, kp2, vp2, pt2, np.array(lens, np.int32), 0.3)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+ALL_PINS = [pin_library, pin_mpmath, pin_q_zero, pin_causal_row0, pin_onehot_edges,
+            pin_rows_sum_to_one, pin_shift, pin_permutation, pin_split_merge,
+            pin_mask_reductions, pin_empty_rows, pin_decode]

@@ -1,0 +1,115 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
+
+This module only draws random numbers and lays them out; it holds none of the attention
+arithmetic. Both the HIP path and the oracle consume exactly the tensors it returns.
+
+Recipe (every draw from one torch CPU generator seeded per workload):
+  * prefill: Q, K, V drawn in that order as float32 standard normals of shape [B,H,N,d],
+    optionally multiplied by an exact power of two in float32, then cast to the run's dtype
+    (round to nearest even);
+  * paged decode: Q [S,H,d], then the S sequence lengths uniform in [len_lo, len_hi], then a
+    random permutation of the physical page ids, then the K and V page pools
+    [num_pages, page_size, H, d]. Slots past a sequence's length in its last page and the
+    spare pages hold NaN, so a kernel that reads them without masking shows it.
+
+The workloads stand in for the shapes the pages report (the pages' LLaMA-7B, BERT and long
+document runs need weights and datasets that are not used here).
+"""
+import math
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+# name -> workload description. mask: 0 none, 1 causal, 2 causal sliding window + global keys.
+WORKLOADS = {
+    "tiny_f32": dict(kind="prefill", B=1, H=2, Nq=128, Nkv=128, d=64, dtype="f32", mask=0,
+                     window=0, n_global=0, input_scale=1.0, seed=1),
+    "dense_f16": dict(kind="prefill", B=4, H=32, Nq=1024, Nkv=1024, d=128, dtype="f16",
+                      mask=0, window=0, n_global=0, input_scale=1.0, seed=2),
+    "dense_bf16": dict(kind="prefill", B=4, H=32, Nq=1024, Nkv=1024, d=128, dtype="bf16",
+                       mask=0, window=0, n_global=0, input_scale=1.0, seed=2),
+    "causal_bf16": dict(kind="prefill", B=4, H=32, Nq=4096, Nkv=4096, d=128, dtype="bf16",
+                        mask=1, window=0, n_global=0, input_scale=0.5, seed=3),
+    "window_bf16": dict(kind="prefill", B=1, H=32, Nq=32768, Nkv=32768, d=128, dtype="bf16",
+                        mask=2, window=2048, n_global=64, input_scale=1.0, seed=4),
+    "decode_f16": dict(kind="decode", S=8, H=32, d=128, dtype="f16", page_size=256,
+                       len_lo=4096, len_hi=8192, max_len=8192, spare_pages=4, seed=5),
+}
+
+
+def default_scale(d):
+    """The float32 value of 1/sqrt(d) that both sides receive."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def gen_prefill(B, H, Nq, Nkv, d, dtype, seed, input_scale=1.0):
+    """Q [B,H,Nq,d], K and V [B,H,Nkv,d] on the CPU in `dtype` ("f32", "f16", "bf16")."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, Nkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, Nkv, d), generator=g, dtype=torch.float32)
+    if input_scale != 1.0:
+        q.mul_(input_scale)
+        k.mul_(input_scale)
+        v.mul_(input_scale)
+    t = DTYPES[dtype]
+    return q.to(t), k.to(t), v.to(t)
+
+
+def gen_decode(S, H, d, dtype, seed, page_size=256, len_lo=4096, len_hi=8192, max_len=None,
+               spare_pages=4, lens=None):
+    """Paged decode inputs.
+
+    Returns dict with q [S,H,d], k_pages/v_pages [P,page_size,H,d] (dtype), page_table
+    [S,max_pages] int32 (-1 where unused), seq_lens [S] int32. `lens` overrides the drawn
+    lengths (the draw still happens so the rest of the stream is unchanged).
+    """
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    t = DTYPES[dtype]
+    q = torch.randn((S, H, d), generator=g, dtype=torch.float32)
+    drawn = torch.randint(len_lo, len_hi + 1, (S,), generator=g, dtype=torch.int64)
+    L = drawn if lens is None else torch.as_tensor(lens, dtype=torch.int64)
+    if max_len is None:
+        max_len = int(L.max())
+    max_pages = (max_len + page_size - 1) // page_size
+    pages_per_seq = [(int(x) + page_size - 1) // page_size for x in L]
+    assert max(pages_per_seq) <= max_pages
+    used = sum(pages_per_seq)
+    total = used + int(spare_pages)
+    perm = torch.randperm(total, generator=g)
+    k_pages = torch.randn((total, page_size, H, d), generator=g, dtype=torch.float32)
+    v_pages = torch.randn((total, page_size, H, d), generator=g, dtype=torch.float32)
+    page_table = torch.full((S, max_pages), -1, dtype=torch.int32)
+    nxt = 0
+    nan = float("nan")
+    for s in range(S):
+        for p in range(pages_per_seq[s]):
+            pid = int(perm[nxt])
+            nxt += 1
+            page_table[s, p] = pid
+        tail = int(L[s]) - (pages_per_seq[s] - 1) * page_size
+        last = int(page_table[s, pages_per_seq[s] - 1])
+        k_pages[last, tail:] = nan
+        v_pages[last, tail:] = nan
+    for i in range(used, total):
+        k_pages[int(perm[i])] = nan
+        v_pages[int(perm[i])] = nan
+    return dict(q=q.to(t), k_pages=k_pages.to(t), v_pages=v_pages.to(t),
+                page_table=page_table, seq_lens=L.to(torch.int32), page_size=page_size,
+                max_pages=max_pages)
+
+
+def gen_workload(name, **override):
+    """Inputs of a named workload (overrides replace any field, e.g. a smaller N)."""
+    w = dict(WORKLOADS[name])
+    w.update(override)
+    if w["kind"] == "prefill":
+        q, k, v = gen_prefill(w["B"], w["H"], w["Nq"], w["Nkv"], w["d"], w["dtype"], w["seed"],
+                              w.get("input_scale", 1.0))
+        return w, dict(q=q, k=k, v=v)
+    inp = gen_decode(w["S"], w["H"], w["d"], w["dtype"], w["seed"], w["page_size"],
+                     w["len_lo"], w["len_hi"], w.get("max_len"), w.get("spare_pages", 4),
+                     w.get("lens"))
+    return w, inp
