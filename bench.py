@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled exact attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_bf16]
+
+One step is one call of the tiled attention forward (query-tile decomposition, Q load, K/V
+tile stream, QK^T, scale and mask, online softmax, PV and the epilogue) over the dense bf16
+workload B=4 H=32 N=1024 d=128, the configuration the throughput metric is quoted on. The
+other workloads (fp16 dense, causal, sliding window + global keys, paged decode) are timed in
+the same run and reported under "workloads". Prints one JSON line.
+
+Throughput counts 4*d FLOPs per visible (query, key) pair (QK^T and PV), with the exact pair
+count of the mask (not whole tiles); decode counts algorithmic HBM bytes (K and V of every
+visible key, the query, the output). Kernel durations come from HIP events recorded on the
+stream the kernels run on. The oracle (fp64, CPU) is timed on a bounded sample of the same
+workload as a reported baseline.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PAGES_BF16_TFLOPS = 1.25    # pages' Ascend 910 bf16 time for this workload, as TFLOP/s
+KERNEL_SOURCES = ["tiled_exact_attention_forward_amd/csrc/fa_fwd.hip",
+                  "tiled_exact_attention_forward_amd/csrc/fa_decode.hip"]
+
+
+# ----------------------------------------------------------------- accounting
+
+def score_matrix_bytes(B, H, N, elem_bytes):
+    """Bytes of a materialised N x N score matrix per (batch, head)."""
+    return B * H * N * N * elem_bytes
+
+
+def tile_bytes(rows, cols, elem_bytes, tiles=1):
+    return rows * cols * elem_bytes * tiles
+
+
+def visible_counts(Nq, Nkv, mode, W=0, G=0):
+    """Visible keys of every query row (closed form, vectorised over rows)."""
+    ip = np.arange(Nq, dtype=np.int64) + (Nkv - Nq)
+    if mode == 0:
+        return np.full(Nq, Nkv, dtype=np.int64)
+    top = np.clip(np.minimum(ip, Nkv - 1) + 1, 0, None)
+    if mode == 1:
+        return top
+    start = np.maximum(0, ip - W + 1)
+    in_win = np.maximum(0, top - start)
+    glob = np.maximum(0, np.minimum(np.minimum(G, start), top))
+    return in_win + glob
+
+
+def prefill_flops(w):
+    pairs = int(visible_counts(w["Nq"], w["Nkv"], w["mask"], w["window"], w["n_global"]).sum())
+    return 4 * w["d"] * pairs * w["B"] * w["H"], pairs * w["B"] * w["H"]
+
+
+def prefill_bytes(w, elem):
+    return elem * w["B"] * w["H"] * w["d"] * (2 * w["Nq"] + 2 * w["Nkv"]) + 4 * w["B"] * w["H"] * w["Nq"]
+
+
+def decode_bytes(w, seq_lens, elem):
+    keys = int(np.asarray(seq_lens, dtype=np.int64).sum())
+    return 2 * keys * w["H"] * w["d"] * elem + 2 * w["S"] * w["H"] * w["d"] * elem + 4 * w["S"] * w["H"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key):
+    """HBM traffic per launch measured with rocprofv3 counters, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    e = t.get("kernels", {}).get(kernel_key)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------- timing
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall
+
+
+def bench_prefill(name, steps, warmup, torch, fa, workloads):
+    w, inp = workloads.gen_workload(name)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = workloads.default_scale(w["d"])
+
+    def step():
+        fa.fa_forward(q, k, v, scale, w["mask"], w["window"], w["n_global"], out=o, lse=lse)
+
+    ms, wall = time_calls(step, steps, warmup, torch)
+    flops, pairs = prefill_flops(w)
+    elem = q.element_size()
+    return dict(workload=name, w=w, ms=ms, wall_s=wall, flops=flops, pairs=pairs,
+                tflops=flops / (ms * 1e-3) / 1e12, bytes=prefill_bytes(w, elem), inputs=inp)
+
+
+def bench_decode(name, steps, warmup, torch, fa, workloads):
+    w, inp = workloads.gen_workload(name)
+    dev = torch.device("cuda:0")
+    q, kp, vp, pt, sl = (inp[x].to(dev) for x in ("q", "k_pages", "v_pages", "page_table",
+                                                  "seq_lens"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    need = fa.fa_decode_paged_workspace_bytes(w["S"], w["H"], w["d"], pt.shape[1], w["page_size"])
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    scale = workloads.default_scale(w["d"])
+
+    def step():
+        fa.fa_decode_paged(q, kp, vp, pt, sl, scale, out=o, lse=lse, workspace=ws)
+
+    ms, wall = time_calls(step, steps, warmup, torch)
+    nbytes = decode_bytes(w, inp["seq_lens"], q.element_size())
+    return dict(workload=name, w=w, ms=ms, wall_s=wall, bytes=nbytes,
+                gbs=nbytes / (ms * 1e-3) / 1e9, seq_lens=[int(x) for x in inp["seq_lens"]])
+
+
+def cpu_baseline(res, budget_s):
+    """fp64 oracle on a bounded, evenly spaced sample of the workload's query rows."""
+    import oracle
+    w, inp = res["w"], res["inputs"]
+    total_rows = w["B"] * w["H"] * w["Nq"]
+    scale = float(np.float32(1.0 / math.sqrt(w["d"])))
+    counts = visible_counts(w["Nq"], w["Nkv"], w["mask"], w["window"], w["n_global"])
+
+    def run(n):
+        rows = np.unique(np.linspace(0, total_rows - 1, n).astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.attention(inp["q"], inp["k"], inp["v"], scale, w["mask"], w["window"],
+                         w["n_global"], rows=rows)
+        dt = time.perf_counter() - t0
+        flops = 4 * w["d"] * int(counts[rows % w["Nq"]].sum())
+        return rows.size, dt, flops
+
+    n, dt, _ = run(min(512, total_rows))
+    target = int(min(total_rows, max(512, n * budget_s / max(dt, 1e-3))))
+    n, dt, flops = run(target)
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
+                kind="oracle", seconds=dt,
+                sample=f"{n} of {total_rows} query rows (evenly spaced over batch, head, row) "
+                       f"of {res['workload']}, fp64 C oracle with OpenMP")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dense_bf16")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="skip the other workloads and the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path has no multi-GPU sharding in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_exact_attention_forward_amd as fa
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()
+
+    head = bench_prefill(args.workload, args.steps, args.warmup, torch, fa, workloads)
+    print(f"[bench] {args.workload}: {head['ms'] * 1e3:.1f} us/step, "
+          f"{head['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    others = {}
+    if not args.only_headline:
+        for name in ("dense_f16", "dense_bf16", "causal_bf16", "window_bf16"):
+            if name == args.workload:
+                continue
+            r = bench_prefill(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch, fa,
+                              workloads)
+            others[name] = dict(us=round(r["ms"] * 1e3, 2), tflops=round(r["tflops"], 2),
+                                frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                visible_pairs=r["pairs"])
+            print(f"[bench] {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
+        d = bench_decode("decode_f16", max(10, args.steps // 4), max(3, args.warmup // 4), torch,
+                         fa, workloads)
+        others["decode_f16"] = dict(us=round(d["ms"] * 1e3, 2), gbs=round(d["gbs"], 1),
+                                    frac_hbm_peak=round(d["gbs"] / PEAK_HBM_GBS, 4),
+                                    bytes=d["bytes"], seq_lens=d["seq_lens"],
+                                    note="split + combine kernels, L2/MALL not flushed")
+        print(f"[bench] decode_f16: {d['ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+
+    base = None
+    if not args.no_cpu_baseline and not args.only_headline:
+        base = cpu_baseline(head, args.cpu_seconds)
+        print(f"[bench] cpu oracle: {base['value'] * 1e3:.2f} GFLOP/s on {base['cores']} threads",
+              file=sys.stderr, flush=True)
+
+    w = head["w"]
+    achieved = head["flops"] / (head["ms"] * 1e-3) / 1e12
+    kernel_key = f"fwd16_bf16_d{w['d']}_mask{w['mask']}_{args.workload}"
+    line = {
+        "metric": "attention fwd TFLOP/s & % bf16 MFMA peak; paged-decode HBM GB/s",
+        "value": round(head["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(head["tflops"] / PAGES_BF16_TFLOPS, 2)
+        if args.workload == "dense_bf16" else None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={w['B']} H={w['H']} Nq={w['Nq']} "
+                               f"Nkv={w['Nkv']} d={w['d']} mask={w['mask']}",
+                   "global_batch": w["B"], "seq_len": w["Nq"], "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(kernel_key),
+                     "kernel": "fwd16_kernel<bf16, 128, mask none>",
+                     "flops_per_launch": head["flops"],
+                     "algorithmic_bytes_per_launch": head["bytes"]},
+        "cpu_baseline": None if base is None else {
+            k: (round(v, 6) if isinstance(v, float) else v) for k, v in base.items()},
+        "workloads": others,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

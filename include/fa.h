@@ -1,0 +1,127 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) tiled exact attention library (libteaf.so).
+ *
+ * Tiled exact attention computes O = softmax(Q K^T * scale + mask) V one query tile at a
+ * time, streaming key/value tiles through on-chip memory and keeping a running maximum and
+ * running sum per query row (online softmax), so the N x N score matrix never reaches HBM.
+ * Sources: "ops-transformer" article (gitcode.csdn.net), section 二.1 "FlashAttention算子"
+ * (conventional attention listing; tiled loop over Q blocks and K/V blocks with an online
+ * softmax update and one final normalisation); zwxr.cn article on ops-transformer, section
+ * 3.1 (running max m and normaliser l per row; fp16 scores with an fp32 softmax
+ * denominator; prefetch of the next K/V block while the current one is computed).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (HIP device memory) owned by the caller. The
+ *    library allocates nothing, keeps no global mutable state and is thread-safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). All work is
+ *    enqueued on it; calls return before the work completes.
+ *  - Return value: FA_OK (0) or a negative fa_status. Argument checks run on the host BEFORE
+ *    any launch; on error nothing is launched and no output is written. A launch failure is
+ *    reported as FA_ERR_HIP. Faults inside a kernel surface at the caller's next
+ *    synchronisation, as for any HIP work.
+ *  - Contents of device buffers (page tables, sequence lengths) cannot be checked on the
+ *    host; out-of-range values there are undefined behaviour.
+ */
+#ifndef TEAF_FA_H
+#define TEAF_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,       /* a size is out of range (B, H, N < 1, window < 1, ...) */
+    FA_ERR_UNSUPPORTED = -3, /* valid but not built: head dim, dtype, mask, page size */
+    FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query function says */
+    FA_ERR_HIP = -5          /* the HIP runtime refused a launch */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/* Masks. Query row i of Nq sits at absolute position i' = i + (Nkv - Nq) (bottom-right
+ * alignment, so a single decode query sees every key). Key j is visible when
+ *   FA_MASK_NONE          : always;
+ *   FA_MASK_CAUSAL        : j <= i'  (the diagonal is kept);
+ *   FA_MASK_WINDOW_GLOBAL : j <= i' and (i' - j < window or j < n_global).
+ * The causal mask follows the LLaMA deployment in the ops-transformer article (section 四,
+ * FlashAttention(causal=True): each token sees only earlier tokens and itself). The window
+ * mask follows the sparse_config of the ascend-transformer-boost article (场景三:
+ * sliding_window mode, window_size 2048, 64 global tokens such as BOS), read as a causal
+ * window of `window` keys ending at the query plus the first `n_global` key positions. */
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW_GLOBAL = 2 } fa_mask;
+
+/*
+ * fa_forward -- tiled exact attention forward pass.
+ *
+ *  q    [B, H, Nq,  d]  dtype, contiguous (row-major, d fastest)
+ *  k    [B, H, Nkv, d]  dtype, contiguous
+ *  v    [B, H, Nkv, d]  dtype, contiguous
+ *  o    [B, H, Nq,  d]  dtype, written
+ *  lse  [B, H, Nq]      float32, written: natural-log log-sum-exp of the scaled visible
+ *                       scores of each row (-inf for a row with no visible key, whose O
+ *                       row is then 0). Required (not NULL).
+ *  scale       multiplies Q K^T (normally 1/sqrt(d)).
+ *  mask_mode   fa_mask; window >= 1 and n_global >= 0 are required for
+ *              FA_MASK_WINDOW_GLOBAL and ignored otherwise.
+ *  dtype       fa_dtype of q, k, v and o. Scores, softmax statistics and the output
+ *              accumulator are float32 for every dtype; for fp16/bf16 the probabilities
+ *              are rounded to the input dtype before the product with V.
+ *  Supported: d in {64, 128}; any B, H, Nq, Nkv >= 1 (no padding needed; tails are
+ *  masked inside the kernel); B*H < 2^31 and every tensor < 2^31 elements per (b, h).
+ *  q, k, v, o need 16-byte alignment.
+ */
+int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int Nq, int Nkv, int d, float scale, int mask_mode, int window, int n_global,
+               int dtype, void *stream);
+
+/*
+ * Paged single-token decode ("ascend-transformer-boost" article, 场景二: KV cache split
+ * into fixed pages of 256 tokens, a new page per overflow, no reallocation; the attention
+ * reads history K/V through the page layout). Each sequence has one query token at the
+ * newest position, which sees all of its seq_lens[s] keys.
+ *
+ *  q           [S, H, d]                                  dtype
+ *  k_pages     [num_pages, page_size, H, d]               dtype (physical page pool)
+ *  v_pages     [num_pages, page_size, H, d]               dtype
+ *  page_table  [S, max_pages_per_seq] int32, row-major: logical page p of sequence s is
+ *              physical page page_table[s*max_pages_per_seq + p]; only the first
+ *              ceil(seq_lens[s]/page_size) entries of a row are read.
+ *  seq_lens    [S] int32, each in [1, max_pages_per_seq*page_size]
+ *  o           [S, H, d]                                  dtype, written
+ *  lse         [S, H] float32, written; may be NULL.
+ *  workspace   device buffer of at least fa_decode_paged_workspace_bytes(...) bytes for
+ *              the per-split partial results (split-KV); contents need no initialisation.
+ *  Supported: page_size == 256, d == 128, dtype FA_F16 or FA_BF16, H a multiple of 8.
+ *  The kernels never read page slots at or past seq_lens[s], nor unused table entries.
+ *  Two kernels run on `stream`: the split pass writes partial (O, LSE) per split of
+ *  the keys; the combine pass merges them by log-sum-exp and writes o and lse.
+ */
+size_t fa_decode_paged_workspace_bytes(int num_seqs, int H, int d, int max_pages_per_seq,
+                                       int page_size);
+
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *page_table, const int32_t *seq_lens, void *o, float *lse,
+                    int page_size, int num_seqs, int H, int d, int max_pages_per_seq,
+                    int num_pages, float scale, int dtype, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *fa_status_string(int status);
+
+/* Text of the HIP error behind the calling thread's most recent FA_ERR_HIP ("no error" if
+ * none). The pointer is static; the text stays valid until the thread's next failing call. */
+const char *fa_last_hip_error(void);
+
+/* Library ABI version: major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TEAF_FA_H */

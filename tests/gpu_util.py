@@ -1,0 +1,87 @@
+"""Helpers for the GPU parity tests: device transfer, tolerances and sampled rows.
+
+Tolerances (stated once, used by every GPU parity test):
+  * fp16 / bf16 outputs: max |O_gpu - O_ref| <= 1e-2 over every compared element and
+    max |LSE_gpu - LSE_ref| <= 1e-3 (the stated bar). Because that bar is loose for
+    outputs of size ~0.05, the relative L2 error ||O_gpu - O_ref|| / ||O_ref|| is also gated:
+    <= 8e-3 (bf16) and <= 2e-3 (fp16). Rounding P and O to the 16-bit type each adds a
+    relative error of at most 2^-9 (bf16) / 2^-12 (fp16), i.e. about 2e-3 / 2.5e-4 rms.
+  * fp32: normwise relative, max |O_gpu - O_ref| <= 1e-5 * max |O_ref|, and
+    |LSE_gpu - LSE_ref| <= 1e-5 * max(1, |LSE_ref|).
+The reference is the fp64 oracle on exactly the values the GPU received; it is not rounded
+to the output type (the tolerance absorbs that rounding).
+"""
+import numpy as np
+import torch
+
+import oracle
+
+O_ABS = 1e-2
+LSE_ABS = 1e-3
+REL_L2 = {"bf16": 8e-3, "f16": 2e-3}
+F32_REL = 1e-5
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU test run without a visible GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(*ts):
+    dev = require_gpu()
+    return [t.to(dev).contiguous() for t in ts]
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def errors(o_gpu, lse_gpu, o_ref, lse_ref):
+    og, lg = f64(o_gpu), f64(lse_gpu)
+    o_ref = np.asarray(o_ref, np.float64).reshape(og.shape)
+    lse_ref = np.asarray(lse_ref, np.float64).reshape(lg.shape)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lg), fin), "LSE finiteness differs"
+    diff = np.abs(og - o_ref)
+    return dict(
+        o_max_abs=float(diff.max()) if diff.size else 0.0,
+        o_ref_max=float(np.abs(o_ref).max()) if o_ref.size else 0.0,
+        o_rel_l2=float(np.linalg.norm(og - o_ref) / max(np.linalg.norm(o_ref), 1e-300)),
+        lse_max_abs=float(np.abs(lg[fin] - lse_ref[fin]).max()) if fin.any() else 0.0,
+        lse_rel=float((np.abs(lg[fin] - lse_ref[fin]) / np.maximum(1, np.abs(lse_ref[fin]))).max())
+        if fin.any() else 0.0,
+        nan=bool(np.isnan(og).any() or np.isnan(lg[fin]).any()),
+    )
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
+    e = errors(o_gpu, lse_gpu, o_ref, lse_ref)
+    assert not e["nan"], f"{label}: NaN in output {e}"
+    if dtype == "f32":
+        assert e["o_max_abs"] <= F32_REL * e["o_ref_max"], f"{label}: {e}"
+        assert e["lse_rel"] <= F32_REL, f"{label}: {e}"
+    else:
+        assert e["o_max_abs"] <= O_ABS, f"{label}: {e}"
+        assert e["lse_max_abs"] <= LSE_ABS, f"{label}: {e}"
+        assert e["o_rel_l2"] <= REL_L2[dtype], f"{label}: {e}"
+    return e
+
+
+def sample_rows(B, H, Nq, tile_edges=(0, 1, 2, 31, 32, 63, 64, 127, 128, 129), extra=(),
+                per_head=16, seed=0):
+    """Flat row ids ((b*H+h)*Nq + i): fixed edge rows in every (b,h) plus random rows."""
+    rng = np.random.default_rng(seed)
+    fixed = sorted({i for i in list(tile_edges) + list(extra) + [Nq - 1, Nq - 2] if 0 <= i < Nq})
+    rows = []
+    for bh in range(B * H):
+        pick = set(fixed) | set(rng.integers(0, Nq, per_head).tolist())
+        rows.extend(bh * Nq + i for i in sorted(pick))
+    return np.array(rows, dtype=np.int64)
+
+
+def gather_rows(o, lse, rows):
+    d = o.shape[-1]
+    of = o.reshape(-1, d)[torch.as_tensor(rows, device=o.device)]
+    lf = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
+    return of, lf

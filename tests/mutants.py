@@ -1,0 +1,35 @@
+"""Plausible mistakes planted in a copy of the oracle source (for sensitivity tests).
+
+Each entry replaces one unique snippet of oracle/attention.c. The copy is built with gcc on
+the CPU into a temporary library; the real oracle is never modified.
+"""
+import oracle
+from oracle import build as obuild
+
+MUTANTS = {
+    "causal_strict": ("return j <= ip;", "return j < ip;"),
+    "window_inclusive": ("(ip - j) < window", "(ip - j) <= window"),
+    "global_inclusive": ("j < n_global", "j <= n_global"),
+    "window_not_causal": ("return j <= ip && ((ip - j)", "return j <= ip + 1 && ((ip - j)"),
+    "no_max_subtraction": ("e = exp(s[j] - m);", "e = exp(s[j]);"),
+    "lse_drops_max": ("*lse = m + log(l);", "*lse = log(l);"),
+    "value_as_key": ("(double)krow[j][c];", "(double)vrow[j][c];"),
+    "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "query_index": ("dot += (double)q[c]", "dot += (double)q[0]"),
+    "no_normalise": ("out[c] /= l;", "out[c] /= (l + 1.0);"),
+    "top_left_causal": ("i + (Nkv - Nq), mode", "i, mode"),
+    "page_slot": ("(size_t)(j % page_size)", "(size_t)((j + 1) % page_size)"),
+    "decode_head": ("* H + h) * d;", "* H + 0) * d;"),
+    "max_ignores_first": ("if (s[j] > m)", "if (j > 0 && s[j] > m)"),
+}
+
+
+def build_mutant(name, tmpdir):
+    before, after = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(before) == 1, f"mutation site for {name} not unique"
+    path = f"{tmpdir}/mutant_{name}.c"
+    with open(path, "w") as f:
+        f.write(src.replace(before, after))
+    lib = obuild.build(path, f"{tmpdir}/libmutant_{name}.so")
+    return oracle.Oracle(lib)

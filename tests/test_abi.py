@@ -1,0 +1,98 @@
+"""C ABI of libteaf.so on the CPU: the library loads, exports every declared entry point, and
+rejects invalid arguments with the documented status before touching the GPU.
+
+No test here passes arguments that would reach a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_exact_attention_forward_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# A fake, 16-byte aligned, non-null "device pointer". Every call below is rejected by the
+# host-side checks before it could be used.
+P = ctypes.c_void_p(0x1000)
+N = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert fa.fa_status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert fa.fa_status_string(s) and fa.fa_status_string(s) != "unknown status"
+    assert fa.fa_status_string(42) == "unknown status"
+    assert fa.fa_version() >= 10000
+
+
+def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nkv=8, d=64, scale=0.125, mask=0, W=0, G=0,
+        dtype=1):
+    return fa.load_library().fa_forward(q, k, v, o, lse, B, H, Nq, Nkv, d, scale, mask, W, G,
+                                        dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=N), fa.FA_ERR_NULL), (dict(k=N), fa.FA_ERR_NULL), (dict(v=N), fa.FA_ERR_NULL),
+    (dict(o=N), fa.FA_ERR_NULL), (dict(lse=N), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=0), fa.FA_ERR_SHAPE), (dict(Nq=0), fa.FA_ERR_SHAPE),
+    (dict(Nkv=-3), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED), (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=2, W=0, G=0), fa.FA_ERR_SHAPE), (dict(mask=2, W=4, G=-1), fa.FA_ERR_SHAPE),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+    (dict(q=ctypes.c_void_p(0x1008)), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 16, H=1 << 16), fa.FA_ERR_SHAPE),
+])
+def test_forward_rejects_before_launch(kw, status):
+    assert fwd(**kw) == status
+
+
+def dec(q=P, kp=P, vp=P, pt=P, sl=P, o=P, lse=N, page=256, S=8, H=32, d=128, maxp=32, npages=300,
+        scale=0.088, dtype=1, ws=P, wsb=None):
+    lib = fa.load_library()
+    if wsb is None:
+        wsb = lib.fa_decode_paged_workspace_bytes(S, H, d, maxp, page)
+    return lib.fa_decode_paged(q, kp, vp, pt, sl, o, lse, page, S, H, d, maxp, npages, scale,
+                               dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=N), fa.FA_ERR_NULL), (dict(kp=N), fa.FA_ERR_NULL), (dict(vp=N), fa.FA_ERR_NULL),
+    (dict(pt=N), fa.FA_ERR_NULL), (dict(sl=N), fa.FA_ERR_NULL), (dict(o=N), fa.FA_ERR_NULL),
+    (dict(S=0), fa.FA_ERR_SHAPE), (dict(H=0), fa.FA_ERR_SHAPE), (dict(maxp=0), fa.FA_ERR_SHAPE),
+    (dict(npages=0), fa.FA_ERR_SHAPE),
+    (dict(page=128), fa.FA_ERR_UNSUPPORTED), (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=12), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=N), fa.FA_ERR_WORKSPACE), (dict(wsb=16), fa.FA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x1004)), fa.FA_ERR_WORKSPACE),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+])
+def test_decode_rejects_before_launch(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_workspace_bytes():
+    lib = fa.load_library()
+    # 8 sequences, 32 heads, d 128, 32 pages of 256 tokens: 128 splits of 64 tokens,
+    # each split keeps 128 partial outputs and one log-sum-exp (float32)
+    assert lib.fa_decode_paged_workspace_bytes(8, 32, 128, 32, 256) == 8 * 32 * 128 * 129 * 4
+    assert lib.fa_decode_paged_workspace_bytes(0, 32, 128, 32, 256) == 0

@@ -1,0 +1,113 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Small shapes compare every element and span several tiles plus ragged tails; the full-size
+workloads run in the same launch configuration the benchmark times and compare every
+element (dense, decode) or sampled rows that include every tile and mask edge (causal,
+window). Tolerances are stated in gpu_util.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_forward_amd as fa
+import workloads
+from gpu_util import check, f64, gather_rows, require_gpu, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, scale, mask=0, W=0, G=0):
+    qd, kd, vd = to_dev(q, k, v)
+    o, lse = fa.fa_forward(qd, kd, vd, scale, mask, W, G)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def run_decode(inp, scale):
+    q, kp, vp, pt, sl = to_dev(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
+                               inp["seq_lens"])
+    o, lse = fa.fa_decode_paged(q, kp, vp, pt, sl, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+MASKS = [(0, 0, 0), (1, 0, 0), (2, 40, 5), (2, 1, 0), (2, 100, 70), (2, 64, 64)]
+SHAPES = [(1, 1, 1, 1), (1, 2, 17, 17), (2, 3, 100, 100), (1, 2, 129, 129), (1, 1, 300, 300),
+          (1, 2, 64, 200), (1, 2, 200, 64), (1, 1, 1, 333), (1, 2, 257, 513)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", MASKS, ids=lambda m: f"m{m[0]}w{m[1]}g{m[2]}")
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(dtype, d, mask, shape):
+    B, H, Nq, Nkv = shape
+    seed = zlib.crc32(repr((dtype, d, mask, shape)).encode()) % 100000
+    q, k, v = workloads.gen_prefill(B, H, Nq, Nkv, d, dtype, seed)
+    scale = workloads.default_scale(d)
+    o, lse = run_fwd(q, k, v, scale, *mask)
+    ro, rl = oracle.attention(q, k, v, scale, *mask)
+    check(o, lse, ro, rl, dtype, f"{dtype} d{d} mask{mask} {shape}")
+
+
+def test_tiny_f32_workload():
+    w, inp = workloads.gen_workload("tiny_f32")
+    scale = workloads.default_scale(w["d"])
+    o, lse = run_fwd(inp["q"], inp["k"], inp["v"], scale, w["mask"])
+    ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], scale, w["mask"])
+    e = check(o, lse, ro, rl, "f32", "tiny_f32")
+    print("tiny_f32", e)
+
+
+@pytest.mark.parametrize("name", ["dense_f16", "dense_bf16"])
+def test_dense_full_size_every_element(name):
+    w, inp = workloads.gen_workload(name)
+    scale = workloads.default_scale(w["d"])
+    o, lse = run_fwd(inp["q"], inp["k"], inp["v"], scale, w["mask"])
+    ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], scale, w["mask"])
+    e = check(o, lse, ro, rl, w["dtype"], name)
+    print(name, e)
+
+
+@pytest.mark.parametrize("name,extra", [
+    ("causal_bf16", (255, 256, 257, 1023, 1024, 2047, 2048, 4094)),
+    ("window_bf16", (62, 63, 64, 65, 2046, 2047, 2048, 2049, 2110, 2111, 2112, 2113, 4095,
+                     4096, 16383, 16384, 32766)),
+])
+def test_masked_full_size_sampled_rows(name, extra):
+    w, inp = workloads.gen_workload(name)
+    scale = workloads.default_scale(w["d"])
+    o, lse = run_fwd(inp["q"], inp["k"], inp["v"], scale, w["mask"], w["window"], w["n_global"])
+    rows = sample_rows(w["B"], w["H"], w["Nq"], extra=extra, per_head=24, seed=w["seed"])
+    ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], scale, w["mask"], w["window"],
+                              w["n_global"], rows=rows)
+    og, lg = gather_rows(o, lse, rows)
+    e = check(og, lg, ro, rl, w["dtype"], name)
+    print(name, len(rows), "rows", e)
+    # every row, including those not sampled: finite, and LSE at least the largest score
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_decode_full_size_every_element():
+    w, inp = workloads.gen_workload("decode_f16")
+    scale = workloads.default_scale(w["d"])
+    o, lse = run_decode(inp, scale)
+    ro, rl = oracle.decode_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
+                                 inp["seq_lens"], scale)
+    e = check(o, lse, ro, rl, "f16", "decode_f16")
+    print("decode_f16", e)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("lens", [[1, 2, 63, 64, 65, 255, 256, 257], [8192, 4096, 7000, 1]])
+def test_decode_ragged_lengths(dtype, lens):
+    w, inp = workloads.gen_workload("decode_f16", dtype=dtype, lens=lens, S=len(lens), H=16,
+                                    max_len=8192)
+    scale = workloads.default_scale(w["d"])
+    o, lse = run_decode(inp, scale)
+    ro, rl = oracle.decode_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
+                                 inp["seq_lens"], scale)
+    check(o, lse, ro, rl, dtype, f"decode {dtype} {lens}")

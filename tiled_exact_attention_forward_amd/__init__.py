@@ -1,0 +1,185 @@
+"""Python binding of libteaf.so, the MI355X (gfx950) tiled exact attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind the
+C ABI declared in include/fa.h. The functions carry the C names:
+
+    fa_forward(q, k, v, ...)          tiled exact attention forward (O and LSE)
+    fa_decode_paged(q, k_pages, ...)  single-token decode against a paged K/V cache
+    fa_decode_paged_workspace_bytes(...)
+    fa_status_string(status)
+
+Tensors are torch tensors on the GPU (torch supplies device memory and the current stream);
+they are passed to the library as raw device pointers. There is no fallback: if the library
+has not been built, importing the binding's functions raises.
+"""
+import ctypes
+import math
+import os
+
+__all__ = ["fa_forward", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+           "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
+           "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
+           "FA_MASK_WINDOW_GLOBAL", "EXPORTED_SYMBOLS"]
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL = 0, 1, 2
+EXPORTED_SYMBOLS = ("fa_forward", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+                    "fa_status_string", "fa_last_hip_error", "fa_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def library_path():
+    return os.path.join(_HERE, "libteaf.so")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = f"{where}: {fa_status_string(status)} (status {status})"
+        if status == FA_ERR_HIP:
+            msg += f": {fa_last_hip_error()}"
+        super().__init__(msg)
+
+
+def load_library():
+    """Load libteaf.so (raises if it was not built: there is no other code path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- load torch's HIP runtime first so the library shares it
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with "
+                          "`python -m tiled_exact_attention_forward_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
+    lib.fa_forward.restype = i
+    lib.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_paged_workspace_bytes.restype = sz
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
+                                    vp]
+    lib.fa_decode_paged.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.restype = i
+    lib.fa_last_hip_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_last_hip_error():
+    return load_library().fa_last_hip_error().decode()
+
+
+def fa_version():
+    return int(load_library().fa_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    m = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(name, t, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def fa_forward(q, k, v, scale=None, mask_mode=FA_MASK_NONE, window=0, n_global=0, out=None,
+               lse=None, stream=None):
+    """O, LSE = attention(q, k, v) with q [B,H,Nq,d], k/v [B,H,Nkv,d] (f32/f16/bf16).
+
+    scale defaults to the float32 value of 1/sqrt(d). Returns (out, lse) with out like q and
+    lse float32 [B,H,Nq]. Runs asynchronously on `stream` (torch's current stream if None).
+    """
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Nkv, d) or tuple(v.shape) != (B, H, Nkv, d):
+        raise ValueError("k and v must be [B,H,Nkv,d] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    rc = load_library().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq,
+                                   Nkv, d, float(scale), int(mask_mode), int(window),
+                                   int(n_global), _dtype_code(q), _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_forward")
+    return out, lse
+
+
+def fa_decode_paged_workspace_bytes(num_seqs, H, d, max_pages_per_seq, page_size=256):
+    return int(load_library().fa_decode_paged_workspace_bytes(
+        int(num_seqs), int(H), int(d), int(max_pages_per_seq), int(page_size)))
+
+
+def fa_decode_paged(q, k_pages, v_pages, page_table, seq_lens, scale=None, out=None, lse=None,
+                    workspace=None, stream=None):
+    """Single-token decode: q [S,H,d]; pages [P,page_size,H,d]; page_table [S,max_pages]
+    int32; seq_lens [S] int32 (all on the GPU). Returns (out [S,H,d], lse [S,H] float32)."""
+    torch = _torch()
+    S, H, d = q.shape
+    P, page_size = k_pages.shape[0], k_pages.shape[1]
+    max_pages = page_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    need = fa_decode_paged_workspace_bytes(S, H, d, max_pages, page_size)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("out", out)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("page_table", page_table, torch.int32)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("workspace", workspace)
+    rc = load_library().fa_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table), _ptr(seq_lens), _ptr(out),
+        _ptr(lse), page_size, S, H, d, max_pages, P, float(scale), _dtype_code(q),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_decode_paged")
+    return out, lse

@@ -1,0 +1,103 @@
+// fa_api.cpp -- the C ABI of libteaf.so: host-side argument checks, then one launch call.
+// Every check runs before anything is enqueued, so a rejected call writes nothing.
+#include <limits.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return FA_OK;
+    g_last_hip = e;
+    return FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char *fa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }
+
+const char *fa_status_string(int status)
+{
+    switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "a size argument is out of range";
+    case FA_ERR_UNSUPPORTED: return "valid arguments that this build does not support";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "the HIP runtime rejected a launch";
+    default: return "unknown status";
+    }
+}
+
+int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int Nq, int Nkv, int d, float scale, int mask_mode, int window, int n_global,
+               int dtype, void *stream)
+{
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (mask_mode != FA_MASK_NONE && mask_mode != FA_MASK_CAUSAL &&
+        mask_mode != FA_MASK_WINDOW_GLOBAL)
+        return FA_ERR_UNSUPPORTED;
+    if (mask_mode == FA_MASK_WINDOW_GLOBAL && (window < 1 || n_global < 0)) return FA_ERR_SHAPE;
+    const long long bh = (long long)B * H;
+    const long long nqt = (Nq + 127) / 128;
+    if (bh * nqt > (long long)INT_MAX) return FA_ERR_SHAPE;
+    if ((long long)Nq * d > (long long)INT_MAX || (long long)Nkv * d > (long long)INT_MAX)
+        return FA_ERR_SHAPE;
+    if (!(scale == scale)) return FA_ERR_SHAPE;  // NaN scale
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return FA_ERR_UNSUPPORTED;
+    teaf::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nkv, d, scale,
+                    mask_mode, mask_mode == FA_MASK_WINDOW_GLOBAL ? window : 0,
+                    mask_mode == FA_MASK_WINDOW_GLOBAL ? n_global : 0, dtype};
+    return hip_status(teaf::launch_forward(a, (hipStream_t)stream));
+}
+
+size_t fa_decode_paged_workspace_bytes(int num_seqs, int H, int d, int max_pages_per_seq,
+                                       int page_size)
+{
+    if (num_seqs < 1 || H < 1 || d < 1 || max_pages_per_seq < 1 || page_size < 1) return 0;
+    const size_t splits = (size_t)teaf::decode_max_splits(max_pages_per_seq, page_size);
+    return (size_t)num_seqs * H * splits * ((size_t)d + 1) * sizeof(float);
+}
+
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *page_table, const int32_t *seq_lens, void *o, float *lse,
+                    int page_size, int num_seqs, int H, int d, int max_pages_per_seq,
+                    int num_pages, float scale, int dtype, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !o) return FA_ERR_NULL;
+    if (num_seqs < 1 || H < 1 || max_pages_per_seq < 1 || num_pages < 1 || page_size < 1)
+        return FA_ERR_SHAPE;
+    if (page_size != 256 || d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (H % teaf::kDecodeHeads != 0) return FA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535 || H / teaf::kDecodeHeads > 65535) return FA_ERR_SHAPE;
+    if ((long long)num_pages * page_size * H * d > (long long)1 << 40) return FA_ERR_SHAPE;
+    if (!(scale == scale)) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+        return FA_ERR_UNSUPPORTED;
+    const size_t need =
+        fa_decode_paged_workspace_bytes(num_seqs, H, d, max_pages_per_seq, page_size);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_WORKSPACE;
+    teaf::DecodeArgs a{q, k_pages, v_pages, page_table, seq_lens, o, lse, page_size,
+                       num_seqs, H, d, max_pages_per_seq, num_pages, scale, dtype, workspace};
+    return hip_status(teaf::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

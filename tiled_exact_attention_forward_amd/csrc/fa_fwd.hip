@@ -1,0 +1,542 @@
+// fa_fwd.hip -- tiled exact attention forward pass for gfx950 (MI355X, CDNA4).
+//
+// Method (ops-transformer article on gitcode.csdn.net, section 二.1 "FlashAttention算子";
+// zwxr.cn article, section 3.1): a workgroup owns one tile of query rows, keeps them on
+// chip, and walks the key/value tiles that its mask leaves visible. Per tile it forms the
+// score block on the matrix cores, updates a running row maximum m and running sum l
+// (online softmax), rescales the output accumulator by exp(m_old - m_new) and adds P V.
+// After the last tile the accumulator is divided by l once. The N x N scores never leave
+// registers. Scores, m, l and the accumulator are fp32 (the pages keep the softmax
+// denominator in fp32); P is rounded to the input type for the P V product.
+//
+// gfx950 mapping (not the pages' Ascend tiling, which was sized for the 910's buffers):
+//  * 256 threads = 4 wave64s, 128 query rows per workgroup, 32 rows per wave;
+//    key/value tiles of 64 rows, double-buffered in LDS (prefetch of tile n+1 from HBM
+//    into registers overlaps the math on tile n, then lands in the other LDS buffer).
+//  * The score block is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,
+//    f16}: lane (g, i) then holds 16 keys of query row i per 32-key block, so the row max
+//    and row sum are in-lane reductions plus one exchange with lane i^32, and the fp32
+//    accumulator converts in place into the B operand (P^T) of O^T = V^T P^T.
+//  * V stays row-major in LDS; the V^T operand is read with ds_read_b64_tr_b16, whose
+//    16-lane transpose hands each lane four consecutive keys of one column.
+//  * exp(x) is evaluated as 2^(x log2 e) with v_exp_f32; the log2 e factor is folded into
+//    the score scale, so each score costs one multiply before the exponential.
+//  * Tiles that a mask hides from every row are never loaded; tiles it hides from one
+//    wave's rows skip that wave's math; only edge tiles evaluate the element mask.
+//  * Workgroup ids are remapped so the query tiles of one (batch, head) run on one XCD and
+//    share its L2 copy of K and V; the query tiles with the most visible keys go first.
+//
+// fp32 inputs use v_mfma_f32_32x32x2f32 (true fp32 products) in a simpler single-buffered
+// kernel with 32-key tiles.
+#include <math.h>
+
+#include "fa_launch.h"
+
+namespace teaf {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kXcds = 8;
+
+// Hardware hands consecutive workgroup ids to the 8 XCDs in turn. Map id w (of n) to a
+// logical index so that each XCD receives one contiguous run of logical indices.
+__device__ __forceinline__ int xcd_remap(int w, int n)
+{
+    const int per = n / kXcds, rem = n % kXcds;
+    const int x = w % kXcds, idx = w / kXcds;
+    return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
+}
+
+template <int MASK>
+__device__ __forceinline__ bool key_visible(int ip, int j, int W, int G)
+{
+    if (MASK == 0) return true;
+    if (MASK == 1) return j <= ip;
+    return j <= ip && (ip - j < W || j < G);
+}
+
+// Key tiles visible to query rows [q0, min(q0+BM, Nq)): [a0,a1) then [b0,b1), ascending.
+struct TileRanges {
+    int a0, a1, b0, b1;
+};
+
+template <int MASK, int BM, int BN>
+__device__ __forceinline__ TileRanges visible_tiles(int q0, int Nq, int Nkv, int W, int G)
+{
+    TileRanges r{0, (Nkv + BN - 1) / BN, 0, 0};
+    if (MASK == 0) return r;
+    const int delta = Nkv - Nq;
+    const int last = min(Nkv - 1, min(q0 + BM, Nq) - 1 + delta);  // newest visible key
+    if (last < 0) {
+        r.a1 = 0;
+        return r;
+    }
+    const int t_end = last / BN + 1;
+    r.a1 = t_end;
+    if (MASK == 1) return r;
+    const int first = max(0, q0 + delta - W + 1);  // oldest window key of the first row
+    const int w_begin = first / BN;
+    const int g_end = (min(G, last + 1) + BN - 1) / BN;
+    if (g_end >= w_begin) return r;  // global tiles touch the window: one range
+    r.a1 = g_end;
+    r.b0 = w_begin;
+    r.b1 = t_end;
+    return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+struct Ops16;
+
+template <>
+struct Ops16<__bf16> {
+    static __device__ __forceinline__ f32x16 mma(s16x8 a, s16x8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ s16x8 pack8(float a0, float a1, float a2, float a3,
+                                                  float a4, float a5, float a6, float a7)
+    {
+        bf16x8 r = {(__bf16)a0, (__bf16)a1, (__bf16)a2, (__bf16)a3,
+                    (__bf16)a4, (__bf16)a5, (__bf16)a6, (__bf16)a7};
+        return __builtin_bit_cast(s16x8, r);
+    }
+    static __device__ __forceinline__ s16x4 pack4(float a0, float a1, float a2, float a3)
+    {
+        bf16x4 r = {(__bf16)a0, (__bf16)a1, (__bf16)a2, (__bf16)a3};
+        return __builtin_bit_cast(s16x4, r);
+    }
+};
+
+template <>
+struct Ops16<_Float16> {
+    static __device__ __forceinline__ f32x16 mma(s16x8 a, s16x8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ s16x8 pack8(float a0, float a1, float a2, float a3,
+                                                  float a4, float a5, float a6, float a7)
+    {
+        f16x8 r = {(_Float16)a0, (_Float16)a1, (_Float16)a2, (_Float16)a3,
+                   (_Float16)a4, (_Float16)a5, (_Float16)a6, (_Float16)a7};
+        return __builtin_bit_cast(s16x8, r);
+    }
+    static __device__ __forceinline__ s16x4 pack4(float a0, float a1, float a2, float a3)
+    {
+        f16x4 r = {(_Float16)a0, (_Float16)a1, (_Float16)a2, (_Float16)a3};
+        return __builtin_bit_cast(s16x4, r);
+    }
+};
+
+// ------------------------------------------------------------------ 16-bit kernel
+
+template <int D>
+struct Cfg16 {
+    static constexpr int BM = 128, BN = 64, NT = 256;
+    static constexpr int KP = D + 8;   // K row pitch in LDS (elements), 16-byte aligned
+    static constexpr int VP = D + 16;  // V row pitch in LDS (elements), 16-byte aligned
+    static constexpr int KE = BN * KP, VE = BN * VP, SE = KE + VE;
+    static constexpr int RC = D / 8;             // 16-byte chunks per row
+    static constexpr int CPT = BN * RC / NT;     // chunks per thread per tile and tensor
+    static constexpr int NKK = D / 16, NDB = D / 32;
+    static constexpr int LDS_BYTES = 2 * SE * 2;
+};
+
+template <typename T, int D, int MASK>
+__global__ __launch_bounds__(256, 2) void fwd16_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
+    int Nkv, float c, int W, int G, int nqt)
+{
+    using C = Cfg16<D>;
+    using Op = Ops16<T>;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT, KP = C::KP, VP = C::VP;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, li = lane & 31;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = L / nqt;
+    const int q0 = (nqt - 1 - L % nqt) * BM;  // most-loaded query tiles first
+    const int delta = Nkv - Nq;
+    const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
+
+    // Q^T fragments (B operand): lane (g, i) holds Q[row i][16kk + 8g .. +7].
+    const int wrow0 = q0 + wave * 32;
+    const int row = wrow0 + li;
+    const int ip = row + delta;
+    s16x8 qf[C::NKK];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+        if (row < Nq)
+            qf[kk] = *(const s16x8 *)(Q + qbase + (size_t)row * D + 16 * kk + 8 * g);
+        else
+            qf[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+
+    const TileRanges tr = visible_tiles<MASK, BM, BN>(q0, Nq, Nkv, W, G);
+    const int na = tr.a1 - tr.a0;
+    const int ntiles = na + (tr.b1 - tr.b0);
+
+    float m = -INFINITY, l = 0.f;
+    f32x16 oacc[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+
+    s16x8 kr[C::CPT], vr[C::CPT];
+    auto tile_id = [&](int n) { return n < na ? tr.a0 + n : tr.b0 + (n - na); };
+    auto gload = [&](int tile) {
+        const int kv0 = tile * BN;
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            const int id = tid + u * NT, r = id / C::RC, cc = id % C::RC;
+            const int key = kv0 + r;
+            if (key < Nkv) {
+                kr[u] = *(const s16x8 *)(K + kvbase + (size_t)key * D + cc * 8);
+                vr[u] = *(const s16x8 *)(V + kvbase + (size_t)key * D + cc * 8);
+            } else {
+                kr[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                vr[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+        uint16_t *ks = smem + buf * C::SE;
+        uint16_t *vs = ks + C::KE;
+#pragma unroll
+        for (int u = 0; u < C::CPT; ++u) {
+            const int id = tid + u * NT, r = id / C::RC, cc = id % C::RC;
+            *(s16x8 *)(ks + r * KP + cc * 8) = kr[u];
+            *(s16x8 *)(vs + r * VP + cc * 8) = vr[u];
+        }
+    };
+
+    if (ntiles > 0) {
+        gload(tile_id(0));
+        lstore(0);
+        __syncthreads();
+    }
+    for (int n = 0; n < ntiles; ++n) {
+        const int tile = tile_id(n);
+        const bool more = n + 1 < ntiles;
+        if (more) gload(tile_id(n + 1));
+        const int kv0 = tile * BN;
+
+        // Wave-uniform visibility of this tile for the wave's 32 rows.
+        bool skip = wrow0 >= Nq;
+        bool need_mask = kv0 + BN > Nkv;
+        if (MASK >= 1) {
+            const int ip0 = wrow0 + delta, ip1 = wrow0 + 31 + delta;
+            if (kv0 > ip1) skip = true;
+            if (kv0 + BN - 1 > ip0) need_mask = true;
+            if (MASK == 2) {
+                if (kv0 + BN - 1 < ip0 - W + 1 && kv0 >= G) skip = true;
+                if (!(ip1 - kv0 < W) && !(kv0 + BN - 1 < G)) need_mask = true;
+            }
+        }
+
+        if (!skip) {
+            const uint16_t *ks = smem + (n & 1) * C::SE;
+            const uint16_t *vs = ks + C::KE;
+            f32x16 sacc[2];
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[jb][e] = 0.f;
+            // S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T fragments.
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; ++kk) {
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    const s16x8 a = *(const s16x8 *)(ks + (jb * 32 + li) * KP + 16 * kk + 8 * g);
+                    sacc[jb] = Op::mma(a, qf[kk], sacc[jb]);
+                }
+            }
+            // Lane (g, i) holds key 32jb + 8(e/4) + 4g + e%4 of row i in sacc[jb][e].
+            float mt = -INFINITY;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float t = sacc[jb][e] * c;
+                    if (need_mask) {
+                        const int key = kv0 + jb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                        if (key >= Nkv || !key_visible<MASK>(ip, key, W, G)) t = -INFINITY;
+                    }
+                    sacc[jb][e] = t;
+                    mt = fmaxf(mt, t);
+                }
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float mn = fmaxf(m, mt);
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            const float alpha = fast_exp2(m - mu);
+            m = mn;
+            float ps = 0.f;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float p = fast_exp2(sacc[jb][e] - mu);
+                    sacc[jb][e] = p;
+                    ps += p;
+                }
+            }
+            l = l * alpha + ps;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+
+            // O^T += V^T P^T over four 16-key chunks. Chunk kc, slot (g, e) is key
+            // 16kc + 8(e/4) + 4g + e%4: P^T is sacc[kc/2][8(kc%2) + e] in place.
+            const int trow = 4 * g + ((lane & 15) >> 2);
+            const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+            for (int kc = 0; kc < BN / 16; ++kc) {
+                const int jb = kc >> 1, o8 = 8 * (kc & 1);
+                const s16x8 pf = Op::pack8(sacc[jb][o8 + 0], sacc[jb][o8 + 1], sacc[jb][o8 + 2],
+                                           sacc[jb][o8 + 3], sacc[jb][o8 + 4], sacc[jb][o8 + 5],
+                                           sacc[jb][o8 + 6], sacc[jb][o8 + 7]);
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    const uint16_t *vp = vs + (kc * 16 + trow) * VP + db * 32 + tcol;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vp);
+                    const s16x4 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vp + 8 * VP));
+                    const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[db] = Op::mma(a, pf, oacc[db]);
+                }
+            }
+        }
+        if (more) lstore((n + 1) & 1);
+        __syncthreads();
+    }
+
+    // Epilogue: both lane halves hold partial sums of the same row.
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row < Nq) {
+        uint16_t *orow = O + qbase + (size_t)row * D;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const s16x4 v4 = Op::pack4(oacc[db][4 * blk + 0] * inv, oacc[db][4 * blk + 1] * inv,
+                                           oacc[db][4 * blk + 2] * inv, oacc[db][4 * blk + 3] * inv);
+                *(s16x4 *)(orow + db * 32 + 8 * blk + 4 * g) = v4;
+            }
+        }
+        if (g == 0)
+            LSE[(size_t)bh * Nq + row] =
+                lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    }
+}
+
+// ------------------------------------------------------------------ fp32 kernel
+
+template <int D, int MASK>
+__global__ __launch_bounds__(256) void fwd32_kernel(const float *__restrict__ Q,
+                                                    const float *__restrict__ K,
+                                                    const float *__restrict__ V,
+                                                    float *__restrict__ O, float *__restrict__ LSE,
+                                                    int Nq, int Nkv, float c, int W, int G, int nqt)
+{
+    constexpr int BM = 128, BN = 32, NT = 256, KP = D + 1;
+    constexpr int NKK = D / 2, NDB = D / 32, RC = D / 4, CPT = BN * RC / NT;
+    __shared__ float ks[BN * KP];
+    __shared__ __attribute__((aligned(16))) float vs[BN * D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, li = lane & 31;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = L / nqt;
+    const int q0 = (nqt - 1 - L % nqt) * BM;
+    const int delta = Nkv - Nq;
+    const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
+    const int wrow0 = q0 + wave * 32, row = wrow0 + li, ip = row + delta;
+
+    // Q^T fragments for the 32x32x2 MFMA: lane (g, i) holds Q[row i][2kk + g].
+    float qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = row < Nq ? Q[qbase + (size_t)row * D + 2 * kk + g] : 0.f;
+
+    const TileRanges tr = visible_tiles<MASK, BM, BN>(q0, Nq, Nkv, W, G);
+    const int na = tr.a1 - tr.a0, ntiles = na + (tr.b1 - tr.b0);
+    float m = -INFINITY, l = 0.f;
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+
+    for (int n = 0; n < ntiles; ++n) {
+        const int tile = n < na ? tr.a0 + n : tr.b0 + (n - na);
+        const int kv0 = tile * BN;
+        __syncthreads();  // previous tile's readers are done
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int id = tid + u * NT, r = id / RC, cc = id % RC, key = kv0 + r;
+            f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+            if (key < Nkv) {
+                kv = *(const f32x4 *)(K + kvbase + (size_t)key * D + 4 * cc);
+                vv = *(const f32x4 *)(V + kvbase + (size_t)key * D + 4 * cc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ks[r * KP + 4 * cc + e] = kv[e];
+            *(f32x4 *)(vs + r * D + 4 * cc) = vv;
+        }
+        __syncthreads();
+
+        bool skip = wrow0 >= Nq;
+        bool need_mask = kv0 + BN > Nkv;
+        if (MASK >= 1) {
+            const int ip0 = wrow0 + delta, ip1 = wrow0 + 31 + delta;
+            if (kv0 > ip1) skip = true;
+            if (kv0 + BN - 1 > ip0) need_mask = true;
+            if (MASK == 2) {
+                if (kv0 + BN - 1 < ip0 - W + 1 && kv0 >= G) skip = true;
+                if (!(ip1 - kv0 < W) && !(kv0 + BN - 1 < G)) need_mask = true;
+            }
+        }
+        if (skip) continue;
+
+        f32x16 sacc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[li * KP + 2 * kk + g], qf[kk], sacc, 0, 0, 0);
+        float mt = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float t = sacc[e] * c;
+            if (need_mask) {
+                const int key = kv0 + 8 * (e >> 2) + 4 * g + (e & 3);
+                if (key >= Nkv || !key_visible<MASK>(ip, key, W, G)) t = -INFINITY;
+            }
+            sacc[e] = t;
+            mt = fmaxf(mt, t);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = fast_exp2(m - mu);
+        m = mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(sacc[e] - mu);
+            sacc[e] = p;
+            ps += p;
+        }
+        l = l * alpha + ps;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        // O^T += V^T P^T, one key per lane half per step: key 8blk + 4g + r.
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int key = 8 * (e >> 2) + 4 * g + (e & 3);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * D + db * 32 + li], sacc[e],
+                                                                oacc[db], 0, 0, 0);
+        }
+    }
+
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row < Nq) {
+        float *orow = O + qbase + (size_t)row * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                f32x4 v4 = {oacc[db][4 * blk] * inv, oacc[db][4 * blk + 1] * inv,
+                            oacc[db][4 * blk + 2] * inv, oacc[db][4 * blk + 3] * inv};
+                *(f32x4 *)(orow + db * 32 + 8 * blk + 4 * g) = v4;
+            }
+        if (g == 0)
+            LSE[(size_t)bh * Nq + row] =
+                lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    }
+}
+
+template <typename T, int D, int MASK>
+hipError_t launch16(const FwdArgs &a, hipStream_t s)
+{
+    using C = Cfg16<D>;
+    const int nqt = (a.Nq + C::BM - 1) / C::BM;
+    const long nblk = (long)nqt * a.B * a.H;
+    auto kern = fwd16_kernel<T, D, MASK>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), C::LDS_BYTES, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (uint16_t *)a.o, a.lse, a.Nq, a.Nkv, a.scale * kLog2e, a.window,
+                       a.n_global, nqt);
+    return hipGetLastError();
+}
+
+template <int D, int MASK>
+hipError_t launch32(const FwdArgs &a, hipStream_t s)
+{
+    const int nqt = (a.Nq + 127) / 128;
+    const long nblk = (long)nqt * a.B * a.H;
+    hipLaunchKernelGGL((fwd32_kernel<D, MASK>), dim3((unsigned)nblk), dim3(256), 0, s,
+                       (const float *)a.q, (const float *)a.k, (const float *)a.v, (float *)a.o,
+                       a.lse, a.Nq, a.Nkv, a.scale * kLog2e, a.window, a.n_global, nqt);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch16_mask(const FwdArgs &a, hipStream_t s)
+{
+    switch (a.mask) {
+    case 0: return launch16<T, D, 0>(a, s);
+    case 1: return launch16<T, D, 1>(a, s);
+    default: return launch16<T, D, 2>(a, s);
+    }
+}
+
+template <int D>
+hipError_t launch32_mask(const FwdArgs &a, hipStream_t s)
+{
+    switch (a.mask) {
+    case 0: return launch32<D, 0>(a, s);
+    case 1: return launch32<D, 1>(a, s);
+    default: return launch32<D, 2>(a, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_forward(const FwdArgs &a, hipStream_t s)
+{
+    (void)hipGetLastError();  // start from a clean error state
+    if (a.dtype == 0) return a.d == 64 ? launch32_mask<64>(a, s) : launch32_mask<128>(a, s);
+    if (a.dtype == 1)
+        return a.d == 64 ? launch16_mask<_Float16, 64>(a, s) : launch16_mask<_Float16, 128>(a, s);
+    return a.d == 64 ? launch16_mask<__bf16, 64>(a, s) : launch16_mask<__bf16, 128>(a, s);
+}
+
+}  // namespace teaf
