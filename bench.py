@@ -187,6 +187,10 @@ def main():
                     help="skip the other workloads and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (for HBM counter scaling)")
+    ap.add_argument("--profile-workload", default=None,
+                    help="only run this workload for --steps calls (for profilers); no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -200,6 +204,23 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fa.load_library()
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {args.copy_calibration} MiB x {args.steps}", file=sys.stderr)
+        return
+    if args.profile_workload:
+        kind = workloads.WORKLOADS[args.profile_workload]["kind"]
+        fn = bench_prefill if kind == "prefill" else bench_decode
+        r = fn(args.profile_workload, args.steps, args.warmup, torch, fa, workloads)
+        print(f"[bench] {args.profile_workload}: {r['ms'] * 1e3:.1f} us per call", file=sys.stderr)
+        return
 
     head = bench_prefill(args.workload, args.steps, args.warmup, torch, fa, workloads)
     print(f"[bench] {args.workload}: {head['ms'] * 1e3:.1f} us/step, "

@@ -28,6 +28,7 @@
 //
 // fp32 inputs use v_mfma_f32_32x32x2f32 (true fp32 products) in a simpler single-buffered
 // kernel with 32-key tiles.
+#include <limits.h>
 #include <math.h>
 
 #include "fa_launch.h"
@@ -147,14 +148,174 @@ struct Ops16<_Float16> {
 template <int D>
 struct Cfg16 {
     static constexpr int BM = 128, BN = 64, NT = 256;
-    static constexpr int KP = D + 8;   // K row pitch in LDS (elements), 16-byte aligned
-    static constexpr int VP = D + 16;  // V row pitch in LDS (elements), 16-byte aligned
-    static constexpr int KE = BN * KP, VE = BN * VP, SE = KE + VE;
-    static constexpr int RC = D / 8;             // 16-byte chunks per row
-    static constexpr int CPT = BN * RC / NT;     // chunks per thread per tile and tensor
+    static constexpr int ROWB = D * 2;                 // bytes of one K or V row
+    static constexpr int TILEB = BN * ROWB;            // bytes of one K (or V) tile
+    static constexpr int STAGEB = 2 * TILEB;           // K tile then V tile
+    static constexpr int LDS_BYTES = 2 * STAGEB;       // two stages
+    static constexpr int CHUNKS = ROWB / 16;           // 16-byte chunks per row
+    static constexpr int ROWS_PER_LOAD = 64 / CHUNKS;  // rows one wave-wide 16-byte load fills
+    static constexpr int LOADS = BN / ROWS_PER_LOAD / 4;  // loads per wave per tile and tensor
     static constexpr int NKK = D / 16, NDB = D / 32;
-    static constexpr int LDS_BYTES = 2 * SE * 2;
 };
+
+// LDS tiles are unpadded rows with an XOR swizzle of the 16-byte chunks (an involution:
+// the same function maps logical to physical and back). Chosen against the 64-bank LDS:
+// a ds_read_b128 serves 16 lanes per cycle, here 16 consecutive K rows at one logical
+// chunk; a ds_read_b64_tr_b16 serves 32 lanes, here 4 consecutive V rows x 64 bytes.
+template <int D>
+__device__ __forceinline__ int k_swz(int row, int chunk)
+{
+    return D == 128 ? chunk ^ (row & 15) : chunk ^ ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row, int chunk)
+{
+    return D == 128 ? chunk ^ (4 * (row & 3)) : chunk ^ (4 * ((row >> 1) & 1));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue this wave's share of the direct HBM-to-LDS loads of the K and V tile that starts
+// at key kv0 into the LDS stage `st`. Rows past Nkv read as zeros (buffer range check).
+template <int D>
+__device__ __forceinline__ void issue_tile(const char *kbh, const char *vbh,
+                                           const unsigned (&koff)[Cfg16<D>::LOADS],
+                                           const unsigned (&voff)[Cfg16<D>::LOADS], int kv0,
+                                           int Nkv, char *st, int wave)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer resource type exists only for the GPU target
+    using C = Cfg16<D>;
+    // Raw buffer descriptors (gfx9 family word 3: data format 32, no swizzle; stride 0)
+    // covering the keys from kv0 to the end: loads at or past that range return zeros.
+    const int rest = (int)((unsigned)(Nkv - kv0) * C::ROWB);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(kbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(vbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+        const int slot = (4 * u + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(st + slot), 16, koff[u], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(st + C::TILEB + slot), 16,
+                                                 voff[u], 0, 0, 0);
+    }
+#endif
+}
+
+// The running maximum is only moved (and O, l rescaled) when a row's new maximum exceeds
+// the one in use by more than this many powers of two; until then probabilities are taken
+// relative to the stale maximum and stay below 2^8, which fp32 sums and 16-bit P hold
+// exactly as well. The result is the same softmax: numerator and denominator share the
+// reference value, and the final division removes it.
+constexpr float kRescaleSlack = 8.0f;
+
+// One 64-key tile for the 32 query rows of a wave. ks/vs: the tile's K and V in LDS.
+// qf: Q^T fragments. c = scale * log2(e) >= 0 (a negative scale is folded into Q).
+// MASKED tiles evaluate the element mask (and the key-range tail); others skip it.
+template <typename T, int D, int MASK, bool MASKED>
+__device__ __forceinline__ void attend_tile(const uint16_t *__restrict__ ks,
+                                            const uint16_t *__restrict__ vs,
+                                            const s16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
+                                            float &m, float &l, float c, int kv0, int ip,
+                                            int Nkv, int W, int G, int lane)
+{
+    using C = Cfg16<D>;
+    using Op = Ops16<T>;
+    const int g = lane >> 5, li = lane & 31;
+    const char *kb = (const char *)ks;
+    const char *vb = (const char *)vs;
+
+    // S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T fragments. Lane (g, j) reads row
+    // 32jb + j, logical chunk 2kk + g.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int r = jb * 32 + li;
+            const s16x8 a = *(const s16x8 *)(kb + r * C::ROWB + 16 * k_swz<D>(r, 2 * kk + g));
+            sacc[jb] = Op::mma(a, qf[kk], kk == 0 ? f32x16{} : sacc[jb]);
+        }
+    }
+
+    // Lane (g, i) holds key 32jb + 8(e/4) + 4g + e%4 of row i in sacc[jb][e].
+    float mx = -INFINITY;
+    if constexpr (MASKED) {
+        // The visible keys of a row form the range [lo, hi] plus the global keys [0, G);
+        // offsets r = key - kv0 - 4g are compile-time constants per element. Scale first
+        // (masked scores become -inf in the scaled domain), then mask.
+        const int base = kv0 + 4 * g;
+        const int hiR = (MASK == 0 ? Nkv - 1 : min(ip, Nkv - 1)) - base;
+        const int loR = (MASK == 2 ? ip - W + 1 : INT_MIN / 2) - base;
+        const int gR = (MASK == 2 ? G : 0) - base;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = jb * 32 + 8 * (e >> 2) + (e & 3);
+                const bool vis = r <= hiR && (MASK != 2 || r >= loR || r < gR);
+                sacc[jb][e] = vis ? sacc[jb][e] * c : -INFINITY;
+                mx = fmaxf(mx, sacc[jb][e]);
+            }
+    } else {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[jb][e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = MASKED ? mx : mx * c;  // tile maximum of the scaled scores
+
+    if (!__all(mt <= m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+
+    float ps = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float p = MASKED ? fast_exp2(sacc[jb][e] - mu)
+                                   : fast_exp2(__builtin_fmaf(sacc[jb][e], c, -mu));
+            sacc[jb][e] = p;
+            ps += p;
+        }
+    l += ps;
+
+    // O^T += V^T P^T over four 16-key chunks. Chunk kc, slot (g, e) is key
+    // 16kc + 8(e/4) + 4g + e%4: P^T is sacc[kc/2][8(kc%2) + e] in place. The V^T operand
+    // comes from two transposed reads of four keys each.
+    // Lane (g, s, j) of a transposed read addresses row 16kc + 8h + 4g + j/4 and the
+    // 8 bytes at element 32db + 16s + 4(j%4): logical chunk 4db + 2s + (j%4)/2.
+    const int trow = 4 * g + ((lane & 15) >> 2);
+    const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int thalf = 8 * (lane & 1);
+#pragma unroll
+    for (int kc = 0; kc < C::BN / 16; ++kc) {
+        const int jb = kc >> 1, o8 = 8 * (kc & 1);
+        const s16x8 pf = Op::pack8(sacc[jb][o8 + 0], sacc[jb][o8 + 1], sacc[jb][o8 + 2],
+                                   sacc[jb][o8 + 3], sacc[jb][o8 + 4], sacc[jb][o8 + 5],
+                                   sacc[jb][o8 + 6], sacc[jb][o8 + 7]);
+        const int r0 = kc * 16 + trow, r1 = r0 + 8;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+            const char *p0 = vb + r0 * C::ROWB + 16 * v_swz<D>(r0, 4 * db + tchunk) + thalf;
+            const char *p1 = vb + r1 * C::ROWB + 16 * v_swz<D>(r1, 4 * db + tchunk) + thalf;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+            const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = Op::mma(a, pf, oacc[db]);
+        }
+    }
+}
 
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(
@@ -164,8 +325,8 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
 {
     using C = Cfg16<D>;
     using Op = Ops16<T>;
-    constexpr int BM = C::BM, BN = C::BN, NT = C::NT, KP = C::KP, VP = C::VP;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    constexpr int BM = C::BM, BN = C::BN;
+    extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
@@ -175,15 +336,18 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
     const int delta = Nkv - Nq;
     const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
 
-    // Q^T fragments (B operand): lane (g, i) holds Q[row i][16kk + 8g .. +7].
+    // Q^T fragments (B operand): lane (g, i) holds Q[row i][16kk + 8g .. +7]. A negative
+    // scale is moved into Q by flipping sign bits (exact), so that c >= 0 below.
     const int wrow0 = q0 + wave * 32;
     const int row = wrow0 + li;
     const int ip = row + delta;
+    const short qsign = c < 0.f ? (short)0x8000 : (short)0;
+    c = fabsf(c);
     s16x8 qf[C::NKK];
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
         if (row < Nq)
-            qf[kk] = *(const s16x8 *)(Q + qbase + (size_t)row * D + 16 * kk + 8 * g);
+            qf[kk] = *(const s16x8 *)(Q + qbase + (size_t)row * D + 16 * kk + 8 * g) ^ qsign;
         else
             qf[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
@@ -195,47 +359,33 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[C::NDB];
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+    for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
 
-    s16x8 kr[C::CPT], vr[C::CPT];
+    // K/V tiles go straight from HBM to LDS (buffer_load ... lds): wave-wide load u of
+    // wave w fills the ROWS_PER_LOAD rows of slot q = 4u + w; lane l lands in physical
+    // chunk l % CHUNKS of row q * ROWS_PER_LOAD + l / CHUNKS, so it fetches the logical
+    // chunk the swizzle stores there. Offsets are relative to the tile's first key.
+    const char *kbh = (const char *)(K + kvbase);
+    const char *vbh = (const char *)(V + kvbase);
+    unsigned koff[C::LOADS], voff[C::LOADS];
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+        const int r = (4 * u + wave) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
+        const int pc = lane % C::CHUNKS;
+        koff[u] = r * C::ROWB + 16 * k_swz<D>(r, pc);
+        voff[u] = r * C::ROWB + 16 * v_swz<D>(r, pc);
+    }
     auto tile_id = [&](int n) { return n < na ? tr.a0 + n : tr.b0 + (n - na); };
-    auto gload = [&](int tile) {
-        const int kv0 = tile * BN;
-#pragma unroll
-        for (int u = 0; u < C::CPT; ++u) {
-            const int id = tid + u * NT, r = id / C::RC, cc = id % C::RC;
-            const int key = kv0 + r;
-            if (key < Nkv) {
-                kr[u] = *(const s16x8 *)(K + kvbase + (size_t)key * D + cc * 8);
-                vr[u] = *(const s16x8 *)(V + kvbase + (size_t)key * D + cc * 8);
-            } else {
-                kr[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                vr[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-        uint16_t *ks = smem + buf * C::SE;
-        uint16_t *vs = ks + C::KE;
-#pragma unroll
-        for (int u = 0; u < C::CPT; ++u) {
-            const int id = tid + u * NT, r = id / C::RC, cc = id % C::RC;
-            *(s16x8 *)(ks + r * KP + cc * 8) = kr[u];
-            *(s16x8 *)(vs + r * VP + cc * 8) = vr[u];
-        }
-    };
-
     if (ntiles > 0) {
-        gload(tile_id(0));
-        lstore(0);
+        issue_tile<D>(kbh, vbh, koff, voff, tile_id(0) * BN, Nkv, (char *)smem, wave);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     for (int n = 0; n < ntiles; ++n) {
         const int tile = tile_id(n);
-        const bool more = n + 1 < ntiles;
-        if (more) gload(tile_id(n + 1));
+        if (n + 1 < ntiles)
+            issue_tile<D>(kbh, vbh, koff, voff, tile_id(n + 1) * BN, Nkv,
+                          (char *)smem + ((n + 1) & 1) * C::STAGEB, wave);
         const int kv0 = tile * BN;
 
         // Wave-uniform visibility of this tile for the wave's 32 rows.
@@ -250,86 +400,19 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
                 if (!(ip1 - kv0 < W) && !(kv0 + BN - 1 < G)) need_mask = true;
             }
         }
-
+        const uint16_t *ks = (const uint16_t *)((const char *)smem + (n & 1) * C::STAGEB);
+        const uint16_t *vs = (const uint16_t *)((const char *)ks + C::TILEB);
         if (!skip) {
-            const uint16_t *ks = smem + (n & 1) * C::SE;
-            const uint16_t *vs = ks + C::KE;
-            f32x16 sacc[2];
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[jb][e] = 0.f;
-            // S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T fragments.
-#pragma unroll
-            for (int kk = 0; kk < C::NKK; ++kk) {
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const s16x8 a = *(const s16x8 *)(ks + (jb * 32 + li) * KP + 16 * kk + 8 * g);
-                    sacc[jb] = Op::mma(a, qf[kk], sacc[jb]);
-                }
-            }
-            // Lane (g, i) holds key 32jb + 8(e/4) + 4g + e%4 of row i in sacc[jb][e].
-            float mt = -INFINITY;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float t = sacc[jb][e] * c;
-                    if (need_mask) {
-                        const int key = kv0 + jb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                        if (key >= Nkv || !key_visible<MASK>(ip, key, W, G)) t = -INFINITY;
-                    }
-                    sacc[jb][e] = t;
-                    mt = fmaxf(mt, t);
-                }
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float mn = fmaxf(m, mt);
-            const float mu = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = fast_exp2(m - mu);
-            m = mn;
-            float ps = 0.f;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = fast_exp2(sacc[jb][e] - mu);
-                    sacc[jb][e] = p;
-                    ps += p;
-                }
-            }
-            l = l * alpha + ps;
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-
-            // O^T += V^T P^T over four 16-key chunks. Chunk kc, slot (g, e) is key
-            // 16kc + 8(e/4) + 4g + e%4: P^T is sacc[kc/2][8(kc%2) + e] in place.
-            const int trow = 4 * g + ((lane & 15) >> 2);
-            const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-            for (int kc = 0; kc < BN / 16; ++kc) {
-                const int jb = kc >> 1, o8 = 8 * (kc & 1);
-                const s16x8 pf = Op::pack8(sacc[jb][o8 + 0], sacc[jb][o8 + 1], sacc[jb][o8 + 2],
-                                           sacc[jb][o8 + 3], sacc[jb][o8 + 4], sacc[jb][o8 + 5],
-                                           sacc[jb][o8 + 6], sacc[jb][o8 + 7]);
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    const uint16_t *vp = vs + (kc * 16 + trow) * VP + db * 32 + tcol;
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vp);
-                    const s16x4 hi =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vp + 8 * VP));
-                    const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[db] = Op::mma(a, pf, oacc[db]);
-                }
-            }
+            if (need_mask)
+                attend_tile<T, D, MASK, true>(ks, vs, qf, oacc, m, l, c, kv0, ip, Nkv, W, G, lane);
+            else
+                attend_tile<T, D, MASK, false>(ks, vs, qf, oacc, m, l, c, kv0, ip, Nkv, W, G, lane);
         }
-        if (more) lstore((n + 1) & 1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
         __syncthreads();
     }
 
-    // Epilogue: both lane halves hold partial sums of the same row.
+    // Epilogue: both lane halves hold partial sums of the same row (same reference max).
     const float lt = l + __shfl_xor(l, 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row < Nq) {
