@@ -96,6 +96,82 @@ __device__ __forceinline__ TileRanges visible_tiles(int q0, int Nq, int Nkv, int
     return r;
 }
 
+// Key-tile schedule of one query tile: the visible tiles, ordered so that the tiles every
+// row of the tile sees completely ("interior": no mask, no skip, no tail) come first and
+// the remaining visible tiles ("edge") last: two interior ranges, then the visible parts of
+// the two gaps the interior leaves (slots for every pairing of gap and visible range).
+constexpr int kRanges = 6;
+struct TileSchedule {
+    int b[kRanges], e[kRanges];
+    int interior, total;
+
+    // Walks the schedule one tile at a time; work beyond an increment happens only when a
+    // range ends.
+    struct Cursor {
+        int k, t, end;
+    };
+    __device__ __forceinline__ Cursor seek(int k) const
+    {
+        Cursor c{kRanges, 0, 0};
+#pragma unroll
+        for (int q = kRanges - 1; q >= 0; --q)
+            if (q >= k && e[q] > b[q]) c = Cursor{q, b[q], e[q]};
+        return c;
+    }
+    __device__ __forceinline__ Cursor begin() const { return seek(0); }
+    __device__ __forceinline__ Cursor next(Cursor c) const
+    {
+        return c.t + 1 < c.end ? Cursor{c.k, c.t + 1, c.end} : seek(c.k + 1);
+    }
+};
+
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+template <int MASK, int BM, int BN>
+__device__ __forceinline__ TileSchedule make_schedule(int q0, int Nq, int Nkv, int W, int G)
+{
+    TileSchedule s;
+#pragma unroll
+    for (int k = 0; k < kRanges; ++k) s.b[k] = s.e[k] = 0;
+    const TileRanges v = visible_tiles<MASK, BM, BN>(q0, Nq, Nkv, W, G);
+    // interior ranges, judged for every row of the tile (padding rows included)
+    const int delta = Nkv - Nq;
+    const int ip0 = q0 + delta, ip1 = q0 + BM - 1 + delta;
+    int lim = Nkv / BN;  // tiles without a key tail
+    if (MASK >= 1) lim = min(lim, max(0, floor_div(ip0 + 1, BN)));  // causal for the first row
+    int i0b = 0, i0e = lim, i1b = 0, i1e = 0;
+    if (MASK == 2) {
+        const int gend = G / BN;                                   // all keys global
+        const int wbeg = max(0, -floor_div(-(ip1 - W + 1), BN));   // in every row's window
+        i0e = min(gend, lim);
+        i1b = max(wbeg, i0e);
+        i1e = lim;
+        if (i1b >= i1e) i1b = i1e = 0;
+    }
+    if (i0e <= i0b) i0b = i0e = 0;
+    s.b[0] = i0b; s.e[0] = i0e;
+    s.b[1] = i1b; s.e[1] = i1e;
+    s.interior = (i0e - i0b) + (i1e - i1b);
+    // edge ranges: the gaps between interior ranges, intersected with the visible ranges
+    const int big = 0x3fffffff;
+    const bool has1 = i1e > i1b;
+    const int c0b = i0e, c0e = has1 ? i1b : big;   // gap after the first interior range
+    const int c1b = has1 ? i1e : 0, c1e = has1 ? big : 0;  // gap after the second one
+    auto put = [&s](int slot, int lo0, int hi0, int lo1, int hi1) {
+        const int lo = max(lo0, lo1), hi = min(hi0, hi1);
+        s.b[slot] = hi > lo ? lo : 0;
+        s.e[slot] = hi > lo ? hi : 0;
+    };
+    put(2, c0b, c0e, v.a0, v.a1);
+    put(3, c0b, c0e, v.b0, v.b1);
+    put(4, c1b, c1e, v.a0, v.a1);
+    put(5, c1b, c1e, v.b0, v.b1);
+    s.total = 0;
+#pragma unroll
+    for (int q = 0; q < kRanges; ++q) s.total += s.e[q] - s.b[q];
+    return s;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T>
@@ -185,6 +261,7 @@ __device__ __forceinline__ void issue_tile(const char *kbh, const char *vbh,
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer resource type exists only for the GPU target
     using C = Cfg16<D>;
+    kv0 = __builtin_amdgcn_readfirstlane(kv0);  // uniform: keeps the descriptors scalar
     // Raw buffer descriptors (gfx9 family word 3: data format 32, no swizzle; stride 0)
     // covering the keys from kv0 to the end: loads at or past that range return zeros.
     const int rest = (int)((unsigned)(Nkv - kv0) * C::ROWB);
@@ -213,17 +290,17 @@ constexpr float kRescaleSlack = 8.0f;
 // qf: Q^T fragments. c = scale * log2(e) >= 0 (a negative scale is folded into Q).
 // MASKED tiles evaluate the element mask (and the key-range tail); others skip it.
 template <typename T, int D, int MASK, bool MASKED>
-__device__ __forceinline__ void attend_tile(const uint16_t *__restrict__ ks,
-                                            const uint16_t *__restrict__ vs,
+__device__ __forceinline__ void attend_tile(const char *__restrict__ st,
+                                            const int (&kofs)[D / 16], const int (&vofs)[D / 32],
                                             const s16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
                                             float &m, float &l, float c, int kv0, int ip,
                                             int Nkv, int W, int G, int lane)
 {
     using C = Cfg16<D>;
     using Op = Ops16<T>;
-    const int g = lane >> 5, li = lane & 31;
-    const char *kb = (const char *)ks;
-    const char *vb = (const char *)vs;
+    const int g = lane >> 5;
+    const char *kb = st;
+    const char *vb = st + C::TILEB;
 
     // S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T fragments. Lane (g, j) reads row
     // 32jb + j, logical chunk 2kk + g.
@@ -232,8 +309,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *__restrict__ ks,
     for (int kk = 0; kk < C::NKK; ++kk) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const int r = jb * 32 + li;
-            const s16x8 a = *(const s16x8 *)(kb + r * C::ROWB + 16 * k_swz<D>(r, 2 * kk + g));
+            const s16x8 a = *(const s16x8 *)(kb + kofs[kk] + jb * 32 * C::ROWB);
             sacc[jb] = Op::mma(a, qf[kk], kk == 0 ? f32x16{} : sacc[jb]);
         }
     }
@@ -294,21 +370,17 @@ __device__ __forceinline__ void attend_tile(const uint16_t *__restrict__ ks,
     // 16kc + 8(e/4) + 4g + e%4: P^T is sacc[kc/2][8(kc%2) + e] in place. The V^T operand
     // comes from two transposed reads of four keys each.
     // Lane (g, s, j) of a transposed read addresses row 16kc + 8h + 4g + j/4 and the
-    // 8 bytes at element 32db + 16s + 4(j%4): logical chunk 4db + 2s + (j%4)/2.
-    const int trow = 4 * g + ((lane & 15) >> 2);
-    const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int thalf = 8 * (lane & 1);
+    // 8 bytes at element 32db + 16s + 4(j%4) (offset vofs[db] for kc = h = 0).
 #pragma unroll
     for (int kc = 0; kc < C::BN / 16; ++kc) {
         const int jb = kc >> 1, o8 = 8 * (kc & 1);
         const s16x8 pf = Op::pack8(sacc[jb][o8 + 0], sacc[jb][o8 + 1], sacc[jb][o8 + 2],
                                    sacc[jb][o8 + 3], sacc[jb][o8 + 4], sacc[jb][o8 + 5],
                                    sacc[jb][o8 + 6], sacc[jb][o8 + 7]);
-        const int r0 = kc * 16 + trow, r1 = r0 + 8;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-            const char *p0 = vb + r0 * C::ROWB + 16 * v_swz<D>(r0, 4 * db + tchunk) + thalf;
-            const char *p1 = vb + r1 * C::ROWB + 16 * v_swz<D>(r1, 4 * db + tchunk) + thalf;
+            const char *p0 = vb + vofs[db] + kc * 16 * C::ROWB;
+            const char *p1 = p0 + 8 * C::ROWB;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
             const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -352,9 +424,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
             qf[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
 
-    const TileRanges tr = visible_tiles<MASK, BM, BN>(q0, Nq, Nkv, W, G);
-    const int na = tr.a1 - tr.a0;
-    const int ntiles = na + (tr.b1 - tr.b0);
+    const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);
 
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[C::NDB];
@@ -375,20 +445,45 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
         koff[u] = r * C::ROWB + 16 * k_swz<D>(r, pc);
         voff[u] = r * C::ROWB + 16 * v_swz<D>(r, pc);
     }
-    auto tile_id = [&](int n) { return n < na ? tr.a0 + n : tr.b0 + (n - na); };
+    // Lane-constant LDS byte offsets of the swizzled operand reads (see attend_tile).
+    int kofs[C::NKK], vofs[C::NDB];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * k_swz<D>(li, 2 * kk + g);
+    {
+        const int trow = 4 * g + ((lane & 15) >> 2);
+        const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+            vofs[db] = trow * C::ROWB + 16 * v_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
+    }
+
+    const int ntiles = sch.total;
+    char *const lds = (char *)smem;
+    TileSchedule::Cursor cur = sch.begin(), nxt = sch.next(cur);
     if (ntiles > 0) {
-        issue_tile<D>(kbh, vbh, koff, voff, tile_id(0) * BN, Nkv, (char *)smem, wave);
+        issue_tile<D>(kbh, vbh, koff, voff, cur.t * BN, Nkv, lds, wave);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
-    for (int n = 0; n < ntiles; ++n) {
-        const int tile = tile_id(n);
+    // Interior tiles: every row sees every key, no per-wave decisions.
+    for (int n = 0; n < sch.interior; ++n) {
+        const int kv0 = cur.t * BN;
         if (n + 1 < ntiles)
-            issue_tile<D>(kbh, vbh, koff, voff, tile_id(n + 1) * BN, Nkv,
-                          (char *)smem + ((n + 1) & 1) * C::STAGEB, wave);
-        const int kv0 = tile * BN;
-
-        // Wave-uniform visibility of this tile for the wave's 32 rows.
+            issue_tile<D>(kbh, vbh, koff, voff, nxt.t * BN, Nkv, lds + ((n + 1) & 1) * C::STAGEB,
+                          wave);
+        attend_tile<T, D, MASK, false>(lds + (n & 1) * C::STAGEB, kofs, vofs, qf, oacc, m, l, c,
+                                       kv0, ip, Nkv, W, G, lane);
+        cur = nxt;
+        nxt = sch.next(nxt);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
+        __syncthreads();
+    }
+    // Edge tiles: per wave, skip the tile, take it whole, or apply the element mask.
+    for (int n = sch.interior; n < ntiles; ++n) {
+        const int kv0 = cur.t * BN;
+        if (n + 1 < ntiles)
+            issue_tile<D>(kbh, vbh, koff, voff, nxt.t * BN, Nkv, lds + ((n + 1) & 1) * C::STAGEB,
+                          wave);
         bool skip = wrow0 >= Nq;
         bool need_mask = kv0 + BN > Nkv;
         if (MASK >= 1) {
@@ -400,15 +495,23 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
                 if (!(ip1 - kv0 < W) && !(kv0 + BN - 1 < G)) need_mask = true;
             }
         }
-        const uint16_t *ks = (const uint16_t *)((const char *)smem + (n & 1) * C::STAGEB);
-        const uint16_t *vs = (const uint16_t *)((const char *)ks + C::TILEB);
-        if (!skip) {
+        const char *st = lds + (n & 1) * C::STAGEB;
+        if (MASK == 0) {
+            // without a mask the only edge tile is the key tail
+            if (!skip)
+                attend_tile<T, D, MASK, true>(st, kofs, vofs, qf, oacc, m, l, c, kv0, ip, Nkv, W,
+                                              G, lane);
+        } else if (!skip) {
             if (need_mask)
-                attend_tile<T, D, MASK, true>(ks, vs, qf, oacc, m, l, c, kv0, ip, Nkv, W, G, lane);
+                attend_tile<T, D, MASK, true>(st, kofs, vofs, qf, oacc, m, l, c, kv0, ip, Nkv, W,
+                                              G, lane);
             else
-                attend_tile<T, D, MASK, false>(ks, vs, qf, oacc, m, l, c, kv0, ip, Nkv, W, G, lane);
+                attend_tile<T, D, MASK, false>(st, kofs, vofs, qf, oacc, m, l, c, kv0, ip, Nkv, W,
+                                               G, lane);
         }
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
+        cur = nxt;
+        nxt = sch.next(nxt);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
