@@ -103,10 +103,12 @@ def test_decode_full_size_every_element():
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("lens", [[1, 2, 63, 64, 65, 255, 256, 257], [8192, 4096, 7000, 1]])
-def test_decode_ragged_lengths(dtype, lens):
+@pytest.mark.parametrize("lens,max_len", [([1, 2, 63, 64, 65, 255, 256, 257], 8192),
+                                          ([8192, 4096, 7000, 1], 8192),
+                                          ([16000, 300, 16384], 16384)])
+def test_decode_ragged_lengths(dtype, lens, max_len):
     w, inp = workloads.gen_workload("decode_f16", dtype=dtype, lens=lens, S=len(lens), H=16,
-                                    max_len=8192)
+                                    max_len=max_len)
     scale = workloads.default_scale(w["d"])
     o, lse = run_decode(inp, scale)
     ro, rl = oracle.decode_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],

@@ -70,7 +70,7 @@ size_t fa_decode_paged_workspace_bytes(int num_seqs, int H, int d, int max_pages
                                        int page_size)
 {
     if (num_seqs < 1 || H < 1 || d < 1 || max_pages_per_seq < 1 || page_size < 1) return 0;
-    const size_t splits = (size_t)teaf::decode_max_splits(max_pages_per_seq, page_size);
+    const size_t splits = (size_t)teaf::decode_workspace_splits(max_pages_per_seq, page_size);
     return (size_t)num_seqs * H * splits * ((size_t)d + 1) * sizeof(float);
 }
 

@@ -7,12 +7,14 @@
 //
 // Decode is a matrix-vector product per (sequence, head): about one flop per byte of K/V,
 // so it is bound by HBM bandwidth and uses plain vector FMAs, not the matrix cores.
-// Split-KV: the split pass gives each workgroup 64 consecutive tokens (a quarter page,
-// never crossing a page) of one sequence for 8 heads. A page stores [token][head][d], so
-// those 8 heads of one token are 2 KB contiguous and every load instruction of a wave
-// covers 1 KB contiguous. Each workgroup keeps an online softmax per head over its tokens
-// and writes a partial output O_s (already divided by its own sum) and its log-sum-exp
-// lse_s. The combine pass merges the splits of each (sequence, head):
+// Split-KV: the split pass gives each workgroup a run of consecutive tokens of one
+// sequence (64, 128 or a whole 256-token page, never crossing a page) for 16 heads (8 if H
+// is not a multiple of 16). A page stores [token][head][d], so those heads of one token
+// are contiguous (4 KB for 16 heads) and every wave-wide load covers 1 KB. K and V stream
+// through non-temporal loads one batch of tokens ahead of the math. Each workgroup keeps an
+// online softmax per head over its tokens and writes a partial output O_s (already divided
+// by its own sum) and its log-sum-exp lse_s. The combine pass merges the splits of each
+// (sequence, head):
 //   lse = log sum_s exp(lse_s),  O = sum_s exp(lse_s - lse) O_s,
 // which equals attention over the union of the splits (the same identity that lets the
 // multimodal case of the boost article split one attention into several calls).
@@ -68,144 +70,272 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
-// grid (max_splits, S, H / 8); 256 threads. Thread t: d chunk c = t % 16 (8 values),
-// local head hl = (t / 16) % 8, token lane tl = t / 128 (tokens tl, tl + 2, ...).
-template <typename T>
+// K/V are read once per call: non-temporal loads stream them past the caches.
+__device__ __forceinline__ s16x8 stream_load(const uint16_t *p)
+{
+    return __builtin_nontemporal_load((const s16x8 *)p);
+}
+
+// Split pass. grid (H / HW, max_splits, S), 256 threads; a workgroup owns SPLIT
+// consecutive tokens (inside one page) of one sequence for HW heads. A page stores
+// [token][head][d], so the HW heads of one token are HW * 256 bytes contiguous (the whole
+// 8 KB row when HW = H = 32): thread t reads 16-byte chunk t % 16 of head (t / 16) % HW'
+// and its 16 apart companions, and each wave-wide load covers 1 KB contiguous.
+//   HW = 32: 2 heads per thread, all 256 threads on one token;
+//   HW = 16: 1 head per thread, all 256 threads on one token;
+//   HW = 8 : 1 head per thread, two token lanes (tokens tl, tl + 2, ...).
+// Loads run one batch of tokens ahead of the math (two register buffers).
+template <typename T, int HW, int SPLIT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t *__restrict__ Qp, const uint16_t *__restrict__ Kp,
     const uint16_t *__restrict__ Vp, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, float *__restrict__ part_o,
     float *__restrict__ part_lse, int H, int max_pages, int max_splits, float c)
 {
-    const int sp = blockIdx.x, s = blockIdx.y, hg = blockIdx.z;
+    constexpr int PAIRS = HW * 16;                       // (head, chunk) pairs per token
+    constexpr int HPT = PAIRS > kThreads ? PAIRS / kThreads : 1;   // heads per thread
+    constexpr int TL = PAIRS < kThreads ? kThreads / PAIRS : 1;    // token lanes
+    constexpr int B = 4;                                 // tokens per lane per batch
+    constexpr int NB = SPLIT / (B * TL);                 // batches per split
+    static_assert(NB % 2 == 0, "batches are processed in pairs");
+
+    const int hg = blockIdx.x, sp = blockIdx.y, s = blockIdx.z;
     const int L = seq_lens[s];
-    const int t0 = sp * kDecodeSplit;
+    const int t0 = sp * SPLIT;
     if (t0 >= L) return;  // workgroup-uniform
     const int tid = threadIdx.x;
-    const int cc = tid & 15, hl = (tid >> 4) & 7, tl = tid >> 7;
-    const int h = hg * kDecodeHeads + hl;
-    const int ntok = min(kDecodeSplit, L - t0);
+    const int cc = tid & 15;
+    const int hr = (tid >> 4) % (HW < 16 ? HW : 16);
+    const int tl = TL > 1 ? tid / PAIRS : 0;
+    const int ntok = min(SPLIT, L - t0);
     const int page = page_table[(size_t)s * max_pages + t0 / kPage];
     const int slot0 = t0 % kPage;
-    // element offset of (token slot0, head h, chunk cc) in the page pool
-    const size_t base = (((size_t)page * kPage + slot0) * H + h) * kD + cc * 8;
     const size_t tstride = (size_t)H * kD;  // elements between consecutive tokens
-
-    float q[8];
-    to_float8<T>(*(const s16x8 *)(Qp + ((size_t)s * H + h) * kD + cc * 8), q);
-
-    float m = -INFINITY, l = 0.f, o[8];
+    size_t base[HPT];
+    float q[HPT][8], m[HPT], l[HPT], o[HPT][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
-
-    for (int b0 = 0; b0 < kDecodeSplit; b0 += 2 * kBatch) {
-        s16x8 kx[kBatch], vx[kBatch];
+    for (int j = 0; j < HPT; ++j) {
+        const int h = hg * HW + hr + 16 * j;
+        base[j] = (((size_t)page * kPage + slot0) * H + h) * kD + cc * 8;
+        to_float8<T>(*(const s16x8 *)(Qp + ((size_t)s * H + h) * kD + cc * 8), q[j]);
+        m[j] = -INFINITY;
+        l[j] = 0.f;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int tt = b0 + tl + 2 * u;
-            if (tt < ntok) {
-                kx[u] = *(const s16x8 *)(Kp + base + tt * tstride);
-                vx[u] = *(const s16x8 *)(Vp + base + tt * tstride);
-            } else {
-                kx[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                vx[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    }
+
+    s16x8 kx[2][HPT][B], vx[2][HPT][B];
+    auto load = [&](int buf, int b) {
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int tt = (b * B + u) * TL + tl;
+#pragma unroll
+            for (int j = 0; j < HPT; ++j) {
+                if (tt < ntok) {
+                    kx[buf][j][u] = stream_load(Kp + base[j] + tt * tstride);
+                    vx[buf][j][u] = stream_load(Vp + base[j] + tt * tstride);
+                } else {
+                    kx[buf][j][u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                    vx[buf][j][u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                }
             }
         }
-        float sc[kBatch];
-        float mb = -INFINITY;
+    };
+    auto consume = [&](int buf, int b) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            float kf[8];
-            to_float8<T>(kx[u], kf);
-            float dot = 0.f;
+        for (int j = 0; j < HPT; ++j) {
+            float sc[B];
+            float mb = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kf[e], dot);
-            dot = row16_sum(dot);
-            const int tt = b0 + tl + 2 * u;
-            sc[u] = tt < ntok ? dot * c : -INFINITY;
-            mb = fmaxf(mb, sc[u]);
+            for (int u = 0; u < B; ++u) {
+                float kf[8];
+                to_float8<T>(kx[buf][j][u], kf);
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot = fmaf(q[j][e], kf[e], dot);
+                dot = row16_sum(dot);
+                const int tt = (b * B + u) * TL + tl;
+                sc[u] = tt < ntok ? dot * c : -INFINITY;
+                mb = fmaxf(mb, sc[u]);
+            }
+            const float mn = fmaxf(m[j], mb);
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - mu);
+            m[j] = mn;
+            l[j] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[j][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const float p = __builtin_amdgcn_exp2f(sc[u] - mu);
+                l[j] += p;
+                float vf[8];
+                to_float8<T>(vx[buf][j][u], vf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[j][e] = fmaf(p, vf[e], o[j][e]);
+            }
         }
-        const float mn = fmaxf(m, mb);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m - mu);
-        m = mn;
-        l *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= alpha;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const float p = __builtin_amdgcn_exp2f(sc[u] - mu);
-            l += p;
-            float vf[8];
-            to_float8<T>(vx[u], vf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(p, vf[e], o[e]);
-        }
+    };
+
+    load(0, 0);
+    for (int b = 0; b < NB; b += 2) {
+        load(1, b + 1);
+        consume(0, b);
+        if (b + 2 < NB) load(0, b + 2);
+        consume(1, b + 1);
     }
 
-    // Merge the two token lanes (threads t and t + 128) through LDS.
-    __shared__ float xm[128], xl[128], xo[128 * 9];
-    if (tl == 1) {
-        xm[tid - 128] = m;
-        xl[tid - 128] = l;
+    // Merge the token lanes through LDS (HW = 8 only), then write the split's partials.
+    if constexpr (TL > 1) {
+        __shared__ float xm[PAIRS], xl[PAIRS], xo[PAIRS * 9];
+        if (tl == 1) {
+            xm[tid - PAIRS] = m[0];
+            xl[tid - PAIRS] = l[0];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xo[(tid - 128) * 9 + e] = o[e];
-    }
-    __syncthreads();
-    if (tl == 0) {
+            for (int e = 0; e < 8; ++e) xo[(tid - PAIRS) * 9 + e] = o[0][e];
+        }
+        __syncthreads();
+        if (tl != 0) return;
         const float m1 = xm[tid], l1 = xl[tid];
-        const float mn = fmaxf(m, m1);
+        const float mn = fmaxf(m[0], m1);
         const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float a0 = __builtin_amdgcn_exp2f(m - mu), a1 = __builtin_amdgcn_exp2f(m1 - mu);
-        const float lt = l * a0 + l1 * a1;
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float a0 = __builtin_amdgcn_exp2f(m[0] - mu), a1 = __builtin_amdgcn_exp2f(m1 - mu);
+        l[0] = l[0] * a0 + l1 * a1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[0][e] = o[0][e] * a0 + xo[tid * 9 + e] * a1;
+        m[0] = mn;
+    }
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+        const int h = hg * HW + hr + 16 * j;
+        const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
         const size_t slot = ((size_t)s * H + h) * max_splits + sp;
         float *po = part_o + slot * kD + cc * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) po[e] = (o[e] * a0 + xo[tid * 9 + e] * a1) * inv;
-        if (cc == 0) part_lse[slot] = lt > 0.f ? mn + __builtin_amdgcn_logf(lt) : -INFINITY;
+        for (int e = 0; e < 8; ++e) po[e] = o[j][e] * inv;
+        if (cc == 0) part_lse[slot] = l[j] > 0.f ? m[j] + __builtin_amdgcn_logf(l[j]) : -INFINITY;
     }
 }
 
-// grid (S, H); 128 threads, one per output column. Partial lse values are in log2 units.
+// grid (S, H); 256 threads = 4 groups of 64. Group q takes splits q, q + 4, ...; thread
+// (q, i) accumulates columns 2i and 2i+1 over them, issuing the loads of up to 32 splits at
+// once, then the groups are summed through LDS. Partial lse values are in log2 units.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineGroups = kCombineThreads / 64;
+constexpr int kCombineBatch = 32;
+
 template <typename T>
-__global__ __launch_bounds__(kD) void decode_combine_kernel(
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse,
     const int32_t *__restrict__ seq_lens, uint16_t *__restrict__ O, float *__restrict__ LSE,
-    int H, int max_splits)
+    int H, int max_splits, int split)
 {
-    const int s = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-    const int ns = (seq_lens[s] + kDecodeSplit - 1) / kDecodeSplit;
+    __shared__ float red[kCombineThreads];
+    __shared__ float2 acc_s[kCombineGroups][64];
+    const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int q = tid >> 6, i = tid & 63;
+    const int ns = (seq_lens[s] + split - 1) / split;
     const size_t slot0 = ((size_t)s * H + h) * max_splits;
+
+    // maximum of the partial lse values
     float mx = -INFINITY;
-    for (int i = 0; i < ns; ++i) mx = fmaxf(mx, part_lse[slot0 + i]);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    float w = 0.f, acc = 0.f;
-    for (int i = 0; i < ns; ++i) {
-        const float a = __builtin_amdgcn_exp2f(part_lse[slot0 + i] - mu);
-        w += a;
-        acc = fmaf(a, part_o[(slot0 + i) * kD + d], acc);
+    for (int j = tid; j < ns; j += kCombineThreads) mx = fmaxf(mx, part_lse[slot0 + j]);
+    red[tid] = mx;
+    __syncthreads();
+    for (int w = kCombineThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+        __syncthreads();
     }
-    O[((size_t)s * H + h) * kD + d] = from_float<T>(w > 0.f ? acc / w : 0.f);
-    if (LSE != nullptr && d == 0)
-        LSE[(size_t)s * H + h] = w > 0.f ? (mu + __builtin_amdgcn_logf(w)) * kLn2 : -INFINITY;
+    const float mu = red[0] == -INFINITY ? 0.f : red[0];
+    __syncthreads();
+
+    float2 acc = {0.f, 0.f};
+    float wsum = 0.f;
+    for (int j0 = q; j0 < ns; j0 += kCombineGroups * kCombineBatch) {
+        float2 o[kCombineBatch];
+        float lw[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int j = j0 + kCombineGroups * u;
+            o[u] = j < ns ? *(const float2 *)(part_o + (slot0 + j) * kD + 2 * i) : float2{0.f, 0.f};
+            lw[u] = j < ns ? part_lse[slot0 + j] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const float w = __builtin_amdgcn_exp2f(lw[u] - mu);
+            acc.x = fmaf(w, o[u].x, acc.x);
+            acc.y = fmaf(w, o[u].y, acc.y);
+            wsum += w;
+        }
+    }
+    acc_s[q][i] = acc;
+    red[tid] = wsum;
+    __syncthreads();
+    if (q == 0) {
+        float2 t = acc_s[0][i];
+        float wt = red[i];
+#pragma unroll
+        for (int g = 1; g < kCombineGroups; ++g) {
+            t.x += acc_s[g][i].x;
+            t.y += acc_s[g][i].y;
+            wt += red[64 * g + i];
+        }
+        const float inv = wt > 0.f ? 1.f / wt : 0.f;
+        uint16_t *op = O + ((size_t)s * H + h) * kD + 2 * i;
+        op[0] = from_float<T>(t.x * inv);
+        op[1] = from_float<T>(t.y * inv);
+        if (LSE != nullptr && i == 0)
+            LSE[(size_t)s * H + h] = wt > 0.f ? (mu + __builtin_amdgcn_logf(wt)) * kLn2 : -INFINITY;
+    }
 }
+
+template <typename T, int HW, int SPLIT>
+hipError_t launch_split(const DecodeArgs &a, hipStream_t st, int max_splits, float *part_o,
+                        float *part_lse)
+{
+    hipLaunchKernelGGL((decode_split_kernel<T, HW, SPLIT>),
+                       dim3((unsigned)(a.H / HW), (unsigned)max_splits, (unsigned)a.S),
+                       dim3(kThreads), 0, st, (const uint16_t *)a.q, (const uint16_t *)a.k_pages,
+                       (const uint16_t *)a.v_pages, a.page_table, a.seq_lens, part_o, part_lse,
+                       a.H, a.max_pages, max_splits, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <typename T, int HW>
+hipError_t launch_width(const DecodeArgs &a, hipStream_t st, int split, float *part_o,
+                        float *part_lse)
+{
+    const int max_splits = (int)(((long)a.max_pages * kPage + split - 1) / split);
+    if (split == 256) return launch_split<T, HW, 256>(a, st, max_splits, part_o, part_lse);
+    if (split == 128) return launch_split<T, HW, 128>(a, st, max_splits, part_o, part_lse);
+    return launch_split<T, HW, 64>(a, st, max_splits, part_o, part_lse);
+}
+
+// Largest split (fewer, longer streams and fewer partials; measured fastest on the 8 x
+// 4096..8192-token workload) that still gives at least kMinSplitGroups workgroups when
+// every sequence is as long as the page table allows.
+constexpr long kMinSplitGroups = 512;
 
 template <typename T>
 hipError_t launch(const DecodeArgs &a, hipStream_t st)
 {
-    const int max_splits = decode_max_splits(a.max_pages, a.page_size);
+    const int hw = a.H % 16 == 0 ? 16 : 8;
+    int split = 64;
+    for (int cand = 256; cand > 64; cand /= 2)
+        if ((long)a.S * (a.H / hw) * (((long)a.max_pages * kPage) / cand) >= kMinSplitGroups) {
+            split = cand;
+            break;
+        }
+    const int ws_splits = decode_workspace_splits(a.max_pages, a.page_size);
     float *part_o = (float *)a.workspace;
-    float *part_lse = part_o + (size_t)a.S * a.H * max_splits * kD;
-    hipLaunchKernelGGL(decode_split_kernel<T>,
-                       dim3((unsigned)max_splits, (unsigned)a.S, (unsigned)(a.H / kDecodeHeads)),
-                       dim3(kThreads), 0, st, (const uint16_t *)a.q, (const uint16_t *)a.k_pages,
-                       (const uint16_t *)a.v_pages, a.page_table, a.seq_lens, part_o, part_lse,
-                       a.H, a.max_pages, max_splits, a.scale * kLog2e);
-    hipError_t e = hipGetLastError();
+    float *part_lse = part_o + (size_t)a.S * a.H * ws_splits * kD;
+    const hipError_t e = hw == 16 ? launch_width<T, 16>(a, st, split, part_o, part_lse)
+                                  : launch_width<T, 8>(a, st, split, part_o, part_lse);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3((unsigned)a.S, (unsigned)a.H), dim3(kD), 0,
-                       st, part_o, part_lse, a.seq_lens, (uint16_t *)a.o, a.lse, a.H, max_splits);
+    const int max_splits = (int)(((long)a.max_pages * kPage + split - 1) / split);
+    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3((unsigned)a.S, (unsigned)a.H),
+                       dim3(kCombineThreads), 0, st, part_o, part_lse, a.seq_lens,
+                       (uint16_t *)a.o, a.lse, a.H, max_splits, split);
     return hipGetLastError();
 }
 

@@ -27,15 +27,18 @@ struct DecodeArgs {
     void *workspace;
 };
 
-// Tokens of one sequence handled by one workgroup of the split pass.
-constexpr int kDecodeSplit = 64;
-// Heads handled by one workgroup of the split pass.
+// Split pass of paged decode: one workgroup takes `split` consecutive tokens of one
+// sequence (64, 128 or the whole 256-token page; a split never crosses a page). The host
+// picks the largest split that still yields enough workgroups; the workspace is sized for
+// the smallest, so it fits every choice.
+constexpr int kDecodeMinSplit = 64;
+// Heads of one workgroup of the split pass: 16 when H is a multiple of 16, else 8.
 constexpr int kDecodeHeads = 8;
 
-inline int decode_max_splits(int max_pages, int page_size)
+inline int decode_workspace_splits(int max_pages, int page_size)
 {
     long tokens = (long)max_pages * page_size;
-    return (int)((tokens + kDecodeSplit - 1) / kDecodeSplit);
+    return (int)((tokens + kDecodeMinSplit - 1) / kDecodeMinSplit);
 }
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
