@@ -241,9 +241,13 @@ def main():
             torch.cuda.empty_cache()
         d = bench_decode("decode_f16", max(10, args.steps // 4), max(3, args.warmup // 4), torch,
                          fa, workloads)
+        split_t = load_traffic("decode_split_f16_h16_s256_decode_f16")
+        comb_t = load_traffic("decode_combine_f16_decode_f16")
         others["decode_f16"] = dict(us=round(d["ms"] * 1e3, 2), gbs=round(d["gbs"], 1),
                                     frac_hbm_peak=round(d["gbs"] / PEAK_HBM_GBS, 4),
                                     bytes=d["bytes"], seq_lens=d["seq_lens"],
+                                    traffic=None if split_t is None or comb_t is None
+                                    else split_t + comb_t,
                                     note="split + combine kernels, L2/MALL not flushed")
         print(f"[bench] decode_f16: {d['ms'] * 1e3:.1f} us, {d['gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
