@@ -10,19 +10,24 @@
 // denominator in fp32); P is rounded to the input type for the P V product.
 //
 // gfx950 mapping (not the pages' Ascend tiling, which was sized for the 910's buffers):
-//  * 256 threads = 4 wave64s, 128 query rows per workgroup, 32 rows per wave;
-//    key/value tiles of 64 rows, double-buffered in LDS (prefetch of tile n+1 from HBM
-//    into registers overlaps the math on tile n, then lands in the other LDS buffer).
+//  * 256 threads = 4 wave64s, 128 query rows per workgroup, 32 rows per wave, two
+//    workgroups per CU; key/value tiles of 32 rows.
+//  * K and V tiles go straight from HBM into a 4-slot LDS ring (buffer_load ... lds), two
+//    tiles ahead of their first use; a workgroup barrier per tile waits only for LDS traffic
+//    and for the one tile it publishes.
 //  * The score block is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,
-//    f16}: lane (g, i) then holds 16 keys of query row i per 32-key block, so the row max
-//    and row sum are in-lane reductions plus one exchange with lane i^32, and the fp32
+//    f16}: lane (g, i) then holds 16 keys of query row i per 32-key tile, so the row max
+//    and row sum are in-lane reductions plus one cross-half register swap, and the fp32
 //    accumulator converts in place into the B operand (P^T) of O^T = V^T P^T.
+//  * Software pipeline per wave: the matrix cores compute the scores of tile t+1 while the
+//    vector unit exponentiates tile t, then accumulate P(t) V(t) while the vector unit sums
+//    P(t) and takes the maximum of tile t+1; scheduling barriers fix that order.
 //  * V stays row-major in LDS; the V^T operand is read with ds_read_b64_tr_b16, whose
 //    16-lane transpose hands each lane four consecutive keys of one column.
 //  * exp(x) is evaluated as 2^(x log2 e) with v_exp_f32; the log2 e factor is folded into
-//    the score scale, so each score costs one multiply before the exponential.
-//  * Tiles that a mask hides from every row are never loaded; tiles it hides from one
-//    wave's rows skip that wave's math; only edge tiles evaluate the element mask.
+//    the score scale, which enters through the FMA that subtracts the row maximum.
+//  * Tiles that a mask hides from every row are never loaded; tiles every row sees
+//    completely skip the element mask, which only edge tiles evaluate.
 //  * Workgroup ids are remapped so the query tiles of one (batch, head) run on one XCD and
 //    share its L2 copy of K and V; the query tiles with the most visible keys go first.
 //
@@ -49,6 +54,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kXcds = 8;
+
 
 // Hardware hands consecutive workgroup ids to the 8 XCDs in turn. Map id w (of n) to a
 // logical index so that each XCD receives one contiguous run of logical indices.
@@ -174,6 +180,25 @@ __device__ __forceinline__ TileSchedule make_schedule(int q0, int Nq, int Nkv, i
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum that propagates NaN; it needs no quieting of its inputs, so a chain of them maps to
+// three-input maximum instructions.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Combine a value with the one held by lane ^ 32 (the other half of the wave) through a
+// cross-half register swap, without a round trip through LDS.
+__device__ __forceinline__ float half_swap_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T>
 struct Ops16;
 
@@ -221,19 +246,6 @@ struct Ops16<_Float16> {
 
 // ------------------------------------------------------------------ 16-bit kernel
 
-template <int D>
-struct Cfg16 {
-    static constexpr int BM = 128, BN = 64, NT = 256;
-    static constexpr int ROWB = D * 2;                 // bytes of one K or V row
-    static constexpr int TILEB = BN * ROWB;            // bytes of one K (or V) tile
-    static constexpr int STAGEB = 2 * TILEB;           // K tile then V tile
-    static constexpr int LDS_BYTES = 2 * STAGEB;       // two stages
-    static constexpr int CHUNKS = ROWB / 16;           // 16-byte chunks per row
-    static constexpr int ROWS_PER_LOAD = 64 / CHUNKS;  // rows one wave-wide 16-byte load fills
-    static constexpr int LOADS = BN / ROWS_PER_LOAD / 4;  // loads per wave per tile and tensor
-    static constexpr int NKK = D / 16, NDB = D / 32;
-};
-
 // LDS tiles are unpadded rows with an XOR swizzle of the 16-byte chunks (an involution:
 // the same function maps logical to physical and back). Chosen against the 64-bank LDS:
 // a ds_read_b128 serves 16 lanes per cycle, here 16 consecutive K rows at one logical
@@ -251,34 +263,6 @@ __device__ __forceinline__ int v_swz(int row, int chunk)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Issue this wave's share of the direct HBM-to-LDS loads of the K and V tile that starts
-// at key kv0 into the LDS stage `st`. Rows past Nkv read as zeros (buffer range check).
-template <int D>
-__device__ __forceinline__ void issue_tile(const char *kbh, const char *vbh,
-                                           const unsigned (&koff)[Cfg16<D>::LOADS],
-                                           const unsigned (&voff)[Cfg16<D>::LOADS], int kv0,
-                                           int Nkv, char *st, int wave)
-{
-#if defined(__HIP_DEVICE_COMPILE__)  // the buffer resource type exists only for the GPU target
-    using C = Cfg16<D>;
-    kv0 = __builtin_amdgcn_readfirstlane(kv0);  // uniform: keeps the descriptors scalar
-    // Raw buffer descriptors (gfx9 family word 3: data format 32, no swizzle; stride 0)
-    // covering the keys from kv0 to the end: loads at or past that range return zeros.
-    const int rest = (int)((unsigned)(Nkv - kv0) * C::ROWB);
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(kbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(vbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
-#pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-        const int slot = (4 * u + wave) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(st + slot), 16, koff[u], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(st + C::TILEB + slot), 16,
-                                                 voff[u], 0, 0, 0);
-    }
-#endif
-}
-
 // The running maximum is only moved (and O, l rescaled) when a row's new maximum exceeds
 // the one in use by more than this many powers of two; until then probabilities are taken
 // relative to the stale maximum and stay below 2^8, which fp32 sums and 16-bit P hold
@@ -286,121 +270,223 @@ __device__ __forceinline__ void issue_tile(const char *kbh, const char *vbh,
 // reference value, and the final division removes it.
 constexpr float kRescaleSlack = 8.0f;
 
-// One 64-key tile for the 32 query rows of a wave. ks/vs: the tile's K and V in LDS.
-// qf: Q^T fragments. c = scale * log2(e) >= 0 (a negative scale is folded into Q).
-// MASKED tiles evaluate the element mask (and the key-range tail); others skip it.
-template <typename T, int D, int MASK, bool MASKED>
-__device__ __forceinline__ void attend_tile(const char *__restrict__ st,
-                                            const int (&kofs)[D / 16], const int (&vofs)[D / 32],
-                                            const s16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                            float &m, float &l, float c, int kv0, int ip,
-                                            int Nkv, int W, int G, int lane)
+// Each wave owns 32 query rows and walks 32-key tiles, software-pipelined: while the
+// matrix cores form the scores of tile t+1, the vector unit turns the scores of tile t into
+// probabilities; while they add P(t) V(t) into the accumulator, the vector unit sums P(t)
+// and takes the row maximum of tile t+1. The instruction order is fixed with scheduling
+// barriers. K and V tiles stream from HBM into a ring of NS LDS slots, NS - 2 tiles ahead of
+// their first use.
+
+template <int D, int NS, int NW_>
+struct CfgSP {
+    static constexpr int NW = NW_, BM = 32 * NW, BN = 32, NT = 64 * NW;
+    static constexpr int ROWB = D * 2;                 // bytes of one K or V row
+    static constexpr int TILEB = BN * ROWB;            // bytes of one K (or V) tile
+    static constexpr int VREG = NS * TILEB;            // V ring starts after the K ring
+    static constexpr int LDS_BYTES = 2 * NS * TILEB;
+    static constexpr int CHUNKS = ROWB / 16;
+    static constexpr int ROWS_PER_LOAD = 64 / CHUNKS;  // rows one wave-wide 16-byte load fills
+    static constexpr int KL = TILEB / 1024;            // wave-wide loads per K (or V) tile
+    static constexpr int LPW = 2 * KL / NW;            // loads per wave per tile (K and V)
+    static_assert(LPW * NW == 2 * KL, "tile loads must split evenly over the waves");
+    static constexpr int NKK = D / 16, NDB = D / 32;
+    static constexpr int KPF = 3;                      // K fragment reads in flight
+    static constexpr int VPF = 2;                      // V fragment read pairs in flight
+};
+
+// Wait until at most `newer` tiles' loads (LPW per tile, this wave's share) are still in
+// flight; loads complete in issue order. vmcnt takes an immediate (6 bits, split over
+// bits 3:0 and 15:14; expcnt and lgkmcnt left unconstrained), hence one case per count.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+template <int LPW, int K>
+__device__ __forceinline__ void wait_tiles(int newer)
 {
-    using C = Cfg16<D>;
-    using Op = Ops16<T>;
-    const int g = lane >> 5;
-    const char *kb = st;
-    const char *vb = st + C::TILEB;
-
-    // S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T fragments. Lane (g, j) reads row
-    // 32jb + j, logical chunk 2kk + g.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) {
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const s16x8 a = *(const s16x8 *)(kb + kofs[kk] + jb * 32 * C::ROWB);
-            sacc[jb] = Op::mma(a, qf[kk], kk == 0 ? f32x16{} : sacc[jb]);
-        }
-    }
-
-    // Lane (g, i) holds key 32jb + 8(e/4) + 4g + e%4 of row i in sacc[jb][e].
-    float mx = -INFINITY;
-    if constexpr (MASKED) {
-        // The visible keys of a row form the range [lo, hi] plus the global keys [0, G);
-        // offsets r = key - kv0 - 4g are compile-time constants per element. Scale first
-        // (masked scores become -inf in the scaled domain), then mask.
-        const int base = kv0 + 4 * g;
-        const int hiR = (MASK == 0 ? Nkv - 1 : min(ip, Nkv - 1)) - base;
-        const int loR = (MASK == 2 ? ip - W + 1 : INT_MIN / 2) - base;
-        const int gR = (MASK == 2 ? G : 0) - base;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = jb * 32 + 8 * (e >> 2) + (e & 3);
-                const bool vis = r <= hiR && (MASK != 2 || r >= loR || r < gR);
-                sacc[jb][e] = vis ? sacc[jb][e] * c : -INFINITY;
-                mx = fmaxf(mx, sacc[jb][e]);
-            }
+    static_assert(K * LPW < 64, "vmcnt field");
+    if constexpr (K <= 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     } else {
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[jb][e]);
+        if (newer >= K)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(K * LPW));
+        else
+            wait_tiles<LPW, K - 1>(newer);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = MASKED ? mx : mx * c;  // tile maximum of the scaled scores
+}
 
+// Workgroup barrier for the LDS ring: waits for this wave's LDS instructions only. The
+// direct-to-LDS loads of tiles further ahead stay in flight (the compiler's fences would
+// wait for every outstanding load, since those loads write LDS); their completion is
+// awaited explicitly with wait_tiles before the barrier that publishes a tile. The empty
+// asm statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void ring_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// Direct HBM-to-LDS loads of this wave's share of the K and V tile that starts at key kv0.
+// Load i of a tile (i < KL: K, else V) fills 1 KB, i.e. ROWS_PER_LOAD rows, of its LDS
+// tile; wave w issues loads w, w + NW, ... off[u]: this lane's byte offset in the tile.
+template <typename C>
+__device__ __forceinline__ void issue_kv(const char *kbh, const char *vbh,
+                                         const unsigned (&off)[C::LPW], int kv0, int Nkv,
+                                         char *kdst, char *vdst, int wave)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    kv0 = __builtin_amdgcn_readfirstlane(kv0);
+    const int rest = (int)((unsigned)(Nkv - kv0) * C::ROWB);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(kbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(vbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < C::LPW; ++u) {
+        const int i = wave + C::NW * u;
+        if (i < C::KL)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(kdst + i * 1024), 16, off[u],
+                                                     0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(vdst + (i - C::KL) * 1024),
+                                                     16, off[u], 0, 0, 0);
+    }
+#endif
+}
+
+// Element mask of a 32-key score tile starting at kv0, for query row ip (lane half g):
+// hidden scores become -inf (unscaled; the scale is applied with the exponent).
+template <int MASK>
+__device__ __forceinline__ void mask_tile(f32x16 &s, int kv0, int ip, int Nkv, int W, int G,
+                                          int g)
+{
+    const int base = kv0 + 4 * g;
+    const int hiR = (MASK == 0 ? Nkv - 1 : min(ip, Nkv - 1)) - base;
+    const int loR = (MASK == 2 ? ip - W + 1 : INT_MIN / 2) - base;
+    const int gR = (MASK == 2 ? G : 0) - base;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + (e & 3);
+        const bool vis = r <= hiR && (MASK != 2 || r >= loR || r < gR);
+        s[e] = vis ? s[e] : -INFINITY;
+    }
+}
+
+__device__ __forceinline__ float max16(const f32x16 &v)
+{
+    const float a = vmax(vmax(vmax(v[0], v[1]), vmax(v[2], v[3])),
+                         vmax(vmax(v[4], v[5]), vmax(v[6], v[7])));
+    const float b = vmax(vmax(vmax(v[8], v[9]), vmax(v[10], v[11])),
+                         vmax(vmax(v[12], v[13]), vmax(v[14], v[15])));
+    return vmax(a, b);
+}
+
+// One pipeline step for tile t. sc: raw scores of tile t (masked if needed), mt its
+// scaled row maximum. NEXT: there is a tile t+1 (K in LDS at kn); mask_next: it needs the
+// element mask (wave-uniform). vc: V of tile t in LDS.
+template <typename T, typename C, int MASK, bool NEXT>
+__device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char *__restrict__ vc,
+                                        const int (&kofs)[C::NKK], const int (&vofs)[C::NDB],
+                                        const s16x8 (&qf)[C::NKK], f32x16 (&oacc)[C::NDB],
+                                        f32x16 &sc, f32x16 &sn, float &m, float &l, float &mt,
+                                        float c, bool mask_next, int kvn, int ip, int Nkv, int W,
+                                        int G, int g)
+{
+    using Op = Ops16<T>;
+    constexpr int NKK = C::NKK, NDB = C::NDB, KPF = C::KPF, VPF = C::VPF;
+    constexpr int EPK = 16 / NKK;   // probabilities formed per score instruction
+    constexpr int NF = 2 * NDB;     // P V matrix instructions
+
+    // K fragment reads for the first matrix instructions go out before the rescale test.
+    s16x8 kf[NKK];
+    if (NEXT) {
+#pragma unroll
+        for (int f = 0; f < KPF; ++f) kf[f] = *(const s16x8 *)(kn + kofs[f]);
+    }
     if (!__all(mt <= m + kRescaleSlack)) {
         const float mn = fmaxf(m, mt);
         const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
         m = mn;
         l *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
-    const float mu = (m == -INFINITY) ? 0.f : m;
+    const float nmu = (m == -INFINITY) ? 0.f : -m;
+    __builtin_amdgcn_sched_barrier(0);
 
-    float ps = 0.f;
+    // Phase A: S(t+1) = K(t+1) Q^T, P(t) = 2^(c S(t) - m).
+    s16x4 vlo[NF], vhi[NF];
+    auto vread = [&](int f) {
+        const int kc = f / NDB, db = f % NDB;
+        const char *p0 = vc + vofs[db] + kc * 16 * C::ROWB;
+        vlo[f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+        vhi[f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 8 * C::ROWB));
+    };
+    s16x8 pf[2];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float p = MASKED ? fast_exp2(sacc[jb][e] - mu)
-                                   : fast_exp2(__builtin_fmaf(sacc[jb][e], c, -mu));
-            sacc[jb][e] = p;
-            ps += p;
+    for (int kk = 0; kk < NKK; ++kk) {
+        if (NEXT) {
+            if (kk + KPF < NKK) kf[kk + KPF] = *(const s16x8 *)(kn + kofs[kk + KPF]);
+            sn = Op::mma(kf[kk], qf[kk], kk == 0 ? f32x16{} : sn);
         }
-    l += ps;
+        if (kk >= NKK - VPF) vread(kk - (NKK - VPF));
+#pragma unroll
+        for (int e = kk * EPK; e < (kk + 1) * EPK; ++e)
+            sc[e] = fast_exp2(__builtin_fmaf(sc[e], c, nmu));
+        if (((kk + 1) * EPK) % 8 == 0) {
+            const int o = (kk + 1) * EPK - 8;
+            pf[o / 8] = Op::pack8(sc[o], sc[o + 1], sc[o + 2], sc[o + 3], sc[o + 4], sc[o + 5],
+                                  sc[o + 6], sc[o + 7]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // O^T += V^T P^T over four 16-key chunks. Chunk kc, slot (g, e) is key
-    // 16kc + 8(e/4) + 4g + e%4: P^T is sacc[kc/2][8(kc%2) + e] in place. The V^T operand
-    // comes from two transposed reads of four keys each.
-    // Lane (g, s, j) of a transposed read addresses row 16kc + 8h + 4g + j/4 and the
-    // 8 bytes at element 32db + 16s + 4(j%4) (offset vofs[db] for kc = h = 0).
+    // Phase B: O^T += V^T P^T(t); l += row sums of P(t); mask and maximum of S(t+1).
+    float ps[4];
 #pragma unroll
-    for (int kc = 0; kc < C::BN / 16; ++kc) {
-        const int jb = kc >> 1, o8 = 8 * (kc & 1);
-        const s16x8 pf = Op::pack8(sacc[jb][o8 + 0], sacc[jb][o8 + 1], sacc[jb][o8 + 2],
-                                   sacc[jb][o8 + 3], sacc[jb][o8 + 4], sacc[jb][o8 + 5],
-                                   sacc[jb][o8 + 6], sacc[jb][o8 + 7]);
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-            const char *p0 = vb + vofs[db] + kc * 16 * C::ROWB;
-            const char *p1 = p0 + 8 * C::ROWB;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-            const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = Op::mma(a, pf, oacc[db]);
+    for (int f = 0; f < NF; ++f) {
+        const int kc = f / NDB, db = f % NDB;
+        if (f + VPF < NF) vread(f + VPF);
+        const s16x8 a = __builtin_shufflevector(vlo[f], vhi[f], 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = Op::mma(a, pf[kc], oacc[db]);
+        // vector work spread over the matrix instructions
+        if (NF == 8) {
+            if (f < 4) ps[f] = (sc[4 * f] + sc[4 * f + 1]) + (sc[4 * f + 2] + sc[4 * f + 3]);
+            if (f == 4) l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            if (NEXT && f == 4 && mask_next) mask_tile<MASK>(sn, kvn, ip, Nkv, W, G, g);
+            if (NEXT && f == 6) mt = half_swap_max(max16(sn)) * c;
+        } else {
+            if (f == 0) {
+                ps[0] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+                ps[1] = (sc[4] + sc[5]) + (sc[6] + sc[7]);
+            }
+            if (f == 1) {
+                ps[2] = (sc[8] + sc[9]) + (sc[10] + sc[11]);
+                ps[3] = (sc[12] + sc[13]) + (sc[14] + sc[15]);
+                l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            }
+            if (NEXT && f == 2 && mask_next) mask_tile<MASK>(sn, kvn, ip, Nkv, W, G, g);
+            if (NEXT && f == 3) mt = half_swap_max(max16(sn)) * c;
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <typename T, int D, int MASK>
-__global__ __launch_bounds__(256, 2) void fwd16_kernel(
+template <typename T, int D, int MASK, int NS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
     int Nkv, float c, int W, int G, int nqt)
 {
-    using C = Cfg16<D>;
+    using C = CfgSP<D, NS, NW>;
     using Op = Ops16<T>;
-    constexpr int BM = C::BM, BN = C::BN;
+    constexpr int BM = C::BM, BN = C::BN, LPW = C::LPW;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, li = lane & 31;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = L / nqt;
@@ -409,12 +495,13 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
     const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
 
     // Q^T fragments (B operand): lane (g, i) holds Q[row i][16kk + 8g .. +7]. A negative
-    // scale is moved into Q by flipping sign bits (exact), so that c >= 0 below.
-    const int wrow0 = q0 + wave * 32;
-    const int row = wrow0 + li;
+    // scale is moved into Q by flipping sign bits (exact). c is kept at least the smallest
+    // normal float so that a hidden score (-inf) times c stays -inf; for |scale| below
+    // that every visible weight is 2^0 either way.
+    const int row = q0 + wave * 32 + li;
     const int ip = row + delta;
     const short qsign = c < 0.f ? (short)0x8000 : (short)0;
-    c = fabsf(c);
+    c = fmaxf(fabsf(c), 1.17549435e-38f);
     s16x8 qf[C::NKK];
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
@@ -425,27 +512,26 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
     }
 
     const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);
+    const int ntl = sch.total, nint = sch.interior;
 
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[C::NDB];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
 
-    // K/V tiles go straight from HBM to LDS (buffer_load ... lds): wave-wide load u of
-    // wave w fills the ROWS_PER_LOAD rows of slot q = 4u + w; lane l lands in physical
-    // chunk l % CHUNKS of row q * ROWS_PER_LOAD + l / CHUNKS, so it fetches the logical
-    // chunk the swizzle stores there. Offsets are relative to the tile's first key.
     const char *kbh = (const char *)(K + kvbase);
     const char *vbh = (const char *)(V + kvbase);
-    unsigned koff[C::LOADS], voff[C::LOADS];
+    // Load u of this wave fills rows r of the K (or V) tile; lane l lands in physical chunk
+    // l % CHUNKS of row r = first + l / CHUNKS, so it fetches the logical chunk the swizzle
+    // stores there. Offsets are relative to the tile's first key.
+    unsigned off[C::LPW];
 #pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-        const int r = (4 * u + wave) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
+    for (int u = 0; u < C::LPW; ++u) {
+        const int i = wave + NW * u;
+        const int r = (i % C::KL) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
         const int pc = lane % C::CHUNKS;
-        koff[u] = r * C::ROWB + 16 * k_swz<D>(r, pc);
-        voff[u] = r * C::ROWB + 16 * v_swz<D>(r, pc);
+        off[u] = r * C::ROWB + 16 * (i < C::KL ? k_swz<D>(r, pc) : v_swz<D>(r, pc));
     }
-    // Lane-constant LDS byte offsets of the swizzled operand reads (see attend_tile).
     int kofs[C::NKK], vofs[C::NDB];
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * k_swz<D>(li, 2 * kk + g);
@@ -457,66 +543,76 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(
             vofs[db] = trow * C::ROWB + 16 * v_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
     }
 
-    const int ntiles = sch.total;
     char *const lds = (char *)smem;
-    TileSchedule::Cursor cur = sch.begin(), nxt = sch.next(cur);
-    if (ntiles > 0) {
-        issue_tile<D>(kbh, vbh, koff, voff, cur.t * BN, Nkv, lds, wave);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-    // Interior tiles: every row sees every key, no per-wave decisions.
-    for (int n = 0; n < sch.interior; ++n) {
-        const int kv0 = cur.t * BN;
-        if (n + 1 < ntiles)
-            issue_tile<D>(kbh, vbh, koff, voff, nxt.t * BN, Nkv, lds + ((n + 1) & 1) * C::STAGEB,
-                          wave);
-        attend_tile<T, D, MASK, false>(lds + (n & 1) * C::STAGEB, kofs, vofs, qf, oacc, m, l, c,
-                                       kv0, ip, Nkv, W, G, lane);
-        cur = nxt;
-        nxt = sch.next(nxt);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
-        __syncthreads();
-    }
-    // Edge tiles: per wave, skip the tile, take it whole, or apply the element mask.
-    for (int n = sch.interior; n < ntiles; ++n) {
-        const int kv0 = cur.t * BN;
-        if (n + 1 < ntiles)
-            issue_tile<D>(kbh, vbh, koff, voff, nxt.t * BN, Nkv, lds + ((n + 1) & 1) * C::STAGEB,
-                          wave);
-        bool skip = wrow0 >= Nq;
-        bool need_mask = kv0 + BN > Nkv;
-        if (MASK >= 1) {
-            const int ip0 = wrow0 + delta, ip1 = wrow0 + 31 + delta;
-            if (kv0 > ip1) skip = true;
-            if (kv0 + BN - 1 > ip0) need_mask = true;
-            if (MASK == 2) {
-                if (kv0 + BN - 1 < ip0 - W + 1 && kv0 >= G) skip = true;
-                if (!(ip1 - kv0 < W) && !(kv0 + BN - 1 < G)) need_mask = true;
-            }
+    auto kslot = [&](int t) { return lds + (t % NS) * C::TILEB; };
+    auto vslot = [&](int t) { return lds + C::VREG + (t % NS) * C::TILEB; };
+
+    // Prologue: tiles 0 .. NS-2 in flight; wait for tiles 0 and 1.
+    TileSchedule::Cursor ld = sch.begin();
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+        if (j < ntl) {
+            issue_kv<C>(kbh, vbh, off, ld.t * BN, Nkv, kslot(j), vslot(j), wave);
+            ld = sch.next(ld);
         }
-        const char *st = lds + (n & 1) * C::STAGEB;
-        if (MASK == 0) {
-            // without a mask the only edge tile is the key tail
-            if (!skip)
-                attend_tile<T, D, MASK, true>(st, kofs, vofs, qf, oacc, m, l, c, kv0, ip, Nkv, W,
-                                              G, lane);
-        } else if (!skip) {
-            if (need_mask)
-                attend_tile<T, D, MASK, true>(st, kofs, vofs, qf, oacc, m, l, c, kv0, ip, Nkv, W,
-                                              G, lane);
-            else
-                attend_tile<T, D, MASK, false>(st, kofs, vofs, qf, oacc, m, l, c, kv0, ip, Nkv, W,
-                                               G, lane);
+    }
+    wait_tiles<LPW, NS - 3>(min(NS - 1, ntl) - 2);
+    ring_barrier();
+
+    f32x16 sa, sb;
+    float mt = -INFINITY;
+    TileSchedule::Cursor nx = sch.begin();
+    if (ntl > 0) {
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk)
+            sa = Op::mma(*(const s16x8 *)(kslot(0) + kofs[kk]), qf[kk],
+                         kk == 0 ? f32x16{} : sa);
+        if (nint == 0) mask_tile<MASK>(sa, nx.t * BN, ip, Nkv, W, G, g);
+        mt = half_swap_max(max16(sa)) * c;
+        nx = sch.next(nx);
+    }
+
+    // Step t: load tile t+NS-1, finish tile t, start tile t+1; then make tile t+2 resident.
+    auto step_end = [&](int t) {
+        wait_tiles<LPW, NS - 3>(min(t + NS - 1, ntl - 1) - (t + 2));
+        ring_barrier();
+    };
+    auto load_ahead = [&](int t) {
+        if (t + NS - 1 < ntl) {
+            issue_kv<C>(kbh, vbh, off, ld.t * BN, Nkv, kslot(t + NS - 1), vslot(t + NS - 1),
+                        wave);
+            ld = sch.next(ld);
         }
-        cur = nxt;
-        nxt = sch.next(nxt);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    };
+    // Two steps per iteration so that sa and sb swap roles without register copies. Every
+    // step in the loop has a tile t+1; the last step is peeled.
+    auto step = [&](int t, f32x16 &cur, f32x16 &nxt) {
+        load_ahead(t);
+        sp_step<T, C, MASK, true>(kslot(t + 1), vslot(t), kofs, vofs, qf, oacc, cur, nxt, m,
+                                      l, mt, c, t + 1 >= nint, nx.t * BN, ip, Nkv, W, G, g);
+        nx = sch.next(nx);
+        step_end(t);
+    };
+    auto last = [&](int t, f32x16 &cur, f32x16 &nxt) {
+        sp_step<T, C, MASK, false>(nullptr, vslot(t), kofs, vofs, qf, oacc, cur, nxt, m, l,
+                                       mt, c, false, 0, ip, Nkv, W, G, g);
+    };
+    if (ntl > 0) {
+        int t = 0;
+        for (; t + 2 < ntl; t += 2) {
+            step(t, sa, sb);
+            step(t + 1, sb, sa);
+        }
+        if (t + 1 < ntl) {
+            step(t, sa, sb);
+            last(t + 1, sb, sa);
+        } else {
+            last(t, sa, sb);
+        }
     }
 
     // Epilogue: both lane halves hold partial sums of the same row (same reference max).
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = half_swap_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row < Nq) {
         uint16_t *orow = O + qbase + (size_t)row * D;
@@ -666,13 +762,16 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float *__restrict__ Q,
     }
 }
 
+// 4 waves (128 query rows) per workgroup, two workgroups per CU, a 4-slot K/V ring.
+constexpr int kStages = 4, kWaves = 4;
+
 template <typename T, int D, int MASK>
 hipError_t launch16(const FwdArgs &a, hipStream_t s)
 {
-    using C = Cfg16<D>;
+    using C = CfgSP<D, kStages, kWaves>;
     const int nqt = (a.Nq + C::BM - 1) / C::BM;
     const long nblk = (long)nqt * a.B * a.H;
-    auto kern = fwd16_kernel<T, D, MASK>;
+    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
