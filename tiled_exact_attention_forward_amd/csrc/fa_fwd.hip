@@ -494,7 +494,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const int delta = Nkv - Nq;
     const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
 
-    // Q^T fragments (B operand): lane (g, i) holds Q[row i][16kk + 8g .. +7]. A negative
+    // Q^T fragments (B operand): lane (g, i) holds Q[row i][16kk + 8g .. +7]. The loads go
+    // out back to back ahead of the first K/V tiles (padding rows read the last row) and are
+    // finished after the wait for those tiles, so no wait sits between them. A negative
     // scale is moved into Q by flipping sign bits (exact). c is kept at least the smallest
     // normal float so that a hidden score (-inf) times c stays -inf; for |scale| below
     // that every visible weight is 2^0 either way.
@@ -503,12 +505,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const short qsign = c < 0.f ? (short)0x8000 : (short)0;
     c = fmaxf(fabsf(c), 1.17549435e-38f);
     s16x8 qf[C::NKK];
+    {
+        const uint16_t *qr = Q + qbase + (size_t)min(row, Nq - 1) * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) {
-        if (row < Nq)
-            qf[kk] = *(const s16x8 *)(Q + qbase + (size_t)row * D + 16 * kk + 8 * g) ^ qsign;
-        else
-            qf[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = *(const s16x8 *)(qr + 16 * kk);
     }
 
     const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);
@@ -558,6 +558,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     }
     wait_tiles<LPW, NS - 3>(min(NS - 1, ntl) - 2);
     ring_barrier();
+    {
+        const short keep = row < Nq ? (short)-1 : (short)0;
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = (qf[kk] ^ qsign) & keep;
+    }
 
     f32x16 sa, sb;
     float mt = -INFINITY;
