@@ -12,7 +12,10 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers (HIP device memory) owned by the caller. The
- *    library allocates nothing, keeps no global mutable state and is thread-safe.
+ *    library allocates nothing and is thread-safe. Its only mutable state is the HIP error
+ *    code of the last failed launch, kept per calling thread (see fa_last_hip_error);
+ *    raising a kernel's dynamic LDS limit (an idempotent runtime attribute) happens on
+ *    every launch.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). All work is
  *    enqueued on it; calls return before the work completes.
  *  - Return value: FA_OK (0) or a negative fa_status. Argument checks run on the host BEFORE
