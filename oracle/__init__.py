@@ -8,8 +8,10 @@ precision); this module only marshals numpy arrays through ctypes.
 Parity pins (tests/test_oracle_*.py): a library routine (torch's CPU scaled-dot-product
 attention in float64 with band masks built from tril), 50-digit mpmath brute force on tiny
 inputs, closed forms (Q = 0 gives the mean of the visible V rows and LSE = ln(count)),
-invariants (rows sum to one, shift and permutation invariance, split-and-merge of keys) and
-one-hot edge probes of every mask boundary.
+invariants (rows sum to one, shift and permutation invariance, split-and-merge of keys),
+one-hot edge probes of every mask boundary, and reductions between masks (a band or prefix
+covering every key is the unmasked case, an empty prefix is causal, an all-ones block layout
+is unmasked).
 """
 import ctypes
 import os
@@ -38,6 +40,11 @@ class Oracle:
             f32p, f32p, f32p, i32p, i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_double, f64p, f64p]
         lib.oracle_decode_paged.restype = ctypes.c_int
+        lib.oracle_attention_block_sparse_rows.argtypes = [
+            f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_uint8), ctypes.c_long, i64p,
+            ctypes.c_long, f64p, f64p]
+        lib.oracle_attention_block_sparse_rows.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -73,6 +80,38 @@ class Oracle:
             _p(o, ctypes.c_double), _p(lse, ctypes.c_double))
         if rc != 0:
             raise ValueError("oracle_attention_rows rejected its arguments")
+        if rows is None:
+            return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+        return o, lse
+
+    def attention_block_sparse(self, q, k, v, scale, layout, block, rows=None):
+        """Exact block-sparse attention in fp64.
+
+        layout: [H, ceil(Nq/block), ceil(Nkv/block)], nonzero = visible tile (shared by every
+        batch entry). Other arguments and the result as in attention().
+        """
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        assert k.shape == (B, H, Nkv, d) and v.shape == (B, H, Nkv, d)
+        lay = np.ascontiguousarray(np.asarray(layout).astype(np.uint8))
+        assert lay.shape == (H, -(-Nq // block), -(-Nkv // block)), lay.shape
+        scale = float(np.float32(scale))
+        if rows is None:
+            n = B * H * Nq
+            rp = None
+        else:
+            rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+            n = rows.size
+            rp = _p(rows, ctypes.c_int64)
+        o = np.empty((n, d), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        rc = self.lib.oracle_attention_block_sparse_rows(
+            _p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float), B, H, Nq,
+            Nkv, d, scale, _p(lay, ctypes.c_uint8), int(block), rp, n, _p(o, ctypes.c_double),
+            _p(lse, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_attention_block_sparse_rows rejected its arguments")
         if rows is None:
             return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
         return o, lse
@@ -140,6 +179,10 @@ def num_threads():
 
 def attention(*args, **kw):
     return default().attention(*args, **kw)
+
+
+def attention_block_sparse(*args, **kw):
+    return default().attention_block_sparse(*args, **kw)
 
 
 def decode_paged(*args, **kw):

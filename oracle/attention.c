@@ -23,6 +23,13 @@
  *   - sliding window + global keys ("ascend-transformer-boost" article, 场景三, sparse_config
  *     with window_size and global_tokens): causal window of W keys including the query's own
  *     position (i' - j < W) plus the first G key positions, still causal;
+ *   - band attention (ops-transformer article on zwxr.cn, section 3.2, 带状注意力: each token
+ *     attends the positions within +-w of it): |i' - j| <= w, on both sides of the query;
+ *   - prefix LM ("ascend-transformer-boost" article, 场景三, names the variant only): keys
+ *     j < P (the prefix) are visible to every query, later keys causally (j <= i');
+ *   - block sparse (same article, names the variant only): a per-head layout of
+ *     block x block tiles over (query index, key index); a key is visible when its tile is
+ *     set; no shift between query and key positions;
  *   - a row with no visible key gives O = 0 and LSE = -inf.
  *
  * Inputs are float32 arrays that hold exactly the values the device sees (fp16 and bf16
@@ -39,7 +46,9 @@
 
 /* Mask predicate: is key position j visible from a query at absolute position ip?
  * mode 0: all keys; mode 1: causal (j <= ip); mode 2: causal window of `window` keys
- * ending at ip, plus the first `n_global` positions (still causal). */
+ * ending at ip, plus the first `n_global` positions (still causal); mode 3: band of
+ * `window` positions on either side of ip; mode 4: prefix LM with a prefix of `n_global`
+ * keys. */
 static int key_visible(long ip, long j, int mode, long window, long n_global)
 {
     if (mode == 0)
@@ -48,14 +57,22 @@ static int key_visible(long ip, long j, int mode, long window, long n_global)
         return j <= ip;
     if (mode == 2)
         return j <= ip && ((ip - j) < window || j < n_global);
+    if (mode == 3)
+        return j >= ip - window && j <= ip + window;
+    if (mode == 4) {
+        const long prefix = n_global;
+        return j < prefix || j - ip <= 0;
+    }
     return 0;
 }
 
 /* One query row against `nkv` key/value rows given by pointers. `s` is scratch of nkv
  * doubles. Writes d outputs and the row's LSE. */
+/* kvis: per-key visibility of this row (block sparse), or NULL to use the mask mode. */
 static void attend_row(const float *q, const float *const *krow, const float *const *vrow,
                        long nkv, int d, double scale, long ip, int mode, long window,
-                       long n_global, double *s, double *out, double *lse)
+                       long n_global, const unsigned char *kvis, double *s, double *out,
+                       double *lse)
 {
     double m = -INFINITY;
     long j;
@@ -63,7 +80,7 @@ static void attend_row(const float *q, const float *const *krow, const float *co
 
     for (j = 0; j < nkv; ++j) {
         double dot = 0.0;
-        if (!key_visible(ip, j, mode, window, n_global)) {
+        if (kvis ? !kvis[j] : !key_visible(ip, j, mode, window, n_global)) {
             s[j] = -INFINITY;
             continue;
         }
@@ -85,7 +102,7 @@ static void attend_row(const float *q, const float *const *krow, const float *co
         double l = 0.0;
         for (j = 0; j < nkv; ++j) {
             double e;
-            if (!key_visible(ip, j, mode, window, n_global))
+            if (s[j] == -INFINITY)
                 continue;
             e = exp(s[j] - m);
             l += e;
@@ -118,7 +135,7 @@ int oracle_attention_rows(const float *q, const float *k, const float *v, int B,
                           double *lse)
 {
     int failed = 0;
-    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || mode < 0 || mode > 2)
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || mode < 0 || mode > 4)
         return -1;
     if (rows == NULL)
         nrows = (long)B * H * Nq;
@@ -146,10 +163,68 @@ int oracle_attention_rows(const float *q, const float *k, const float *v, int B,
                     vp[j] = vb + (size_t)j * d;
                 }
                 attend_row(q + (size_t)flat * d, kp, vp, Nkv, d, scale, i + (Nkv - Nq), mode,
-                           window, n_global, s, o + (size_t)r * d, lse + r);
+                           window, n_global, NULL, s, o + (size_t)r * d, lse + r);
             }
         }
         free(s);
+        free((void *)kp);
+        free((void *)vp);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * Block-sparse attention over contiguous [B,H,N,d] tensors for a list of query rows.
+ * layout: [H][ceil(Nq/block)][ceil(Nkv/block)] bytes, nonzero = the tile of query block
+ * i/block and key block j/block is visible (the same layout for every batch entry).
+ * rows, o, lse as in oracle_attention_rows.
+ */
+int oracle_attention_block_sparse_rows(const float *q, const float *k, const float *v, int B,
+                                       int H, long Nq, long Nkv, int d, double scale,
+                                       const uint8_t *layout, long block, const int64_t *rows,
+                                       long nrows, double *o, double *lse)
+{
+    int failed = 0;
+    long nqb, nkb;
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || block < 1 || layout == NULL)
+        return -1;
+    nqb = (Nq + block - 1) / block;
+    nkb = (Nkv + block - 1) / block;
+    if (rows == NULL)
+        nrows = (long)B * H * Nq;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)Nkv);
+        unsigned char *vis = (unsigned char *)malloc((size_t)Nkv);
+        const float **kp = (const float **)malloc(sizeof(float *) * (size_t)Nkv);
+        const float **vp = (const float **)malloc(sizeof(float *) * (size_t)Nkv);
+        long r;
+        if (s == NULL || vis == NULL || kp == NULL || vp == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (r = 0; r < nrows; ++r) {
+                int64_t flat = rows ? rows[r] : (int64_t)r;
+                long i = (long)(flat % Nq);
+                long bh = (long)(flat / Nq);
+                long h = bh % H;
+                const uint8_t *lrow = layout + ((size_t)h * nqb + (size_t)(i / block)) * nkb;
+                const float *kb = k + (size_t)bh * Nkv * d;
+                const float *vb = v + (size_t)bh * Nkv * d;
+                long j;
+                for (j = 0; j < Nkv; ++j) {
+                    kp[j] = kb + (size_t)j * d;
+                    vp[j] = vb + (size_t)j * d;
+                    vis[j] = lrow[j / block] != 0;
+                }
+                attend_row(q + (size_t)flat * d, kp, vp, Nkv, d, scale, i, 0, 0, 0, vis, s,
+                           o + (size_t)r * d, lse + r);
+            }
+        }
+        free(s);
+        free(vis);
         free((void *)kp);
         free((void *)vp);
     }
@@ -204,7 +279,7 @@ int oracle_decode_paged(const float *q, const float *k_pages, const float *v_pag
                     kp[j] = k_pages + off;
                     vp[j] = v_pages + off;
                 }
-                attend_row(q + (size_t)t * d, kp, vp, L, d, scale, L - 1, 1, 0, 0, s,
+                attend_row(q + (size_t)t * d, kp, vp, L, d, scale, L - 1, 1, 0, 0, NULL, s,
                            o + (size_t)t * d, lse + t);
             }
         }

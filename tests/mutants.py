@@ -21,6 +21,13 @@ MUTANTS = {
     "page_slot": ("(size_t)(j % page_size)", "(size_t)((j + 1) % page_size)"),
     "decode_head": ("* H + h) * d;", "* H + 0) * d;"),
     "max_ignores_first": ("if (s[j] > m)", "if (j > 0 && s[j] > m)"),
+    "band_narrow_left": ("j >= ip - window &&", "j > ip - window &&"),
+    "band_wide_right": ("j <= ip + window;", "j <= ip + window + 1;"),
+    "prefix_inclusive": ("j < prefix ||", "j <= prefix ||"),
+    "prefix_not_causal": ("j - ip <= 0;", "j - ip <= 1;"),
+    "block_query_index": ("(size_t)(i / block)) * nkb", "(size_t)((i + 1) / block)) * nkb"),
+    "block_key_index": ("lrow[j / block] != 0", "lrow[(j + 1) / block] != 0"),
+    "block_head": ("long h = bh % H;", "long h = 0;"),
 }
 
 

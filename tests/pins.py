@@ -15,7 +15,9 @@ source) and raises AssertionError when the oracle disagrees with:
     every mask edge: the causal diagonal, the key after it, the first and last key of the
     window, the last global key and the key after it.
 Masks: 0 none, 1 causal (diagonal kept, aligned bottom-right), 2 causal window of W keys
-ending at the query plus the first G keys.
+ending at the query plus the first G keys, 3 band of W positions on both sides of the query,
+4 prefix LM (the first G keys visible to every query, the rest causal); block sparse takes a
+per-head layout of block x block tiles.
 """
 import math
 
@@ -38,10 +40,35 @@ def band_mask(Nq, Nkv, mode, W=0, G=0):
     causal = torch.tril(ones, diagonal=delta)
     if mode == 1:
         return causal
+    if mode == 3:
+        return torch.tril(ones, diagonal=delta + W) & ~torch.tril(ones, diagonal=delta - W - 1)
+    if mode == 4:
+        prefix = torch.zeros(Nq, Nkv, dtype=torch.bool)
+        prefix[:, :G] = True
+        return causal | prefix
     window = causal & ~torch.tril(ones, diagonal=delta - W)
     glob = causal.clone()
     glob[:, G:] = False
     return window | glob
+
+
+def block_mask(layout, block, Nq, Nkv):
+    """Boolean [H, Nq, Nkv] visibility of a block layout, expanded with a Kronecker product."""
+    lay = torch.from_numpy(np.asarray(layout, dtype=np.int64))
+    tile = torch.ones(block, block, dtype=torch.int64)
+    full = torch.stack([torch.kron(lay[h], tile) for h in range(lay.shape[0])])
+    return full[:, :Nq, :Nkv] != 0
+
+
+def library_attention_mask(q, k, v, scale, m):
+    """torch SDPA + logsumexp in float64 with an explicit boolean mask (broadcast)."""
+    qt = torch.from_numpy(np.asarray(q, dtype=np.float64))
+    kt = torch.from_numpy(np.asarray(k, dtype=np.float64))
+    vt = torch.from_numpy(np.asarray(v, dtype=np.float64))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    s = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) * scale
+    s = s.masked_fill(~m, float("-inf"))
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
 
 
 def library_attention(q, k, v, scale, mode, W=0, G=0):
@@ -62,10 +89,14 @@ def visible_keys(ip, Nkv, mode, W, G):
     if mode == 0:
         return list(range(Nkv))
     hi = min(ip, Nkv - 1)
-    if hi < 0:
+    if hi < 0 and mode in (1, 2):
         return []
     if mode == 1:
         return list(range(0, hi + 1))
+    if mode == 3:
+        return list(range(max(0, ip - W), min(Nkv - 1, ip + W) + 1))
+    if mode == 4:
+        return sorted(set(range(0, hi + 1)) | set(range(0, min(G, Nkv))))
     win = set(range(max(0, ip - W + 1), hi + 1))
     glob = set(range(0, min(G, hi + 1)))
     return sorted(win | glob)
@@ -75,6 +106,10 @@ def visible_count(ip, Nkv, mode, W, G):
     """Closed-form count of visible keys (no enumeration)."""
     if mode == 0:
         return Nkv
+    if mode == 3:
+        return max(0, min(Nkv - 1, ip + W) - max(0, ip - W) + 1)
+    if mode == 4:
+        return min(Nkv, max(G, ip + 1, 0))
     if ip < 0:
         return 0
     top = min(ip, Nkv - 1) + 1
@@ -348,6 +383,165 @@ def pin_decode(orc):
     assert np.array_equal(o, o2) and np.array_equal(l, l2)
 
 
+def _random_layout(H, nqb, nkb, seed, density=0.35):
+    lay = (np.random.default_rng(seed).random((H, nqb, nkb)) < density).astype(np.uint8)
+    lay[:, :, 0] |= (np.arange(nqb) % 3 == 0).astype(np.uint8)  # some rows with block 0
+    return lay
+
+
+def pin_library_more_masks(orc):
+    """Band (3), prefix LM (4) and block sparse against torch SDPA with masks built by tril
+    offsets and Kronecker products."""
+    cases = [(1, 2, 33, 33, 8, 3, 4, 0), (1, 1, 12, 30, 8, 3, 6, 0), (2, 2, 25, 25, 16, 3, 0, 0),
+             (1, 2, 33, 33, 8, 4, 0, 9), (1, 1, 12, 30, 8, 4, 0, 20), (1, 1, 30, 12, 8, 4, 0, 5),
+             (2, 1, 20, 20, 8, 4, 0, 0), (1, 1, 40, 40, 4, 3, 100, 0)]
+    for n, (B, H, Nq, Nkv, d, mode, W, G) in enumerate(cases):
+        q = _rand((B, H, Nq, d), 3000 + 3 * n)
+        k = _rand((B, H, Nkv, d), 3001 + 3 * n)
+        v = _rand((B, H, Nkv, d), 3002 + 3 * n)
+        scale = float(np.float32(1 / math.sqrt(d)))
+        o, lse = orc.attention(q, k, v, scale, mode, W, G)
+        ro, rl = library_attention_mask(q, k, v, scale, band_mask(Nq, Nkv, mode, W, G))
+        assert np.allclose(o, ro, rtol=1e-12, atol=1e-13), f"library O mismatch case {n}"
+        assert np.allclose(lse, rl, rtol=1e-12, atol=1e-13), f"library LSE mismatch case {n}"
+    for n, (B, H, Nq, Nkv, d, blk) in enumerate([(1, 2, 40, 40, 8, 8), (2, 3, 33, 50, 8, 16),
+                                                 (1, 1, 7, 64, 4, 4)]):
+        q = _rand((B, H, Nq, d), 3100 + 3 * n)
+        k = _rand((B, H, Nkv, d), 3101 + 3 * n)
+        v = _rand((B, H, Nkv, d), 3102 + 3 * n)
+        lay = _random_layout(H, -(-Nq // blk), -(-Nkv // blk), 3200 + n)
+        m = block_mask(lay, blk, Nq, Nkv)[None]
+        rows = m.any(dim=-1)[0]
+        o, lse = orc.attention_block_sparse(q, k, v, 0.4, lay, blk)
+        ro, rl = library_attention_mask(q, k, v, float(np.float32(0.4)), m)
+        for h in range(H):
+            vis = rows[h].numpy()
+            assert np.allclose(o[:, h][:, vis], ro[:, h][:, vis], rtol=1e-12, atol=1e-13), n
+            assert np.allclose(lse[:, h][:, vis], rl[:, h][:, vis], rtol=1e-12, atol=1e-13), n
+            assert np.all(o[:, h][:, ~vis] == 0) and np.all(np.isneginf(lse[:, h][:, ~vis])), n
+
+
+def pin_mpmath_more_masks(orc):
+    for n, (Nq, Nkv, d, mode, W, G) in enumerate([(7, 7, 4, 3, 2, 0), (5, 9, 4, 3, 1, 0),
+                                                 (9, 5, 4, 3, 3, 0), (7, 7, 4, 4, 0, 3),
+                                                 (4, 9, 2, 4, 0, 2), (9, 4, 2, 4, 0, 2)]):
+        q = _rand((1, 1, Nq, d), 3300 + n) * 2
+        k = _rand((1, 1, Nkv, d), 3400 + n) * 2
+        v = _rand((1, 1, Nkv, d), 3500 + n)
+        o, lse = orc.attention(q, k, v, 0.7, mode, W, G)
+        for i in range(Nq):
+            keys = visible_keys(i + Nkv - Nq, Nkv, mode, W, G)
+            if not keys:
+                assert np.all(o[0, 0, i] == 0) and np.isneginf(lse[0, 0, i]), (n, i)
+                continue
+            ro, rl = mp_attention_row(q[0, 0, i], k[0, 0], v[0, 0], np.float32(0.7), keys)
+            assert np.allclose(o[0, 0, i], ro, rtol=1e-12, atol=1e-14), (n, i)
+            assert abs(lse[0, 0, i] - rl) <= 1e-12 * max(1.0, abs(rl)), (n, i)
+    # block sparse: key sets enumerated from the layout row
+    blk, Nq, Nkv, d = 3, 8, 10, 4
+    lay = np.array([[[1, 0, 1, 0], [0, 1, 0, 1], [1, 1, 0, 0]]], np.uint8)
+    q = _rand((1, 1, Nq, d), 3600) * 2
+    k = _rand((1, 1, Nkv, d), 3601) * 2
+    v = _rand((1, 1, Nkv, d), 3602)
+    o, lse = orc.attention_block_sparse(q, k, v, 0.7, lay, blk)
+    for i in range(Nq):
+        keys = [j for j in range(Nkv) if lay[0, i // blk, j // blk]]
+        ro, rl = mp_attention_row(q[0, 0, i], k[0, 0], v[0, 0], np.float32(0.7), keys)
+        assert np.allclose(o[0, 0, i], ro, rtol=1e-12, atol=1e-14), i
+        assert abs(lse[0, 0, i] - rl) <= 1e-12 * max(1.0, abs(rl)), i
+
+
+def pin_q_zero_more_masks(orc):
+    for n, (Nq, Nkv, mode, W, G) in enumerate([(50, 50, 3, 7, 0), (30, 60, 3, 5, 0),
+                                               (60, 30, 3, 2, 0), (50, 50, 4, 0, 13),
+                                               (20, 50, 4, 0, 40), (50, 20, 4, 0, 6)]):
+        d = 8
+        q = np.zeros((1, 2, Nq, d), np.float32)
+        k = _rand((1, 2, Nkv, d), 3700 + n)
+        v = _rand((1, 2, Nkv, d), 3800 + n)
+        o, lse = orc.attention(q, k, v, 0.3, mode, W, G)
+        pre = np.concatenate([np.zeros((1, 2, 1, d)), np.cumsum(v.astype(np.float64), axis=2)],
+                             axis=2)
+        for i in range(Nq):
+            ip = i + Nkv - Nq
+            cnt = visible_count(ip, Nkv, mode, W, G)
+            if cnt == 0:
+                assert np.all(o[0, :, i] == 0) and np.all(np.isneginf(lse[0, :, i])), (n, i)
+                continue
+            assert abs(lse[0, :, i] - math.log(cnt)).max() < 1e-12, (n, i)
+            if mode == 3:
+                a, b = max(0, ip - W), min(Nkv - 1, ip + W) + 1
+            else:
+                a, b = 0, min(Nkv, max(G, ip + 1))
+            tot = pre[0, :, b] - pre[0, :, a]
+            assert np.allclose(o[0, :, i], tot / cnt, rtol=1e-12, atol=1e-13), (n, i)
+
+
+def pin_onehot_more_edges(orc):
+    N, d, scale = 48, 64, 1.0 / 8.0
+    W = 5
+    # band: i+W and i-W visible, i+W+1 and i-W-1 not
+    probes = {20: (25, True), 21: (27, False), 30: (25, True), 31: (25, False), 0: (5, True),
+              47: (42, True), 1: (7, False)}
+    q, k, v = onehot_case(N, d, W, 0, [(i, js) for i, (js, _) in probes.items()])
+    q *= 5
+    o, lse = orc.attention(q, k, v, scale, 3, W, 0)
+    for i, (js, vis) in probes.items():
+        keys = visible_keys(i, N, 3, W, 0)
+        assert (js in keys) == vis, (i, js)
+        want = v[0, 0, js] if vis else v[0, 0, keys].astype(np.float64).mean(axis=0)
+        assert np.allclose(o[0, 0, i], want, rtol=1e-12, atol=1e-12), ("band", i, js)
+    # prefix LM with P = 10: row 0 sees key 9 but not key 10; row 20 sees 20, not 21
+    P = 10
+    probes = {0: (9, True), 1: (10, False), 20: (20, True), 21: (22, False), 3: (8, True)}
+    q, k, v = onehot_case(N, d, 0, P, [(i, js) for i, (js, _) in probes.items()])
+    q *= 5
+    o, lse = orc.attention(q, k, v, scale, 4, 0, P)
+    for i, (js, vis) in probes.items():
+        keys = visible_keys(i, N, 4, 0, P)
+        assert (js in keys) == vis, (i, js)
+        want = v[0, 0, js] if vis else v[0, 0, keys].astype(np.float64).mean(axis=0)
+        assert np.allclose(o[0, 0, i], want, rtol=1e-12, atol=1e-12), ("prefix", i, js)
+    # block sparse, block 8: row 9 (query block 1) probes key 16 (block 2, set) and key 8
+    # (block 1, not set); row 17 (block 2) probes key 7 (block 0, set) and 24 (block 3, not)
+    lay = np.zeros((1, 6, 6), np.uint8)
+    lay[0, 1, 2] = lay[0, 1, 0] = 1
+    lay[0, 2, 0] = lay[0, 2, 2] = 1
+    q, k, v = onehot_case(N, d, 0, 0, [(9, 16), (10, 8), (17, 7), (18, 24)])
+    q *= 5
+    o, _ = orc.attention_block_sparse(q, k, v, scale, lay, 8)
+    both = np.r_[0:8, 16:24]
+    assert np.allclose(o[0, 0, 9], v[0, 0, 16], atol=1e-12)
+    assert np.allclose(o[0, 0, 10], v[0, 0, both].astype(np.float64).mean(axis=0), atol=1e-12)
+    assert np.allclose(o[0, 0, 17], v[0, 0, 7], atol=1e-12)
+    assert np.allclose(o[0, 0, 18], v[0, 0, both].astype(np.float64).mean(axis=0), atol=1e-12)
+    assert np.all(o[0, 0, 0:8] == 0)  # query block 0 has no visible tile
+
+
+def pin_more_mask_reductions(orc):
+    q = _rand((1, 2, 24, 8), 3900)
+    k = _rand((1, 2, 24, 8), 3901)
+    v = _rand((1, 2, 24, 8), 3902)
+    on, ln = orc.attention(q, k, v, 0.35, 0)
+    oc, lc = orc.attention(q, k, v, 0.35, 1)
+    for W in (23, 24, 1000):   # a band reaching every key is the unmasked case
+        ob, lb = orc.attention(q, k, v, 0.35, 3, W, 0)
+        assert np.array_equal(ob, on) and np.array_equal(lb, ln), W
+    ob, _ = orc.attention(q, k, v, 0.35, 3, 0, 0)   # band of width 0: each row sees itself
+    assert np.array_equal(ob, v.astype(np.float64))
+    op, lp = orc.attention(q, k, v, 0.35, 4, 0, 0)  # empty prefix: causal
+    assert np.array_equal(op, oc) and np.array_equal(lp, lc)
+    for P in (24, 50):                               # prefix covering every key: unmasked
+        op, lp = orc.attention(q, k, v, 0.35, 4, 0, P)
+        assert np.array_equal(op, on) and np.array_equal(lp, ln), P
+    for blk in (4, 7, 24, 32):                       # all-ones layout: unmasked
+        lay = np.ones((2, -(-24 // blk), -(-24 // blk)), np.uint8)
+        ob, lb = orc.attention_block_sparse(q, k, v, 0.35, lay, blk)
+        assert np.array_equal(ob, on) and np.array_equal(lb, ln), blk
+
+
 ALL_PINS = [pin_library, pin_mpmath, pin_q_zero, pin_causal_row0, pin_onehot_edges,
             pin_rows_sum_to_one, pin_shift, pin_permutation, pin_split_merge,
-            pin_mask_reductions, pin_empty_rows, pin_decode]
+            pin_mask_reductions, pin_empty_rows, pin_decode, pin_library_more_masks,
+            pin_mpmath_more_masks, pin_q_zero_more_masks, pin_onehot_more_edges,
+            pin_more_mask_reductions]
