@@ -54,6 +54,10 @@ def visible_counts(Nq, Nkv, mode, W=0, G=0):
     top = np.clip(np.minimum(ip, Nkv - 1) + 1, 0, None)
     if mode == 1:
         return top
+    if mode == 3:
+        return np.maximum(0, np.minimum(Nkv - 1, ip + W) - np.maximum(0, ip - W) + 1)
+    if mode == 4:
+        return np.minimum(Nkv, np.maximum(np.maximum(G, ip + 1), 0))
     start = np.maximum(0, ip - W + 1)
     in_win = np.maximum(0, top - start)
     glob = np.maximum(0, np.minimum(np.minimum(G, start), top))
@@ -258,7 +262,8 @@ def main():
           f"{head['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     others = {}
     if not args.only_headline:
-        for name in ("dense_f16", "dense_bf16", "causal_bf16", "window_bf16"):
+        for name in ("dense_f16", "dense_bf16", "causal_bf16", "window_bf16", "band_bf16",
+                     "prefix_bf16"):
             if name == args.workload:
                 continue
             r = bench_prefill(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch, fa,

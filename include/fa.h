@@ -50,13 +50,25 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
  * alignment, so a single decode query sees every key). Key j is visible when
  *   FA_MASK_NONE          : always;
  *   FA_MASK_CAUSAL        : j <= i'  (the diagonal is kept);
- *   FA_MASK_WINDOW_GLOBAL : j <= i' and (i' - j < window or j < n_global).
+ *   FA_MASK_WINDOW_GLOBAL : j <= i' and (i' - j < window or j < n_global);
+ *   FA_MASK_BAND          : i' - window <= j <= i' + window  (both sides of the query);
+ *   FA_MASK_PREFIX_LM     : j <= i' or j < n_global  (n_global = prefix length).
  * The causal mask follows the LLaMA deployment in the ops-transformer article (section 四,
  * FlashAttention(causal=True): each token sees only earlier tokens and itself). The window
  * mask follows the sparse_config of the ascend-transformer-boost article (场景三:
  * sliding_window mode, window_size 2048, 64 global tokens such as BOS), read as a causal
- * window of `window` keys ending at the query plus the first `n_global` key positions. */
-typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW_GLOBAL = 2 } fa_mask;
+ * window of `window` keys ending at the query plus the first `n_global` key positions. The
+ * band mask is the band attention of the zwxr.cn article on ops-transformer (section 3.2:
+ * each token attends the positions within +-w of it). Prefix LM is one of the sparse
+ * variants the ascend-transformer-boost article names (场景三), read as: the first
+ * n_global keys are visible to every query, later keys causally. */
+typedef enum {
+    FA_MASK_NONE = 0,
+    FA_MASK_CAUSAL = 1,
+    FA_MASK_WINDOW_GLOBAL = 2,
+    FA_MASK_BAND = 3,
+    FA_MASK_PREFIX_LM = 4
+} fa_mask;
 
 /*
  * fa_forward -- tiled exact attention forward pass.
@@ -69,8 +81,9 @@ typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW_GLOBAL = 2 }
  *                       scores of each row (-inf for a row with no visible key, whose O
  *                       row is then 0). Required (not NULL).
  *  scale       multiplies Q K^T (normally 1/sqrt(d)).
- *  mask_mode   fa_mask; window >= 1 and n_global >= 0 are required for
- *              FA_MASK_WINDOW_GLOBAL and ignored otherwise.
+ *  mask_mode   fa_mask. FA_MASK_WINDOW_GLOBAL needs window >= 1 and n_global >= 0;
+ *              FA_MASK_BAND needs window >= 0 (0: each row sees only its own position);
+ *              FA_MASK_PREFIX_LM needs n_global >= 0 (0: causal). Unused ones are ignored.
  *  dtype       fa_dtype of q, k, v and o. Scores, softmax statistics and the output
  *              accumulator are float32 for every dtype; for fp16/bf16 the probabilities
  *              are rounded to the input dtype before the product with V.

@@ -55,7 +55,8 @@ def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nkv=8, d=64, scale=0.125, mas
     (dict(Nkv=-3), fa.FA_ERR_SHAPE),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=3), fa.FA_ERR_UNSUPPORTED), (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
-    (dict(mask=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=5), fa.FA_ERR_UNSUPPORTED), (dict(mask=-1), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=3, W=-1), fa.FA_ERR_SHAPE), (dict(mask=4, G=-1), fa.FA_ERR_SHAPE),
     (dict(mask=2, W=0, G=0), fa.FA_ERR_SHAPE), (dict(mask=2, W=4, G=-1), fa.FA_ERR_SHAPE),
     (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
     (dict(q=ctypes.c_void_p(0x1008)), fa.FA_ERR_UNSUPPORTED),

@@ -30,7 +30,10 @@ def test_page_printed_byte_counts():
 @pytest.mark.parametrize("Nq,Nkv,mode,W,G", [(64, 64, 0, 0, 0), (64, 64, 1, 0, 0),
                                               (40, 90, 1, 0, 0), (90, 40, 1, 0, 0),
                                               (120, 120, 2, 16, 5), (70, 150, 2, 33, 60),
-                                              (50, 50, 2, 1, 0), (50, 50, 2, 200, 0)])
+                                              (50, 50, 2, 1, 0), (50, 50, 2, 200, 0),
+                                              (80, 80, 3, 7, 0), (40, 90, 3, 5, 0),
+                                              (90, 40, 3, 0, 0), (80, 80, 4, 0, 20),
+                                              (40, 90, 4, 0, 60), (90, 40, 4, 0, 5)])
 def test_visible_counts_match_oracle(Nq, Nkv, mode, W, G):
     q = np.zeros((1, 1, Nq, 4), np.float32)
     k = np.random.default_rng(0).standard_normal((1, 1, Nkv, 4)).astype(np.float32)

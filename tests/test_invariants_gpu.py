@@ -39,7 +39,7 @@ def fwd(q, k, v, scale, mask=0, W=0, G=0):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("mask", [(0, 0, 0), (1, 0, 0), (2, 50, 7)])
+@pytest.mark.parametrize("mask", [(0, 0, 0), (1, 0, 0), (2, 50, 7), (3, 20, 0), (4, 0, 70)])
 def test_rows_sum_to_one(dtype, mask):
     q, k, _ = workloads.gen_prefill(2, 3, 200, 200, 128, dtype, 11)
     v = torch.ones_like(q)
@@ -51,7 +51,10 @@ def test_rows_sum_to_one(dtype, mask):
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("shape,mask", [((300, 300), (0, 0, 0)), ((300, 300), (1, 0, 0)),
                                         ((150, 300), (1, 0, 0)), ((300, 300), (2, 70, 9)),
-                                        ((257, 257), (2, 1, 0)), ((200, 300), (2, 64, 130))])
+                                        ((257, 257), (2, 1, 0)), ((200, 300), (2, 64, 130)),
+                                        ((300, 300), (3, 45, 0)), ((150, 300), (3, 7, 0)),
+                                        ((300, 150), (3, 100, 0)), ((300, 300), (4, 0, 100)),
+                                        ((150, 300), (4, 0, 200)), ((300, 150), (4, 0, 40))])
 def test_q_zero_gives_log_count(dtype, shape, mask):
     Nq, Nkv = shape
     _, k, v = workloads.gen_prefill(1, 2, Nq, Nkv, 64, dtype, 12)
@@ -60,7 +63,10 @@ def test_q_zero_gives_log_count(dtype, shape, mask):
     counts = np.array([pins.visible_count(i + Nkv - Nq, Nkv, mask[0], mask[1], mask[2])
                        for i in range(Nq)])
     lg = f64(lse)
-    assert np.abs(lg - np.log(counts)[None, None, :]).max() <= 2e-6 * np.log(counts).max() + 1e-6
+    seen = counts > 0
+    lc = np.log(counts[seen])
+    assert np.abs(lg[:, :, seen] - lc[None, None, :]).max() <= 2e-6 * lc.max() + 1e-6
+    assert np.all(np.isneginf(lg[:, :, ~seen]))  # rows without a visible key
     ro, rl = oracle.attention(q, k, v, 0.125, *mask)
     check(o, lse, ro, rl, dtype, "q=0")
 
@@ -95,8 +101,33 @@ def test_onehot_edge_probes(dtype):
         assert np.abs(og[i] - other).max() > 5e-2, (i, j)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("mask", [(3, 16, 0), (4, 0, 16)])
+def test_onehot_edge_probes_band_prefix(dtype, mask):
+    N, d = 128, 128
+    mode, W, G = mask
+    if mode == 3:  # band +-16: both edges, across 32-key tile boundaries
+        probes = {40: 56, 41: 58, 60: 44, 61: 44, 0: 16, 1: 18, 127: 111, 126: 109, 31: 47,
+                  33: 16}
+    else:          # prefix of 16 keys: the prefix edge from early rows, the diagonal later
+        probes = {0: 15, 1: 16, 2: 2, 3: 4, 63: 63, 64: 65, 100: 15, 101: 17, 127: 127}
+    q, k, v = pins.onehot_case(N, d, W, G, list(probes.items()), c=8.0, alpha=40.0)
+    t = workloads.DTYPES[dtype]
+    q, k, v = torch.from_numpy(q).to(t), torch.from_numpy(k).to(t), torch.from_numpy(v).to(t)
+    o, lse = fwd(q, k, v, 0.125, mode, W, G)
+    ro, rl = oracle.attention(q, k, v, 0.125, mode, W, G)
+    check(o, lse, ro, rl, dtype, f"onehot mode {mode}")
+    og, vf = f64(o)[0, 0], f64(v)[0, 0]
+    for i, j in probes.items():
+        keys = pins.visible_keys(i, N, mode, W, G)
+        want = vf[j] if j in keys else vf[keys].mean(axis=0)
+        other = vf[keys].mean(axis=0) if j in keys else vf[j]
+        assert np.abs(og[i] - want).max() < 1e-2, (i, j)
+        assert np.abs(og[i] - other).max() > 5e-2, (i, j)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
-@pytest.mark.parametrize("mask", [(0, 0, 0), (1, 0, 0), (2, 30, 3)])
+@pytest.mark.parametrize("mask", [(0, 0, 0), (1, 0, 0), (2, 30, 3), (3, 40, 0), (4, 0, 60)])
 def test_never_reads_past_the_keys(dtype, mask):
     dev = require_gpu()
     B, H, Nq, Nkv, d = 1, 2, 150, 100, 128
@@ -173,7 +204,7 @@ def test_decode_matches_forward_and_causal_last_row(dtype):
         assert np.abs(f64(lc)[0, :, L - 1] - f64(lse)[s]).max() < 1e-3
 
 
-@pytest.mark.parametrize("mask", [(0, 0, 0), (1, 0, 0), (2, 100, 10)])
+@pytest.mark.parametrize("mask", [(0, 0, 0), (1, 0, 0), (2, 100, 10), (3, 300, 0), (4, 0, 500)])
 def test_bitwise_deterministic(mask):
     q, k, v = workloads.gen_prefill(2, 4, 700, 700, 128, "bf16", 15)
     qd, kd, vd = to_dev(q, k, v)

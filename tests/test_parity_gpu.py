@@ -35,7 +35,8 @@ def run_decode(inp, scale):
 
 
 MASKS = [(0, 0, 0), (1, 0, 0), (2, 40, 5), (2, 1, 0), (2, 100, 70), (2, 64, 64), (2, 200, 130),
-         (2, 65, 63)]
+         (2, 65, 63), (3, 0, 0), (3, 33, 0), (3, 200, 0), (3, 1000, 0), (4, 0, 0), (4, 0, 63),
+         (4, 0, 130), (4, 0, 1000)]
 SHAPES = [(1, 1, 1, 1), (1, 2, 17, 17), (2, 3, 100, 100), (1, 2, 129, 129), (1, 1, 300, 300),
           (1, 2, 64, 200), (1, 2, 200, 64), (1, 1, 1, 333), (1, 2, 257, 513)]
 
@@ -77,6 +78,9 @@ def test_dense_full_size_every_element(name):
     ("causal_bf16", (255, 256, 257, 1023, 1024, 2047, 2048, 4094)),
     ("window_bf16", (62, 63, 64, 65, 2046, 2047, 2048, 2049, 2110, 2111, 2112, 2113, 4095,
                      4096, 16383, 16384, 32766)),
+    ("band_bf16", (0, 1, 2047, 2048, 2049, 4095, 4096, 16384, 30718, 30719, 30720, 32766,
+                   32767)),
+    ("prefix_bf16", (0, 1, 127, 128, 1022, 1023, 1024, 1025, 2047, 4095)),
 ])
 def test_masked_full_size_sampled_rows(name, extra):
     w, inp = workloads.gen_workload(name)

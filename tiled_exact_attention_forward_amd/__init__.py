@@ -19,12 +19,12 @@ import os
 __all__ = ["fa_forward", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
            "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
-           "FA_MASK_WINDOW_GLOBAL", "EXPORTED_SYMBOLS"]
+           "FA_MASK_WINDOW_GLOBAL", "FA_MASK_BAND", "FA_MASK_PREFIX_LM", "EXPORTED_SYMBOLS"]
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
-FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL = 0, 1, 2
+FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = ("fa_forward", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
                     "fa_status_string", "fa_last_hip_error", "fa_version")
 

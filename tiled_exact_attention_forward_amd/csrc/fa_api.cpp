@@ -3,6 +3,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fa.h"
 #include "fa_launch.h"
 
@@ -48,10 +50,10 @@ int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse,
     if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-    if (mask_mode != FA_MASK_NONE && mask_mode != FA_MASK_CAUSAL &&
-        mask_mode != FA_MASK_WINDOW_GLOBAL)
-        return FA_ERR_UNSUPPORTED;
+    if (mask_mode < FA_MASK_NONE || mask_mode > FA_MASK_PREFIX_LM) return FA_ERR_UNSUPPORTED;
     if (mask_mode == FA_MASK_WINDOW_GLOBAL && (window < 1 || n_global < 0)) return FA_ERR_SHAPE;
+    if (mask_mode == FA_MASK_BAND && window < 0) return FA_ERR_SHAPE;
+    if (mask_mode == FA_MASK_PREFIX_LM && n_global < 0) return FA_ERR_SHAPE;
     const long long bh = (long long)B * H;
     const long long nqt = (Nq + 127) / 128;
     if (bh * nqt > (long long)INT_MAX) return FA_ERR_SHAPE;
@@ -60,9 +62,13 @@ int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse,
     if (!(scale == scale)) return FA_ERR_SHAPE;  // NaN scale
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return FA_ERR_UNSUPPORTED;
-    teaf::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nkv, d, scale,
-                    mask_mode, mask_mode == FA_MASK_WINDOW_GLOBAL ? window : 0,
-                    mask_mode == FA_MASK_WINDOW_GLOBAL ? n_global : 0, dtype};
+    // Window and global/prefix counts beyond Nq + Nkv and Nkv change nothing; clamping them
+    // keeps the kernels' position arithmetic inside int.
+    const bool uses_w = mask_mode == FA_MASK_WINDOW_GLOBAL || mask_mode == FA_MASK_BAND;
+    const bool uses_g = mask_mode == FA_MASK_WINDOW_GLOBAL || mask_mode == FA_MASK_PREFIX_LM;
+    const int wc = uses_w ? (int)std::min<long long>(window, (long long)Nq + Nkv) : 0;
+    const int gc = uses_g ? std::min(n_global, Nkv) : 0;
+    teaf::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nkv, d, scale, mask_mode, wc, gc, dtype};
     return hip_status(teaf::launch_forward(a, (hipStream_t)stream));
 }
 

@@ -70,6 +70,8 @@ __device__ __forceinline__ bool key_visible(int ip, int j, int W, int G)
 {
     if (MASK == 0) return true;
     if (MASK == 1) return j <= ip;
+    if (MASK == 3) return j >= ip - W && j <= ip + W;
+    if (MASK == 4) return j <= ip || j < G;
     return j <= ip && (ip - j < W || j < G);
 }
 
@@ -84,6 +86,22 @@ __device__ __forceinline__ TileRanges visible_tiles(int q0, int Nq, int Nkv, int
     TileRanges r{0, (Nkv + BN - 1) / BN, 0, 0};
     if (MASK == 0) return r;
     const int delta = Nkv - Nq;
+    if (MASK == 3) {  // band: from the first row's oldest key to the last row's newest key
+        const int lo = max(0, q0 + delta - W);
+        const int hi = min(Nkv - 1, min(q0 + BM, Nq) - 1 + delta + W);
+        if (hi < lo) {
+            r.a1 = 0;
+            return r;
+        }
+        r.a0 = lo / BN;
+        r.a1 = hi / BN + 1;
+        return r;
+    }
+    if (MASK == 4) {  // prefix LM: the prefix and everything up to the last row
+        const int last = min(Nkv - 1, max(min(q0 + BM, Nq) - 1 + delta, G - 1));
+        r.a1 = last < 0 ? 0 : last / BN + 1;
+        return r;
+    }
     const int last = min(Nkv - 1, min(q0 + BM, Nq) - 1 + delta);  // newest visible key
     if (last < 0) {
         r.a1 = 0;
@@ -103,10 +121,10 @@ __device__ __forceinline__ TileRanges visible_tiles(int q0, int Nq, int Nkv, int
 }
 
 // Key-tile schedule of one query tile: the visible tiles, ordered so that the tiles every
-// row of the tile sees completely ("interior": no mask, no skip, no tail) come first and
-// the remaining visible tiles ("edge") last: two interior ranges, then the visible parts of
-// the two gaps the interior leaves (slots for every pairing of gap and visible range).
-constexpr int kRanges = 6;
+// row of the tile sees completely ("interior": no mask, no tail) come first and the
+// remaining visible tiles ("edge") last: two interior ranges, then the visible parts of the
+// (up to three) gaps around them, one slot for every pairing of gap and visible range.
+constexpr int kRanges = 8;
 struct TileSchedule {
     int b[kRanges], e[kRanges];
     int interior, total;
@@ -144,7 +162,7 @@ __device__ __forceinline__ TileSchedule make_schedule(int q0, int Nq, int Nkv, i
     const int delta = Nkv - Nq;
     const int ip0 = q0 + delta, ip1 = q0 + BM - 1 + delta;
     int lim = Nkv / BN;  // tiles without a key tail
-    if (MASK >= 1) lim = min(lim, max(0, floor_div(ip0 + 1, BN)));  // causal for the first row
+    if (MASK == 1 || MASK == 2) lim = min(lim, max(0, floor_div(ip0 + 1, BN)));  // causal
     int i0b = 0, i0e = lim, i1b = 0, i1e = 0;
     if (MASK == 2) {
         const int gend = G / BN;                                   // all keys global
@@ -154,24 +172,33 @@ __device__ __forceinline__ TileSchedule make_schedule(int q0, int Nq, int Nkv, i
         i1e = lim;
         if (i1b >= i1e) i1b = i1e = 0;
     }
+    if (MASK == 3) {  // keys every row sees: [ip1 - W, ip0 + W]
+        i0b = max(0, -floor_div(-(ip1 - W), BN));
+        i0e = min(lim, floor_div(ip0 + W + 1, BN));
+    }
+    if (MASK == 4)  // keys every row sees: the prefix and everything up to the first row
+        i0e = min(lim, max(0, floor_div(max(G, ip0 + 1), BN)));
     if (i0e <= i0b) i0b = i0e = 0;
     s.b[0] = i0b; s.e[0] = i0e;
     s.b[1] = i1b; s.e[1] = i1e;
     s.interior = (i0e - i0b) + (i1e - i1b);
-    // edge ranges: the gaps between interior ranges, intersected with the visible ranges
+    // edge ranges: the gaps around the interior ranges, intersected with the visible ranges
     const int big = 0x3fffffff;
-    const bool has1 = i1e > i1b;
-    const int c0b = i0e, c0e = has1 ? i1b : big;   // gap after the first interior range
-    const int c1b = has1 ? i1e : 0, c1e = has1 ? big : 0;  // gap after the second one
+    const bool h0 = i0e > i0b, h1 = i1e > i1b;
+    const int ga_b = 0, ga_e = h0 ? i0b : (h1 ? i1b : big);      // before the interior
+    const int gb_b = h0 && h1 ? i0e : 0, gb_e = h0 && h1 ? i1b : 0;  // between the two
+    const int gc_b = h1 ? i1e : (h0 ? i0e : 0), gc_e = h0 || h1 ? big : 0;  // after it
     auto put = [&s](int slot, int lo0, int hi0, int lo1, int hi1) {
         const int lo = max(lo0, lo1), hi = min(hi0, hi1);
         s.b[slot] = hi > lo ? lo : 0;
         s.e[slot] = hi > lo ? hi : 0;
     };
-    put(2, c0b, c0e, v.a0, v.a1);
-    put(3, c0b, c0e, v.b0, v.b1);
-    put(4, c1b, c1e, v.a0, v.a1);
-    put(5, c1b, c1e, v.b0, v.b1);
+    put(2, ga_b, ga_e, v.a0, v.a1);
+    put(3, ga_b, ga_e, v.b0, v.b1);
+    put(4, gb_b, gb_e, v.a0, v.a1);
+    put(5, gb_b, gb_e, v.b0, v.b1);
+    put(6, gc_b, gc_e, v.a0, v.a1);
+    put(7, gc_b, gc_e, v.b0, v.b1);
     s.total = 0;
 #pragma unroll
     for (int q = 0; q < kRanges; ++q) s.total += s.e[q] - s.b[q];
@@ -361,13 +388,20 @@ __device__ __forceinline__ void mask_tile(f32x16 &s, int kv0, int ip, int Nkv, i
                                           int g)
 {
     const int base = kv0 + 4 * g;
-    const int hiR = (MASK == 0 ? Nkv - 1 : min(ip, Nkv - 1)) - base;
-    const int loR = (MASK == 2 ? ip - W + 1 : INT_MIN / 2) - base;
-    const int gR = (MASK == 2 ? G : 0) - base;
+    const int hiR = (MASK == 0 || MASK == 4 ? Nkv - 1
+                     : MASK == 3            ? min(ip + W, Nkv - 1)
+                                            : min(ip, Nkv - 1)) -
+                    base;
+    const int loR = (MASK == 2 ? ip - W + 1 : MASK == 3 ? ip - W : INT_MIN / 2) - base;
+    const int gR = (MASK == 2 || MASK == 4 ? G : 0) - base;
+    const int cR = ip - base;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int r = 8 * (e >> 2) + (e & 3);
-        const bool vis = r <= hiR && (MASK != 2 || r >= loR || r < gR);
+        bool vis = r <= hiR;
+        if (MASK == 2) vis = vis && (r >= loR || r < gR);
+        if (MASK == 3) vis = vis && r >= loR;
+        if (MASK == 4) vis = vis && (r <= cR || r < gR);
         s[e] = vis ? s[e] : -INFINITY;
     }
 }
@@ -692,8 +726,8 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float *__restrict__ Q,
         __syncthreads();
 
         bool skip = wrow0 >= Nq;
-        bool need_mask = kv0 + BN > Nkv;
-        if (MASK >= 1) {
+        bool need_mask = kv0 + BN > Nkv || MASK >= 3;
+        if (MASK == 1 || MASK == 2) {
             const int ip0 = wrow0 + delta, ip1 = wrow0 + 31 + delta;
             if (kv0 > ip1) skip = true;
             if (kv0 + BN - 1 > ip0) need_mask = true;
@@ -804,7 +838,9 @@ hipError_t launch16_mask(const FwdArgs &a, hipStream_t s)
     switch (a.mask) {
     case 0: return launch16<T, D, 0>(a, s);
     case 1: return launch16<T, D, 1>(a, s);
-    default: return launch16<T, D, 2>(a, s);
+    case 2: return launch16<T, D, 2>(a, s);
+    case 3: return launch16<T, D, 3>(a, s);
+    default: return launch16<T, D, 4>(a, s);
     }
 }
 
@@ -814,7 +850,9 @@ hipError_t launch32_mask(const FwdArgs &a, hipStream_t s)
     switch (a.mask) {
     case 0: return launch32<D, 0>(a, s);
     case 1: return launch32<D, 1>(a, s);
-    default: return launch32<D, 2>(a, s);
+    case 2: return launch32<D, 2>(a, s);
+    case 3: return launch32<D, 3>(a, s);
+    default: return launch32<D, 4>(a, s);
     }
 }
 

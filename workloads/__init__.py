@@ -22,7 +22,8 @@ import torch
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
-# name -> workload description. mask: 0 none, 1 causal, 2 causal sliding window + global keys.
+# name -> workload description. mask: 0 none, 1 causal, 2 causal sliding window + global keys,
+# 3 band of `window` positions on both sides, 4 prefix LM with an `n_global`-key prefix.
 WORKLOADS = {
     "tiny_f32": dict(kind="prefill", B=1, H=2, Nq=128, Nkv=128, d=64, dtype="f32", mask=0,
                      window=0, n_global=0, input_scale=1.0, seed=1),
@@ -34,6 +35,10 @@ WORKLOADS = {
                         mask=1, window=0, n_global=0, input_scale=0.5, seed=3),
     "window_bf16": dict(kind="prefill", B=1, H=32, Nq=32768, Nkv=32768, d=128, dtype="bf16",
                         mask=2, window=2048, n_global=64, input_scale=1.0, seed=4),
+    "band_bf16": dict(kind="prefill", B=1, H=32, Nq=32768, Nkv=32768, d=128, dtype="bf16",
+                      mask=3, window=2048, n_global=0, input_scale=1.0, seed=6),
+    "prefix_bf16": dict(kind="prefill", B=4, H=32, Nq=4096, Nkv=4096, d=128, dtype="bf16",
+                        mask=4, window=0, n_global=1024, input_scale=0.5, seed=7),
     "decode_f16": dict(kind="decode", S=8, H=32, d=128, dtype="f16", page_size=256,
                        len_lo=4096, len_hi=8192, max_len=8192, spare_pages=4, seed=5),
 }
