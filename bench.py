@@ -64,7 +64,18 @@ def visible_counts(Nq, Nkv, mode, W=0, G=0):
     return in_win + glob
 
 
-def prefill_flops(w):
+def block_sparse_pairs(layout, Nq, Nkv, block):
+    """Visible (query, key) pairs of a block layout [H, nqb, nkb], summed over heads."""
+    lay = np.asarray(layout, dtype=np.int64) != 0
+    rows = np.minimum(block, Nq - block * np.arange(lay.shape[1]))
+    keys = np.minimum(block, Nkv - block * np.arange(lay.shape[2]))
+    return int((lay * rows[None, :, None] * keys[None, None, :]).sum())
+
+
+def prefill_flops(w, layout=None):
+    if w["mask"] == 5:
+        pairs = block_sparse_pairs(layout, w["Nq"], w["Nkv"], w["block"]) * w["B"]
+        return 4 * w["d"] * pairs, pairs
     pairs = int(visible_counts(w["Nq"], w["Nkv"], w["mask"], w["window"], w["n_global"]).sum())
     return 4 * w["d"] * pairs * w["B"] * w["H"], pairs * w["B"] * w["H"]
 
@@ -144,12 +155,19 @@ def bench_prefill(name, steps, warmup, torch, fa, workloads, cold_calls=20):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     scale = workloads.default_scale(w["d"])
 
-    def step():
-        fa.fa_forward(q, k, v, scale, w["mask"], w["window"], w["n_global"], out=o, lse=lse)
+    if w["mask"] == 5:
+        lay = inp["layout"].to(dev)
+
+        def step():
+            fa.fa_forward_block_sparse(q, k, v, lay, w["block"], scale, out=o, lse=lse)
+    else:
+        def step():
+            fa.fa_forward(q, k, v, scale, w["mask"], w["window"], w["n_global"], out=o,
+                          lse=lse)
 
     ms, wall = time_calls(step, steps, warmup, torch)
     cold = time_cold(step, cold_calls, torch) if cold_calls else (ms, ms, ms)
-    flops, pairs = prefill_flops(w)
+    flops, pairs = prefill_flops(w, inp.get("layout"))
     elem = q.element_size()
     return dict(workload=name, w=w, ms=ms, wall_s=wall, flops=flops, pairs=pairs,
                 tflops=flops / (ms * 1e-3) / 1e12, bytes=prefill_bytes(w, elem), inputs=inp,
@@ -263,7 +281,7 @@ def main():
     others = {}
     if not args.only_headline:
         for name in ("dense_f16", "dense_bf16", "causal_bf16", "window_bf16", "band_bf16",
-                     "prefix_bf16"):
+                     "prefix_bf16", "blocksparse_bf16"):
             if name == args.workload:
                 continue
             r = bench_prefill(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch, fa,

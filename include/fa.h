@@ -96,6 +96,25 @@ int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse,
                int dtype, void *stream);
 
 /*
+ * fa_forward_block_sparse -- block-sparse attention forward (one of the sparse variants the
+ * ascend-transformer-boost article lists in 场景三; the pages name it without a format, read
+ * here as a layout of visible tiles).
+ *
+ *  q, k, v, o, lse, B, H, Nq, Nkv, d, scale, dtype, stream: as fa_forward.
+ *  layout  [H, ceil(Nq/block), ceil(Nkv/block)] uint8 DEVICE array, row-major: key j is
+ *          visible from query row i of head h when layout[h][i/block][j/block] != 0. The
+ *          same layout serves every batch entry. There is no shift between query and key
+ *          positions (row i and key i share a block index). A row whose layout row is all
+ *          zero gets O = 0 and LSE = -inf.
+ *  block   tile edge in positions; only 128 is built (FA_ERR_UNSUPPORTED otherwise).
+ *  Supported: as fa_forward, with Nkv <= 262144 (2048 key blocks; a workgroup keeps its
+ *  list of visible key blocks on chip). The layout's contents are not checked on the host.
+ */
+int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int Nq, int Nkv, int d, float scale,
+                            const uint8_t *layout, int block, int dtype, void *stream);
+
+/*
  * Paged single-token decode ("ascend-transformer-boost" article, 场景二: KV cache split
  * into fixed pages of 256 tokens, a new page per overflow, no reallocation; the attention
  * reads history K/V through the page layout). Each sequence has one query token at the

@@ -91,6 +91,23 @@ def test_decode_rejects_before_launch(kw, status):
     assert dec(**kw) == status
 
 
+def bs(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nkv=8, d=64, scale=0.125, layout=P,
+       block=128, dtype=1):
+    return fa.load_library().fa_forward_block_sparse(q, k, v, o, lse, B, H, Nq, Nkv, d, scale,
+                                                     layout, block, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=None), fa.FA_ERR_NULL), (dict(q=None), fa.FA_ERR_NULL),
+    (dict(block=64), fa.FA_ERR_UNSUPPORTED), (dict(block=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nkv=262145), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED), (dict(Nq=0), fa.FA_ERR_SHAPE),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+])
+def test_block_sparse_rejects_before_launch(kw, status):
+    assert bs(**kw) == status
+
+
 def test_decode_workspace_bytes():
     lib = fa.load_library()
     # 8 sequences, 32 heads, d 128, 32 pages of 256 tokens: 128 splits of 64 tokens,

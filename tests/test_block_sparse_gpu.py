@@ -1,0 +1,105 @@
+"""Block-sparse forward (fa_forward_block_sparse) against the fp64 oracle on the GPU.
+
+Small shapes compare every element over random layouts (including query blocks with no
+visible key block, and ragged query and key tails); the full-size workload compares sampled
+rows that include the first and last rows of several query blocks. An all-ones layout must
+reproduce the unmasked forward pass bit for bit (same kernel, same tile order).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_forward_amd as fa
+import workloads
+from gpu_util import check, f64, gather_rows, require_gpu, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bs(q, k, v, layout, scale):
+    qd, kd, vd = to_dev(q, k, v)
+    o, lse = fa.fa_forward_block_sparse(qd, kd, vd, layout.to(qd.device), 128, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+SHAPES = [(1, 1, 1, 1), (1, 2, 128, 128), (2, 3, 200, 300), (1, 2, 300, 200), (1, 1, 513, 257),
+          (1, 2, 64, 1000), (1, 1, 1000, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("density", [0.0, 0.3, 1.0])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(dtype, d, density, shape):
+    B, H, Nq, Nkv = shape
+    seed = zlib.crc32(repr((dtype, d, density, shape)).encode()) % 100000
+    q, k, v = workloads.gen_prefill(B, H, Nq, Nkv, d, dtype, seed)
+    g = torch.Generator("cpu").manual_seed(seed + 1)
+    nqb, nkb = -(-Nq // 128), -(-Nkv // 128)
+    lay = (torch.rand((H, nqb, nkb), generator=g) < density).to(torch.uint8)
+    scale = workloads.default_scale(d)
+    o, lse = run_bs(q, k, v, lay, scale)
+    ro, rl = oracle.attention_block_sparse(q, k, v, scale, lay.numpy(), 128)
+    check(o, lse, ro, rl, dtype, f"block sparse {dtype} d{d} p{density} {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_all_ones_layout_equals_unmasked_bitwise(dtype):
+    q, k, v = workloads.gen_prefill(2, 2, 300, 420, 128, dtype, 21)
+    lay = torch.ones((2, 3, 4), dtype=torch.uint8)
+    o, lse = run_bs(q, k, v, lay, 0.0884)
+    qd, kd, vd = to_dev(q, k, v)
+    o0, l0 = fa.fa_forward(qd, kd, vd, 0.0884, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(lse, l0)
+
+
+def test_empty_layout_rows_give_zero_and_minus_inf():
+    q, k, v = workloads.gen_prefill(1, 2, 256, 256, 128, "bf16", 22)
+    lay = torch.zeros((2, 2, 2), dtype=torch.uint8)
+    lay[0, 1, 0] = 1
+    o, lse = run_bs(q, k, v, lay, 0.0884)
+    of, lf = f64(o), f64(lse)
+    assert np.all(of[0, 0, :128] == 0) and np.all(np.isneginf(lf[0, 0, :128]))
+    assert np.all(of[0, 1] == 0) and np.all(np.isneginf(lf[0, 1]))
+    assert np.all(np.isfinite(lf[0, 0, 128:]))
+    ro, rl = oracle.attention_block_sparse(q, k, v, 0.0884, lay.numpy(), 128)
+    check(o, lse, ro, rl, "bf16", "empty rows")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_never_reads_past_the_keys(dtype):
+    dev = require_gpu()
+    B, H, Nq, Nkv, d = 1, 2, 150, 200, 128
+    q, k, v = workloads.gen_prefill(B, H, Nq, Nkv, d, dtype, 23)
+    n = k.numel()
+    pad = 64 * 128 * 4
+    ks = torch.full((n + pad,), float("nan"), dtype=k.dtype, device=dev)
+    vs = torch.full((n + pad,), float("nan"), dtype=k.dtype, device=dev)
+    ks[:n] = k.reshape(-1).to(dev)
+    vs[:n] = v.reshape(-1).to(dev)
+    lay = torch.ones((H, 2, 2), dtype=torch.uint8)
+    lay[1, 0, 1] = 0
+    o, lse = fa.fa_forward_block_sparse(q.to(dev), ks[:n].view(k.shape), vs[:n].view(v.shape),
+                                        lay.to(dev), 128, 0.0884)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_block_sparse(q, k, v, 0.0884, lay.numpy(), 128)
+    check(o, lse, ro, rl, dtype, "nan canary block sparse")
+
+
+def test_full_size_sampled_rows():
+    w, inp = workloads.gen_workload("blocksparse_bf16")
+    scale = workloads.default_scale(w["d"])
+    o, lse = run_bs(inp["q"], inp["k"], inp["v"], inp["layout"], scale)
+    extra = (0, 127, 128, 255, 8191, 8192, 16255, 16256, 16383)
+    rows = sample_rows(w["B"], w["H"], w["Nq"], extra=extra, per_head=24, seed=w["seed"])
+    ro, rl = oracle.attention_block_sparse(inp["q"], inp["k"], inp["v"], scale,
+                                           inp["layout"].numpy(), w["block"], rows=rows)
+    og, lg = gather_rows(o, lse, rows)
+    e = check(og, lg, ro, rl, w["dtype"], "blocksparse_bf16")
+    print("blocksparse_bf16", len(rows), "rows", e)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()

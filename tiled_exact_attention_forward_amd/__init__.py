@@ -16,7 +16,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_forward", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+__all__ = ["fa_forward", "fa_forward_block_sparse", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
            "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
            "FA_MASK_WINDOW_GLOBAL", "FA_MASK_BAND", "FA_MASK_PREFIX_LM", "EXPORTED_SYMBOLS"]
@@ -25,8 +25,9 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_H
     0, -1, -2, -3, -4, -5)
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
-EXPORTED_SYMBOLS = ("fa_forward", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
-                    "fa_status_string", "fa_last_hip_error", "fa_version")
+EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_decode_paged",
+                    "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_last_hip_error",
+                    "fa_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -59,6 +60,8 @@ def load_library():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
     lib.fa_forward.restype = i
+    lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i, vp]
+    lib.fa_forward_block_sparse.restype = i
     lib.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_paged_workspace_bytes.restype = sz
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
@@ -145,6 +148,37 @@ def fa_forward(q, k, v, scale=None, mask_mode=FA_MASK_NONE, window=0, n_global=0
                                    int(n_global), _dtype_code(q), _stream(stream))
     if rc != FA_OK:
         raise FaError(rc, "fa_forward")
+    return out, lse
+
+
+def fa_forward_block_sparse(q, k, v, layout, block=128, scale=None, out=None, lse=None,
+                            stream=None):
+    """Block-sparse attention: layout is a uint8 GPU tensor [H, ceil(Nq/block),
+    ceil(Nkv/block)] (nonzero = visible tile), shared by every batch entry. Other arguments
+    and the result as fa_forward."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Nkv, d) or tuple(v.shape) != (B, H, Nkv, d):
+        raise ValueError("k and v must be [B,H,Nkv,d] matching q")
+    want = (H, -(-Nq // block), -(-Nkv // block))
+    if tuple(layout.shape) != want or not layout.is_contiguous():
+        raise ValueError(f"layout must be a contiguous {want} tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("layout", layout, torch.uint8)
+    rc = load_library().fa_forward_block_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, d, float(scale),
+        _ptr(layout), int(block), _dtype_code(q), _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_forward_block_sparse")
     return out, lse
 
 

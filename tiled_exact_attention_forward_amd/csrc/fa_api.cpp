@@ -72,6 +72,30 @@ int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse,
     return hip_status(teaf::launch_forward(a, (hipStream_t)stream));
 }
 
+int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int Nq, int Nkv, int d, float scale,
+                            const uint8_t *layout, int block, int dtype, void *stream)
+{
+    if (!q || !k || !v || !o || !lse || !layout) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (block != teaf::kBlockSparseEdge) return FA_ERR_UNSUPPORTED;
+    if ((long long)Nkv > (long long)teaf::kBlockSparseMaxKeyBlocks * teaf::kBlockSparseEdge)
+        return FA_ERR_UNSUPPORTED;
+    const long long bh = (long long)B * H;
+    const long long nqt = (Nq + 127) / 128;
+    if (bh * nqt > (long long)INT_MAX) return FA_ERR_SHAPE;
+    if ((long long)Nq * d > (long long)INT_MAX || (long long)Nkv * d > (long long)INT_MAX)
+        return FA_ERR_SHAPE;
+    if (!(scale == scale)) return FA_ERR_SHAPE;  // NaN scale
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return FA_ERR_UNSUPPORTED;
+    teaf::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nkv, d, scale, teaf::kMaskBlockSparse, 0, 0,
+                    dtype, layout};
+    return hip_status(teaf::launch_forward(a, (hipStream_t)stream));
+}
+
 size_t fa_decode_paged_workspace_bytes(int num_seqs, int H, int d, int max_pages_per_seq,
                                        int page_size)
 {

@@ -54,6 +54,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kXcds = 8;
+// Mask id of the block-sparse path (layout of kSparseBlock x kSparseBlock tiles) and the
+// largest number of key blocks a query block's list holds.
+constexpr int kBlockSparse = kMaskBlockSparse, kSparseBlock = kBlockSparseEdge,
+              kMaxKeyBlocks = kBlockSparseMaxKeyBlocks;
 
 
 // Hardware hands consecutive workgroup ids to the 8 XCDs in turn. Map id w (of n) to a
@@ -68,7 +72,7 @@ __device__ __forceinline__ int xcd_remap(int w, int n)
 template <int MASK>
 __device__ __forceinline__ bool key_visible(int ip, int j, int W, int G)
 {
-    if (MASK == 0) return true;
+    if (MASK == 0 || MASK == kBlockSparse) return true;  // block sparse: decided per tile
     if (MASK == 1) return j <= ip;
     if (MASK == 3) return j >= ip - W && j <= ip + W;
     if (MASK == 4) return j <= ip || j < G;
@@ -84,7 +88,7 @@ template <int MASK, int BM, int BN>
 __device__ __forceinline__ TileRanges visible_tiles(int q0, int Nq, int Nkv, int W, int G)
 {
     TileRanges r{0, (Nkv + BN - 1) / BN, 0, 0};
-    if (MASK == 0) return r;
+    if (MASK == 0 || MASK == kBlockSparse) return r;
     const int delta = Nkv - Nq;
     if (MASK == 3) {  // band: from the first row's oldest key to the last row's newest key
         const int lo = max(0, q0 + delta - W);
@@ -512,7 +516,7 @@ template <typename T, int D, int MASK, int NS, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
-    int Nkv, float c, int W, int G, int nqt)
+    int Nkv, float c, int W, int G, int nqt, const uint8_t *__restrict__ layout, int H)
 {
     using C = CfgSP<D, NS, NW>;
     using Op = Ops16<T>;
@@ -545,8 +549,62 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
         for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = *(const s16x8 *)(qr + 16 * kk);
     }
 
-    const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);
-    const int ntl = sch.total, nint = sch.interior;
+    char *const lds = (char *)smem;
+    // Range schedule (masks 0-4), or for the block-sparse mask a list of the visible key
+    // blocks of this query block, built in LDS after the K/V ring.
+    const TileSchedule sch = make_schedule<MASK == kBlockSparse ? 0 : MASK, BM, BN>(
+        q0, Nq, Nkv, W, G);
+    int ntl = sch.total, nint = sch.interior;
+    const uint16_t *blist = (const uint16_t *)(lds + C::LDS_BYTES + 16);
+    const int tail_kv0 = ((Nkv + BN - 1) / BN - 1) * BN;  // first key of the last key tile
+    if constexpr (MASK == kBlockSparse) {
+        static_assert(BM == kSparseBlock && kSparseBlock % BN == 0, "one query block per tile");
+        constexpr int TPB = kSparseBlock / BN, CH = kMaxKeyBlocks / (64 * NW);
+        const int nkb = (Nkv + kSparseBlock - 1) / kSparseBlock;
+        const uint8_t *lrow = layout + ((size_t)(bh % H) * nqt + q0 / kSparseBlock) * nkb;
+        int *wcnt = (int *)(lds + C::LDS_BYTES);
+        uint16_t *bl = (uint16_t *)(lds + C::LDS_BYTES + 16);
+        bool f[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {  // all layout loads first, one wait
+            const int b = u * 64 * NW + tid;
+            f[u] = b < nkb && lrow[b] != 0;
+        }
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            if (u * 64 * NW >= nkb) break;
+            const unsigned long long mk = __ballot(f[u]);
+            if (lane == 0) wcnt[wave] = __popcll(mk);
+            __syncthreads();
+            int before = 0, total = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int cw = wcnt[w];
+                before += w < wave ? cw : 0;
+                total += cw;
+            }
+            if (f[u])
+                bl[n + before + __popcll(mk & ((1ull << lane) - 1))] =
+                    (uint16_t)(u * 64 * NW + tid);
+            n += total;
+            __syncthreads();
+        }
+        // stream position p holds tile TPB * blist[p / TPB] + p % TPB; only the final key
+        // block can have fewer tiles, and it comes last; only the key-tail tile is masked
+        if (n == 0) {
+            ntl = nint = 0;
+        } else {
+            const int lastb = __builtin_amdgcn_readfirstlane((int)bl[n - 1]);
+            const int all = (Nkv + BN - 1) / BN;
+            ntl = TPB * (n - 1) + (lastb == nkb - 1 ? all - TPB * lastb : TPB);
+            nint = ntl - (lastb == nkb - 1 && Nkv % BN != 0 ? 1 : 0);
+        }
+    }
+    auto bs_tile = [&](int p) {
+        constexpr int TPB = kSparseBlock / BN;
+        return __builtin_amdgcn_readfirstlane((int)blist[p / TPB] * TPB + p % TPB);
+    };
 
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[C::NDB];
@@ -577,7 +635,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
             vofs[db] = trow * C::ROWB + 16 * v_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
     }
 
-    char *const lds = (char *)smem;
     auto kslot = [&](int t) { return lds + (t % NS) * C::TILEB; };
     auto vslot = [&](int t) { return lds + C::VREG + (t % NS) * C::TILEB; };
 
@@ -586,7 +643,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) {
         if (j < ntl) {
-            issue_kv<C>(kbh, vbh, off, ld.t * BN, Nkv, kslot(j), vslot(j), wave);
+            const int tl = MASK == kBlockSparse ? bs_tile(j) : ld.t;
+            issue_kv<C>(kbh, vbh, off, tl * BN, Nkv, kslot(j), vslot(j), wave);
             ld = sch.next(ld);
         }
     }
@@ -606,7 +664,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
         for (int kk = 0; kk < C::NKK; ++kk)
             sa = Op::mma(*(const s16x8 *)(kslot(0) + kofs[kk]), qf[kk],
                          kk == 0 ? f32x16{} : sa);
-        if (nint == 0) mask_tile<MASK>(sa, nx.t * BN, ip, Nkv, W, G, g);
+        if (nint == 0)
+            mask_tile<MASK == kBlockSparse ? 0 : MASK>(
+                sa, MASK == kBlockSparse ? tail_kv0 : nx.t * BN, ip, Nkv, W, G, g);
         mt = half_swap_max(max16(sa)) * c;
         nx = sch.next(nx);
     }
@@ -618,7 +678,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     };
     auto load_ahead = [&](int t) {
         if (t + NS - 1 < ntl) {
-            issue_kv<C>(kbh, vbh, off, ld.t * BN, Nkv, kslot(t + NS - 1), vslot(t + NS - 1),
+            const int tl = MASK == kBlockSparse ? bs_tile(t + NS - 1) : ld.t;
+            issue_kv<C>(kbh, vbh, off, tl * BN, Nkv, kslot(t + NS - 1), vslot(t + NS - 1),
                         wave);
             ld = sch.next(ld);
         }
@@ -627,14 +688,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     // step in the loop has a tile t+1; the last step is peeled.
     auto step = [&](int t, f32x16 &cur, f32x16 &nxt) {
         load_ahead(t);
-        sp_step<T, C, MASK, true>(kslot(t + 1), vslot(t), kofs, vofs, qf, oacc, cur, nxt, m,
-                                      l, mt, c, t + 1 >= nint, nx.t * BN, ip, Nkv, W, G, g);
+        sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, true>(
+            kslot(t + 1), vslot(t), kofs, vofs, qf, oacc, cur, nxt, m, l, mt, c, t + 1 >= nint,
+            MASK == kBlockSparse ? tail_kv0 : nx.t * BN, ip, Nkv, W, G, g);
         nx = sch.next(nx);
         step_end(t);
     };
     auto last = [&](int t, f32x16 &cur, f32x16 &nxt) {
-        sp_step<T, C, MASK, false>(nullptr, vslot(t), kofs, vofs, qf, oacc, cur, nxt, m, l,
-                                       mt, c, false, 0, ip, Nkv, W, G, g);
+        sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, false>(
+            nullptr, vslot(t), kofs, vofs, qf, oacc, cur, nxt, m, l, mt, c, false, 0, ip, Nkv, W,
+            G, g);
     };
     if (ntl > 0) {
         int t = 0;
@@ -677,7 +740,8 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float *__restrict__ Q,
                                                     const float *__restrict__ K,
                                                     const float *__restrict__ V,
                                                     float *__restrict__ O, float *__restrict__ LSE,
-                                                    int Nq, int Nkv, float c, int W, int G, int nqt)
+                                                    int Nq, int Nkv, float c, int W, int G, int nqt,
+                                                    const uint8_t *__restrict__ layout, int H)
 {
     constexpr int BM = 128, BN = 32, NT = 256, KP = D + 1;
     constexpr int NKK = D / 2, NDB = D / 32, RC = D / 4, CPT = BN * RC / NT;
@@ -707,9 +771,15 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float *__restrict__ Q,
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
 
+    const uint8_t *lrow = nullptr;
+    if (MASK == kBlockSparse) {
+        const int nkb = (Nkv + kSparseBlock - 1) / kSparseBlock;
+        lrow = layout + ((size_t)(bh % H) * nqt + q0 / kSparseBlock) * nkb;
+    }
     for (int n = 0; n < ntiles; ++n) {
         const int tile = n < na ? tr.a0 + n : tr.b0 + (n - na);
         const int kv0 = tile * BN;
+        if (MASK == kBlockSparse && lrow[kv0 / kSparseBlock] == 0) continue;  // whole workgroup
         __syncthreads();  // previous tile's readers are done
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
@@ -726,7 +796,7 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float *__restrict__ Q,
         __syncthreads();
 
         bool skip = wrow0 >= Nq;
-        bool need_mask = kv0 + BN > Nkv || MASK >= 3;
+        bool need_mask = kv0 + BN > Nkv || MASK == 3 || MASK == 4;
         if (MASK == 1 || MASK == 2) {
             const int ip0 = wrow0 + delta, ip1 = wrow0 + 31 + delta;
             if (kv0 > ip1) skip = true;
@@ -811,13 +881,15 @@ hipError_t launch16(const FwdArgs &a, hipStream_t s)
     const int nqt = (a.Nq + C::BM - 1) / C::BM;
     const long nblk = (long)nqt * a.B * a.H;
     auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves>;
+    // block sparse: wave counts and the key-block list (2 bytes a block) after the ring
+    const int lds = MASK == kBlockSparse ? C::LDS_BYTES + 16 + 2 * kMaxKeyBlocks : C::LDS_BYTES;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), C::LDS_BYTES, s,
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), lds, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        (uint16_t *)a.o, a.lse, a.Nq, a.Nkv, a.scale * kLog2e, a.window,
-                       a.n_global, nqt);
+                       a.n_global, nqt, a.layout, a.H);
     return hipGetLastError();
 }
 
@@ -828,7 +900,8 @@ hipError_t launch32(const FwdArgs &a, hipStream_t s)
     const long nblk = (long)nqt * a.B * a.H;
     hipLaunchKernelGGL((fwd32_kernel<D, MASK>), dim3((unsigned)nblk), dim3(256), 0, s,
                        (const float *)a.q, (const float *)a.k, (const float *)a.v, (float *)a.o,
-                       a.lse, a.Nq, a.Nkv, a.scale * kLog2e, a.window, a.n_global, nqt);
+                       a.lse, a.Nq, a.Nkv, a.scale * kLog2e, a.window, a.n_global, nqt,
+                       a.layout, a.H);
     return hipGetLastError();
 }
 
@@ -840,7 +913,8 @@ hipError_t launch16_mask(const FwdArgs &a, hipStream_t s)
     case 1: return launch16<T, D, 1>(a, s);
     case 2: return launch16<T, D, 2>(a, s);
     case 3: return launch16<T, D, 3>(a, s);
-    default: return launch16<T, D, 4>(a, s);
+    case 4: return launch16<T, D, 4>(a, s);
+    default: return launch16<T, D, kBlockSparse>(a, s);
     }
 }
 
@@ -852,7 +926,8 @@ hipError_t launch32_mask(const FwdArgs &a, hipStream_t s)
     case 1: return launch32<D, 1>(a, s);
     case 2: return launch32<D, 2>(a, s);
     case 3: return launch32<D, 3>(a, s);
-    default: return launch32<D, 4>(a, s);
+    case 4: return launch32<D, 4>(a, s);
+    default: return launch32<D, kBlockSparse>(a, s);
     }
 }
 

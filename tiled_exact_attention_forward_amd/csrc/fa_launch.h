@@ -14,7 +14,12 @@ struct FwdArgs {
     int B, H, Nq, Nkv, d;
     float scale;
     int mask, window, n_global, dtype;
+    const uint8_t *layout;  // block-sparse layout (mask 5), else null
 };
+
+// Block-sparse forward: mask id, tile edge and the largest key-block count a query block's
+// visible-block list holds in LDS.
+constexpr int kMaskBlockSparse = 5, kBlockSparseEdge = 128, kBlockSparseMaxKeyBlocks = 2048;
 
 struct DecodeArgs {
     const void *q, *k_pages, *v_pages;

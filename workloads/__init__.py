@@ -23,7 +23,8 @@ import torch
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 # name -> workload description. mask: 0 none, 1 causal, 2 causal sliding window + global keys,
-# 3 band of `window` positions on both sides, 4 prefix LM with an `n_global`-key prefix.
+# 3 band of `window` positions on both sides, 4 prefix LM with an `n_global`-key prefix,
+# 5 block sparse (a seeded layout of block x block tiles, see gen_layout).
 WORKLOADS = {
     "tiny_f32": dict(kind="prefill", B=1, H=2, Nq=128, Nkv=128, d=64, dtype="f32", mask=0,
                      window=0, n_global=0, input_scale=1.0, seed=1),
@@ -39,6 +40,9 @@ WORKLOADS = {
                       mask=3, window=2048, n_global=0, input_scale=1.0, seed=6),
     "prefix_bf16": dict(kind="prefill", B=4, H=32, Nq=4096, Nkv=4096, d=128, dtype="bf16",
                         mask=4, window=0, n_global=1024, input_scale=0.5, seed=7),
+    "blocksparse_bf16": dict(kind="prefill", B=1, H=32, Nq=16384, Nkv=16384, d=128,
+                             dtype="bf16", mask=5, window=0, n_global=0, input_scale=1.0,
+                             seed=8, block=128, density=0.125),
     "decode_f16": dict(kind="decode", S=8, H=32, d=128, dtype="f16", page_size=256,
                        len_lo=4096, len_hi=8192, max_len=8192, spare_pages=4, seed=5),
 }
@@ -61,6 +65,19 @@ def gen_prefill(B, H, Nq, Nkv, d, dtype, seed, input_scale=1.0):
         v.mul_(input_scale)
     t = DTYPES[dtype]
     return q.to(t), k.to(t), v.to(t)
+
+
+def gen_layout(H, Nq, Nkv, block, density, seed):
+    """Block-sparse layout [H, ceil(Nq/block), ceil(Nkv/block)] uint8: each tile visible with
+    probability `density` (one uniform draw per tile from a generator seeded `seed`), plus
+    the diagonal tiles, so that every query block sees at least one key block when
+    Nkv >= Nq."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    nqb, nkb = -(-Nq // block), -(-Nkv // block)
+    lay = (torch.rand((H, nqb, nkb), generator=g) < density).to(torch.uint8)
+    n = min(nqb, nkb)
+    lay[:, torch.arange(n), torch.arange(n)] = 1
+    return lay
 
 
 def gen_decode(S, H, d, dtype, seed, page_size=256, len_lo=4096, len_hi=8192, max_len=None,
@@ -113,7 +130,11 @@ def gen_workload(name, **override):
     if w["kind"] == "prefill":
         q, k, v = gen_prefill(w["B"], w["H"], w["Nq"], w["Nkv"], w["d"], w["dtype"], w["seed"],
                               w.get("input_scale", 1.0))
-        return w, dict(q=q, k=k, v=v)
+        out = dict(q=q, k=k, v=v)
+        if w["mask"] == 5:  # block sparse: the layout comes after the tensors, own seed
+            out["layout"] = gen_layout(w["H"], w["Nq"], w["Nkv"], w["block"], w["density"],
+                                       w["seed"] + 1000)
+        return w, out
     inp = gen_decode(w["S"], w["H"], w["d"], w["dtype"], w["seed"], w["page_size"],
                      w["len_lo"], w["len_hi"], w.get("max_len"), w.get("spare_pages", 4),
                      w.get("lens"))
