@@ -11,7 +11,8 @@ inputs, closed forms (Q = 0 gives the mean of the visible V rows and LSE = ln(co
 invariants (rows sum to one, shift and permutation invariance, split-and-merge of keys),
 one-hot edge probes of every mask boundary, and reductions between masks (a band or prefix
 covering every key is the unmasked case, an empty prefix is causal, an all-ones block layout
-is unmasked).
+is unmasked). The gradients are pinned to torch autograd in float64, central finite
+differences of the forward pass and the invariants of the softmax Jacobian.
 """
 import ctypes
 import os
@@ -45,6 +46,11 @@ class Oracle:
             ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_uint8), ctypes.c_long, i64p,
             ctypes.c_long, f64p, f64p]
         lib.oracle_attention_block_sparse_rows.restype = ctypes.c_int
+        lib.oracle_attention_backward.argtypes = [
+            f32p, f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_long, ctypes.c_long, f64p,
+            f64p, f64p]
+        lib.oracle_attention_backward.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -83,6 +89,27 @@ class Oracle:
         if rows is None:
             return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
         return o, lse
+
+    def attention_backward(self, q, k, v, dout, scale, mask_mode=0, window=0, n_global=0):
+        """Gradients (dq, dk, dv) of exact attention for upstream gradient dout, fp64.
+
+        q, dout: [B,H,Nq,d]; k, v: [B,H,Nkv,d]. Returns float64 arrays of the same shapes.
+        """
+        q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        assert k.shape == (B, H, Nkv, d) and v.shape == k.shape and g.shape == q.shape
+        dq = np.empty(q.shape, np.float64)
+        dk = np.empty(k.shape, np.float64)
+        dv = np.empty(k.shape, np.float64)
+        rc = self.lib.oracle_attention_backward(
+            _p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
+            _p(g, ctypes.c_float), B, H, Nq, Nkv, d, float(np.float32(scale)), int(mask_mode),
+            int(window), int(n_global), _p(dq, ctypes.c_double), _p(dk, ctypes.c_double),
+            _p(dv, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_attention_backward rejected its arguments")
+        return dq, dk, dv
 
     def attention_block_sparse(self, q, k, v, scale, layout, block, rows=None):
         """Exact block-sparse attention in fp64.
@@ -183,6 +210,10 @@ def attention(*args, **kw):
 
 def attention_block_sparse(*args, **kw):
     return default().attention_block_sparse(*args, **kw)
+
+
+def attention_backward(*args, **kw):
+    return default().attention_backward(*args, **kw)
 
 
 def decode_paged(*args, **kw):

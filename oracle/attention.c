@@ -232,6 +232,102 @@ int oracle_attention_block_sparse_rows(const float *q, const float *k, const flo
 }
 
 /*
+ * Gradients of exact attention with respect to Q, K and V for an upstream gradient dO, in
+ * fp64, from the plain definition (the pages stress that the score matrix is recomputed,
+ * not stored, for the backward pass: ops-transformer article on zwxr.cn, section 2.2,
+ * gradient checkpointing; here the oracle simply materialises each row again):
+ *   P_ij  = exp(s_ij - m_i) / l_i                 (0 for hidden keys)
+ *   D_i   = sum_c dO_ic O_ic                       (O from the same P)
+ *   dP_ij = sum_c dO_ic v_jc
+ *   dS_ij = P_ij (dP_ij - D_i)                     (softmax Jacobian)
+ *   dQ_i  = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i
+ * Masks as oracle_attention_rows. All outputs [B,H,N,d] doubles. Parallel over (b, h).
+ */
+int oracle_attention_backward(const float *q, const float *k, const float *v, const float *dout,
+                              int B, int H, long Nq, long Nkv, int d, double scale, int mode,
+                              long window, long n_global, double *dq, double *dk, double *dv)
+{
+    int failed = 0;
+    long bh;
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || mode < 0 || mode > 4)
+        return -1;
+    memset(dk, 0, sizeof(double) * (size_t)B * H * Nkv * d);
+    memset(dv, 0, sizeof(double) * (size_t)B * H * Nkv * d);
+
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)Nkv);
+        double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (p == NULL || orow == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (bh = 0; bh < (long)B * H; ++bh) {
+                const float *qb = q + (size_t)bh * Nq * d, *kb = k + (size_t)bh * Nkv * d;
+                const float *vb = v + (size_t)bh * Nkv * d, *gb = dout + (size_t)bh * Nq * d;
+                double *dqb = dq + (size_t)bh * Nq * d, *dkb = dk + (size_t)bh * Nkv * d;
+                double *dvb = dv + (size_t)bh * Nkv * d;
+                long i, j;
+                int c;
+                for (i = 0; i < Nq; ++i) {
+                    const float *qi = qb + (size_t)i * d, *gi = gb + (size_t)i * d;
+                    const long ip = i + (Nkv - Nq);
+                    double m = -INFINITY, l = 0.0, D = 0.0;
+                    for (j = 0; j < Nkv; ++j) {
+                        double dot = 0.0;
+                        if (!key_visible(ip, j, mode, window, n_global)) {
+                            p[j] = -INFINITY;
+                            continue;
+                        }
+                        for (c = 0; c < d; ++c)
+                            dot += (double)qi[c] * (double)kb[(size_t)j * d + c];
+                        p[j] = scale * dot;
+                        if (p[j] > m)
+                            m = p[j];
+                    }
+                    for (c = 0; c < d; ++c)
+                        orow[c] = 0.0;
+                    for (c = 0; c < d; ++c)
+                        dqb[(size_t)i * d + c] = 0.0;
+                    if (m == -INFINITY)
+                        continue; /* no visible key: every gradient term is zero */
+                    for (j = 0; j < Nkv; ++j) {
+                        p[j] = (p[j] == -INFINITY) ? 0.0 : exp(p[j] - m);
+                        l += p[j];
+                    }
+                    for (j = 0; j < Nkv; ++j) {
+                        p[j] /= l;
+                        if (p[j] == 0.0)
+                            continue;
+                        for (c = 0; c < d; ++c)
+                            orow[c] += p[j] * (double)vb[(size_t)j * d + c];
+                    }
+                    for (c = 0; c < d; ++c)
+                        D += (double)gi[c] * orow[c];
+                    for (j = 0; j < Nkv; ++j) {
+                        double dp = 0.0, ds;
+                        if (p[j] == 0.0)
+                            continue;
+                        for (c = 0; c < d; ++c)
+                            dp += (double)gi[c] * (double)vb[(size_t)j * d + c];
+                        ds = p[j] * (dp - D);
+                        for (c = 0; c < d; ++c) {
+                            dqb[(size_t)i * d + c] += scale * ds * (double)kb[(size_t)j * d + c];
+                            dkb[(size_t)j * d + c] += scale * ds * (double)qi[c];
+                            dvb[(size_t)j * d + c] += p[j] * (double)gi[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(orow);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
  * Single-token decode against a paged K/V cache ("ascend-transformer-boost" article, 场景二:
  * the cache is cut into fixed pages of page_size tokens; a sequence's pages need not be
  * contiguous). Pages are [num_pages, page_size, H, d]; logical token j of sequence s lives

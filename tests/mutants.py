@@ -28,6 +28,14 @@ MUTANTS = {
     "block_query_index": ("(size_t)(i / block)) * nkb", "(size_t)((i + 1) / block)) * nkb"),
     "block_key_index": ("lrow[j / block] != 0", "lrow[(j + 1) / block] != 0"),
     "block_head": ("long h = bh % H;", "long h = 0;"),
+    "bwd_no_rowterm": ("ds = p[j] * (dp - D);", "ds = p[j] * dp;"),
+    "bwd_dk_no_scale": ("dkb[(size_t)j * d + c] += scale * ds", "dkb[(size_t)j * d + c] += ds"),
+    "bwd_dv_from_ds": ("dvb[(size_t)j * d + c] += p[j] * (double)gi[c];",
+                       "dvb[(size_t)j * d + c] += ds * (double)gi[c];"),
+    "bwd_rowterm_from_v": ("D += (double)gi[c] * orow[c];",
+                           "D += (double)gi[c] * (double)vb[c];"),
+    "bwd_dq_uses_q": ("scale * ds * (double)kb[(size_t)j * d + c];",
+                      "scale * ds * (double)qi[c];"),
 }
 
 

@@ -14,6 +14,8 @@ source) and raises AssertionError when the oracle disagrees with:
   * one-hot probes that put a dominant score on one key and check which V row comes out, at
     every mask edge: the causal diagonal, the key after it, the first and last key of the
     window, the last global key and the key after it.
+The backward oracle is pinned to torch autograd in float64, to central finite differences of
+the oracle's own forward pass, and to exact invariants of the softmax Jacobian.
 Masks: 0 none, 1 causal (diagonal kept, aligned bottom-right), 2 causal window of W keys
 ending at the query plus the first G keys, 3 band of W positions on both sides of the query,
 4 prefix LM (the first G keys visible to every query, the rest causal); block sparse takes a
@@ -540,8 +542,90 @@ def pin_more_mask_reductions(orc):
         assert np.array_equal(ob, on) and np.array_equal(lb, ln), blk
 
 
+# --------------------------------------------------------------------------- backward
+
+def library_backward(q, k, v, dout, scale, m):
+    """Gradients from torch autograd through an explicit float64 softmax attention."""
+    qt, kt, vt = (torch.tensor(np.asarray(x, np.float64), requires_grad=True) for x in (q, k, v))
+    s = torch.matmul(qt, kt.transpose(-1, -2)) * scale
+    s = s.masked_fill(~m, float("-inf"))
+    p = torch.nan_to_num(torch.softmax(s, dim=-1))  # rows without a key: zeros
+    torch.matmul(p, vt).backward(torch.tensor(np.asarray(dout, np.float64)))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def pin_backward_library(orc):
+    cases = [(1, 2, 13, 17, 8, 0, 0, 0), (2, 1, 20, 20, 8, 1, 0, 0), (1, 2, 25, 12, 4, 1, 0, 0),
+             (1, 1, 30, 30, 8, 2, 5, 3), (1, 2, 19, 26, 8, 3, 4, 0), (1, 1, 22, 22, 16, 4, 0, 6)]
+    for n, (B, H, Nq, Nkv, d, mode, W, G) in enumerate(cases):
+        q = _rand((B, H, Nq, d), 4000 + 4 * n)
+        k = _rand((B, H, Nkv, d), 4001 + 4 * n)
+        v = _rand((B, H, Nkv, d), 4002 + 4 * n)
+        g = _rand((B, H, Nq, d), 4003 + 4 * n)
+        scale = float(np.float32(1 / math.sqrt(d)))
+        got = orc.attention_backward(q, k, v, g, scale, mode, W, G)
+        want = library_backward(q, k, v, g, scale, band_mask(Nq, Nkv, mode, W, G))
+        for name, a, b in zip(("dq", "dk", "dv"), got, want):
+            assert np.allclose(a, b, rtol=1e-11, atol=1e-12), (n, name, np.abs(a - b).max())
+
+
+def pin_backward_finite_difference(orc):
+    """Central differences of L = sum(O * dO) computed by the oracle's own forward pass, with
+    steps of 2^-10 that are exact in float32 around the inputs used."""
+    h = 2.0 ** -10
+    for n, (Nq, Nkv, d, mode, W, G) in enumerate([(5, 6, 3, 0, 0, 0), (6, 6, 3, 1, 0, 0),
+                                                 (7, 7, 2, 3, 1, 0), (6, 6, 2, 4, 0, 2),
+                                                 (7, 7, 2, 2, 2, 1)]):
+        rng = np.random.default_rng(4100 + n)
+        q, k, v, g = (np.round(rng.standard_normal(sh) * 64) / 64
+                      for sh in ((1, 1, Nq, d), (1, 1, Nkv, d), (1, 1, Nkv, d), (1, 1, Nq, d)))
+        q, k, v, g = (x.astype(np.float32) for x in (q, k, v, g))
+        dq, dk, dv = orc.attention_backward(q, k, v, g, 0.5, mode, W, G)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attention(qq, kk, vv, 0.5, mode, W, G)
+            return float((o * g.astype(np.float64)).sum())
+
+        for which, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros(x.shape)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += np.float32(h)
+                xm[idx] -= np.float32(h)
+                if which == "q":
+                    num[idx] = (loss(xp, k, v) - loss(xm, k, v)) / (2 * h)
+                elif which == "k":
+                    num[idx] = (loss(q, xp, v) - loss(q, xm, v)) / (2 * h)
+                else:
+                    num[idx] = (loss(q, k, xp) - loss(q, k, xm)) / (2 * h)
+            assert np.allclose(grad, num, rtol=1e-5, atol=2e-6), (n, which,
+                                                                  np.abs(grad - num).max())
+
+
+def pin_backward_invariants(orc):
+    """Each row's softmax Jacobian annihilates constants: sum_j dS_ij = 0, so dK summed over
+    keys is zero; and P rows sum to one, so dV summed over keys is dO summed over the rows
+    that see a key. dO = 0 gives zero gradients; rows without a key give dQ = 0."""
+    for n, (Nq, Nkv, mode, W, G) in enumerate([(40, 40, 0, 0, 0), (40, 40, 1, 0, 0),
+                                               (30, 50, 2, 7, 3), (50, 30, 3, 4, 0),
+                                               (36, 36, 4, 0, 9)]):
+        q = _rand((2, 2, Nq, 8), 4200 + n)
+        k = _rand((2, 2, Nkv, 8), 4210 + n)
+        v = _rand((2, 2, Nkv, 8), 4220 + n)
+        g = _rand((2, 2, Nq, 8), 4230 + n)
+        dq, dk, dv = orc.attention_backward(q, k, v, g, 0.4, mode, W, G)
+        assert np.abs(dk.sum(axis=2)).max() < 1e-12, n
+        seen = np.array([visible_count(i + Nkv - Nq, Nkv, mode, W, G) > 0 for i in range(Nq)])
+        want = g.astype(np.float64)[:, :, seen].sum(axis=2)
+        assert np.allclose(dv.sum(axis=2), want, rtol=1e-12, atol=1e-12), n
+        assert np.all(dq[:, :, ~seen] == 0), n
+        z = orc.attention_backward(q, k, v, np.zeros_like(g), 0.4, mode, W, G)
+        assert all(np.all(x == 0) for x in z), n
+
+
 ALL_PINS = [pin_library, pin_mpmath, pin_q_zero, pin_causal_row0, pin_onehot_edges,
             pin_rows_sum_to_one, pin_shift, pin_permutation, pin_split_merge,
             pin_mask_reductions, pin_empty_rows, pin_decode, pin_library_more_masks,
             pin_mpmath_more_masks, pin_q_zero_more_masks, pin_onehot_more_edges,
-            pin_more_mask_reductions]
+            pin_more_mask_reductions, pin_backward_library, pin_backward_finite_difference,
+            pin_backward_invariants]
