@@ -115,6 +115,40 @@ int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o
                             const uint8_t *layout, int block, int dtype, void *stream);
 
 /*
+ * fa_backward -- gradients dQ, dK, dV of fa_forward for the loss gradient dO.
+ *
+ * The pages keep the N x N scores out of memory and recompute them in the backward pass,
+ * which they call cheap ("ops-transformer" article on gitcode.csdn.net, section 二.1: the
+ * conventional scores would have to be read again in back-propagation; "ascend-transformer-
+ * boost" article, 场景一: the checkpoint boundary sits on the FlashAttention output because
+ * recomputing it costs little). Here P = exp(scale Q K^T - LSE) is rebuilt tile by tile from
+ * the forward's LSE, and with D_i = sum_c dO_ic O_ic
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK = scale dS^T Q,  dQ = scale dS K.
+ *
+ *  q, k, v        as fa_forward (the same tensors the forward saw).
+ *  o, lse         the forward's outputs for q, k, v with the same scale and mask.
+ *  dout           [B, H, Nq, d] dtype: gradient of the loss with respect to o.
+ *  dq             [B, H, Nq, d] dtype, written.
+ *  dk, dv         [B, H, Nkv, d] dtype, written (zero for a key no query sees).
+ *  B .. n_global  as fa_forward. A row with lse = -inf (no visible key) contributes nothing.
+ *  dtype          FA_F16 or FA_BF16 only. Products take fp16/bf16 operands (P and dS are
+ *                 rounded to dtype) with float32 accumulation; the outputs are rounded
+ *                 once at the end.
+ *  workspace      device buffer of at least fa_backward_workspace_bytes(B, H, Nq) bytes
+ *                 (per-row D and log2-scaled LSE); contents need no initialisation; 16-byte
+ *                 aligned.
+ *  Supported: d in {64, 128}; masks FA_MASK_NONE .. FA_MASK_PREFIX_LM; sizes as fa_forward.
+ *  Three kernels run on `stream` (row statistics, then dK/dV, then dQ); no atomics, so the
+ *  results are bitwise reproducible. All tensor pointers need 16-byte alignment.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int Nq);
+
+int fa_backward(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                const void *dout, void *dq, void *dk, void *dv, int B, int H, int Nq, int Nkv,
+                int d, float scale, int mask_mode, int window, int n_global, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Paged single-token decode ("ascend-transformer-boost" article, 场景二: KV cache split
  * into fixed pages of 256 tokens, a new page per overflow, no reallocation; the attention
  * reads history K/V through the page layout). Each sequence has one query token at the

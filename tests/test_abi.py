@@ -114,3 +114,36 @@ def test_decode_workspace_bytes():
     # each split keeps 128 partial outputs and one log-sum-exp (float32)
     assert lib.fa_decode_paged_workspace_bytes(8, 32, 128, 32, 256) == 8 * 32 * 128 * 129 * 4
     assert lib.fa_decode_paged_workspace_bytes(0, 32, 128, 32, 256) == 0
+
+
+def bwd(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=1, Nq=8, Nkv=8, d=64,
+        scale=0.125, mask=0, W=0, G=0, dtype=1, ws=P, wsb=None):
+    lib = fa.load_library()
+    if wsb is None:
+        wsb = lib.fa_backward_workspace_bytes(B, H, Nq)
+    return lib.fa_backward(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nkv, d, scale, mask, W, G,
+                           dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=N), fa.FA_ERR_NULL), (dict(o=N), fa.FA_ERR_NULL), (dict(lse=N), fa.FA_ERR_NULL),
+    (dict(do=N), fa.FA_ERR_NULL), (dict(dq=N), fa.FA_ERR_NULL), (dict(dk=N), fa.FA_ERR_NULL),
+    (dict(dv=N), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(Nkv=0), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED), (dict(mask=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=2, W=0), fa.FA_ERR_SHAPE), (dict(mask=3, W=-2), fa.FA_ERR_SHAPE),
+    (dict(mask=4, G=-1), fa.FA_ERR_SHAPE), (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+    (dict(ws=N), fa.FA_ERR_WORKSPACE), (dict(wsb=8 * 4), fa.FA_ERR_WORKSPACE),
+    (dict(dk=ctypes.c_void_p(0x1002)), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 16, H=1 << 16, wsb=1 << 62), fa.FA_ERR_SHAPE),
+])
+def test_backward_rejects_before_launch(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_backward_workspace_bytes():
+    lib = fa.load_library()
+    # one float D_i and one float log2-scaled LSE per query row
+    assert lib.fa_backward_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 2 * 4
+    assert lib.fa_backward_workspace_bytes(1, 1, 0) == 0

@@ -1,0 +1,149 @@
+"""Parity of the backward pass (fa_backward through the C ABI) with the fp64 oracle's
+gradients, on the GPU.
+
+The HIP backward receives O and LSE from the HIP forward (the chain a caller runs); the
+oracle recomputes everything from q, k, v and dO in fp64. Small shapes compare every element
+over several tiles and ragged tails for every mask; the full-size dense and causal workloads
+run in the benchmark's launch configuration and compare whole heads (heads are independent,
+so one head's slice is an exact sub-problem for the oracle).
+
+Tolerance (gradients are sums of many products whose operands P and dS are rounded to the
+16-bit type, u = 2^-8 for bf16 and 2^-11 for fp16, and D_i uses the forward's rounded O):
+  * max |g_gpu - g_ref| <= 8u * max |g_ref| + F over each gradient tensor, and
+    ||g_gpu - g_ref||_2 <= 4u * ||g_ref||_2 (three roundings of relative size <= u/2 each);
+  * F is the float32 accumulation floor of dS = P (dP - D): both dP_ij and D_i are d-term
+    dot products of size <= max|dO| max|V| (O is a convex combination of V rows), so with
+    gamma_d = d 2^-24 (Higham's bound) and a 16x margin for the order of the sums,
+    F = |scale| * 2 d 2^-20 * max|dO| max|V| max(max|Q|, max|K|) for dQ and dK, 0 for dV.
+    It matters only where dQ and dK vanish analytically (every row sees one key, so
+    dP = D); there the rel-L2 gate is skipped;
+  * structural zeros (rows without a visible key in dQ, keys no row sees in dK and dV) are
+    exactly zero.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_forward_amd as fa
+import workloads
+from gpu_util import f64, to_dev
+from pins import band_mask
+
+pytestmark = pytest.mark.gpu
+
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def run_bwd(q, k, v, do, scale, mask=0, W=0, G=0):
+    qd, kd, vd, gd = to_dev(q, k, v, do)
+    o, lse = fa.fa_forward(qd, kd, vd, scale, mask, W, G)
+    dq, dk, dv = fa.fa_backward(qd, kd, vd, o, lse, gd, scale, mask, W, G)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check_grads(got, ref, dtype, label, inputs, scale, vis):
+    """inputs = (q, k, v, do) as given to both sides; vis = bool [Nq, Nkv] visibility."""
+    u = U[dtype]
+    q, k, v, do = (float(t.float().abs().max()) for t in inputs)
+    d = inputs[0].shape[-1]
+    fl = abs(scale) * 2 * d * 2.0 ** -20 * do * v * max(q, k)
+    zero_rows = ~vis.any(dim=1).numpy()  # [Nq]
+    zero_keys = ~vis.any(dim=0).numpy()  # [Nkv]
+    out = {}
+    for name, g, r, floor in zip(("dq", "dk", "dv"), got, ref, (fl, fl, 0.0)):
+        g = f64(g)
+        r = np.asarray(r, np.float64).reshape(g.shape)
+        assert not np.isnan(g).any(), f"{label}: NaN in {name}"
+        diff = np.abs(g - r)
+        rmax = float(np.abs(r).max()) if r.size else 0.0
+        mabs = float(diff.max()) if diff.size else 0.0
+        rl2 = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+        out[name] = (mabs, rmax, rl2)
+        assert mabs <= 8 * u * rmax + floor, f"{label}: {name} max-abs {mabs} ref max {rmax}"
+        if rmax > 64 * floor:
+            assert rl2 <= 4 * u, f"{label}: {name} rel-L2 {rl2}"
+        structural = zero_rows if name == "dq" else zero_keys
+        assert np.all(g[:, :, structural] == 0.0), f"{label}: {name} nonzero at a structural 0"
+    return out
+
+
+MASKS = [(0, 0, 0), (1, 0, 0), (2, 40, 5), (2, 1, 0), (2, 100, 70), (2, 65, 63), (3, 0, 0),
+         (3, 33, 0), (3, 200, 0), (4, 0, 0), (4, 0, 63), (4, 0, 130), (4, 0, 1000)]
+SHAPES = [(1, 1, 1, 1), (1, 2, 17, 17), (2, 3, 100, 100), (1, 2, 129, 129), (1, 1, 300, 300),
+          (1, 2, 64, 200), (1, 2, 200, 64), (1, 1, 1, 333), (1, 2, 257, 513)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", MASKS, ids=lambda m: f"m{m[0]}w{m[1]}g{m[2]}")
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_small(dtype, d, mask, shape):
+    B, H, Nq, Nkv = shape
+    seed = zlib.crc32(repr(("bwd", dtype, d, mask, shape)).encode()) % 100000
+    q, k, v = workloads.gen_prefill(B, H, Nq, Nkv, d, dtype, seed)
+    do = workloads.gen_dout((B, H, Nq, d), dtype, seed + 1)
+    scale = workloads.default_scale(d)
+    got = run_bwd(q, k, v, do, scale, *mask)
+    ref = oracle.attention_backward(q, k, v, do, scale, *mask)
+    check_grads(got, ref, dtype, f"{dtype} d{d} mask{mask} {shape}", (q, k, v, do), scale,
+                band_mask(Nq, Nkv, *mask))
+
+
+def test_backward_negative_scale_and_large_inputs():
+    """A negative scale flips which keys dominate; inputs x8 make P close to one-hot."""
+    q, k, v = workloads.gen_prefill(1, 2, 200, 300, 128, "bf16", 91, input_scale=8.0)
+    do = workloads.gen_dout((1, 2, 200, 128), "bf16", 92)
+    for scale in (-workloads.default_scale(128), workloads.default_scale(128)):
+        for mask in ((0, 0, 0), (1, 0, 0), (3, 20, 0)):
+            got = run_bwd(q, k, v, do, scale, *mask)
+            ref = oracle.attention_backward(q, k, v, do, scale, *mask)
+            check_grads(got, ref, "bf16", f"scale {scale} mask {mask}", (q, k, v, do), scale,
+                        band_mask(200, 300, *mask))
+
+
+def test_backward_deterministic():
+    q, k, v = workloads.gen_prefill(2, 4, 640, 640, 128, "bf16", 93)
+    do = workloads.gen_dout((2, 4, 640, 128), "bf16", 94)
+    scale = workloads.default_scale(128)
+    a = run_bwd(q, k, v, do, scale, 1)
+    b = run_bwd(q, k, v, do, scale, 1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def full_size_heads(name, heads, override=None):
+    w, inp = workloads.gen_workload(name, **(override or {}))
+    B, H, Nq, d = inp["q"].shape
+    do = workloads.gen_dout((B, H, Nq, d), w["dtype"], w["seed"] + 500)
+    scale = workloads.default_scale(d)
+    mask = (w["mask"], w["window"], w["n_global"])
+    got = run_bwd(inp["q"], inp["k"], inp["v"], do, scale, *mask)
+    vis = band_mask(Nq, inp["k"].shape[2], *mask)
+    for b, h in heads:
+        sl = lambda t: t[b:b + 1, h:h + 1]  # noqa: E731
+        ref = oracle.attention_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(do), scale,
+                                        *mask)
+        ins = tuple(sl(t) for t in (inp["q"], inp["k"], inp["v"], do))
+        check_grads([sl(g) for g in got], ref, w["dtype"], f"{name} head ({b},{h})", ins, scale,
+                    vis)
+
+
+def test_backward_full_size_dense():
+    full_size_heads("dense_bf16", [(0, 0), (1, 17), (3, 31)])
+
+
+def test_backward_full_size_causal():
+    full_size_heads("causal_bf16", [(0, 0), (2, 13), (3, 31)])
+
+
+@pytest.mark.parametrize("name,override", [
+    ("window_bf16", dict(Nq=8192, Nkv=8192)),
+    ("band_bf16", dict(Nq=8192, Nkv=8192)),
+    ("prefix_bf16", None),
+])
+def test_backward_long_masks(name, override):
+    full_size_heads(name, [(0, 0), (0, 31)], override)

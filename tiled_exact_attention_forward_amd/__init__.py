@@ -4,6 +4,9 @@ Argument marshalling only: every step of the computation runs in the HIP kernels
 C ABI declared in include/fa.h. The functions carry the C names:
 
     fa_forward(q, k, v, ...)          tiled exact attention forward (O and LSE)
+    fa_forward_block_sparse(...)      forward with a block-sparse layout of visible tiles
+    fa_backward(q, k, v, o, lse, dout, ...)  gradients dQ, dK, dV
+    fa_backward_workspace_bytes(...)
     fa_decode_paged(q, k_pages, ...)  single-token decode against a paged K/V cache
     fa_decode_paged_workspace_bytes(...)
     fa_status_string(status)
@@ -16,7 +19,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_forward", "fa_forward_block_sparse", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+__all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_bytes",
+           "fa_decode_paged", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
            "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
            "FA_MASK_WINDOW_GLOBAL", "FA_MASK_BAND", "FA_MASK_PREFIX_LM", "EXPORTED_SYMBOLS"]
@@ -25,7 +29,8 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_H
     0, -1, -2, -3, -4, -5)
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
-EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_decode_paged",
+EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_backward",
+                    "fa_backward_workspace_bytes", "fa_decode_paged",
                     "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_last_hip_error",
                     "fa_version")
 
@@ -62,6 +67,11 @@ def load_library():
     lib.fa_forward.restype = i
     lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i, vp]
     lib.fa_forward_block_sparse.restype = i
+    lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_backward_workspace_bytes.restype = sz
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i,
+                                vp, sz, vp]
+    lib.fa_backward.restype = i
     lib.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_paged_workspace_bytes.restype = sz
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
@@ -180,6 +190,46 @@ def fa_forward_block_sparse(q, k, v, layout, block=128, scale=None, out=None, ls
     if rc != FA_OK:
         raise FaError(rc, "fa_forward_block_sparse")
     return out, lse
+
+
+def fa_backward_workspace_bytes(B, H, Nq):
+    return int(load_library().fa_backward_workspace_bytes(int(B), int(H), int(Nq)))
+
+
+def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, window=0,
+                n_global=0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of fa_forward: q [B,H,Nq,d], k/v [B,H,Nkv,d] (f16/bf16), o and lse the
+    forward's outputs for the same arguments, dout like o. Returns (dq, dk, dv)."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Nkv, d) or tuple(v.shape) != (B, H, Nkv, d):
+        raise ValueError("k and v must be [B,H,Nkv,d] matching q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be [B,H,Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_backward_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("workspace", workspace)
+    rc = load_library().fa_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dv), B, H, Nq, Nkv, d, float(scale), int(mask_mode), int(window), int(n_global),
+        _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_backward")
+    return dq, dk, dv
 
 
 def fa_decode_paged_workspace_bytes(num_seqs, H, d, max_pages_per_seq, page_size=256):

@@ -46,7 +46,23 @@ inline int decode_workspace_splits(int max_pages, int page_size)
     return (int)((tokens + kDecodeMinSplit - 1) / kDecodeMinSplit);
 }
 
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    int B, H, Nq, Nkv, d;
+    float scale;
+    int mask, window, n_global, dtype;
+    void *workspace;  // 2 * B * H * Nq floats: D = rowsum(dO o O), then log2-domain LSE
+};
+
+inline size_t backward_workspace_floats(int B, int H, int Nq)
+{
+    return 2 * (size_t)B * H * Nq;
+}
+
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace teaf

@@ -7,6 +7,8 @@ Recipe (every draw from one torch CPU generator seeded per workload):
   * prefill: Q, K, V drawn in that order as float32 standard normals of shape [B,H,N,d],
     optionally multiplied by an exact power of two in float32, then cast to the run's dtype
     (round to nearest even);
+  * backward: dO [B,H,Nq,d] from its own generator (gen_dout), float32 standard normals
+    cast to the run's dtype;
   * paged decode: Q [S,H,d], then the S sequence lengths uniform in [len_lo, len_hi], then a
     random permutation of the physical page ids, then the K and V page pools
     [num_pages, page_size, H, d]. Slots past a sequence's length in its last page and the
@@ -65,6 +67,17 @@ def gen_prefill(B, H, Nq, Nkv, d, dtype, seed, input_scale=1.0):
         v.mul_(input_scale)
     t = DTYPES[dtype]
     return q.to(t), k.to(t), v.to(t)
+
+
+def gen_dout(shape, dtype, seed, input_scale=1.0):
+    """Upstream gradient dO for the backward pass: float32 standard normals of `shape` from a
+    generator seeded `seed` (its own stream, so Q, K, V stay those of the forward),
+    optionally times an exact power of two, cast to `dtype`."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    do = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    if input_scale != 1.0:
+        do.mul_(input_scale)
+    return do.to(DTYPES[dtype])
 
 
 def gen_layout(H, Nq, Nkv, block, density, seed):
