@@ -41,6 +41,11 @@ class Oracle:
             f32p, f32p, f32p, i32p, i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_double, f64p, f64p]
         lib.oracle_decode_paged.restype = ctypes.c_int
+        lib.oracle_prefill_paged.argtypes = [
+            f32p, f32p, f32p, i32p, i32p, i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_double,
+            ctypes.c_int, ctypes.c_long, ctypes.c_long, f64p, f64p]
+        lib.oracle_prefill_paged.restype = ctypes.c_int
         lib.oracle_attention_block_sparse_rows.argtypes = [
             f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_long,
             ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_uint8), ctypes.c_long, i64p,
@@ -143,6 +148,30 @@ class Oracle:
             return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
         return o, lse
 
+    def prefill_paged(self, q, k_pages, v_pages, page_table, seq_lens, q_lens, scale,
+                      mask_mode=1, window=0, n_global=0):
+        """Chunked prefill against a paged cache, fp64: q [S,Qmax,H,d], sequence s's chunk is
+        its newest q_lens[s] tokens of seq_lens[s]. Returns (o [S,Qmax,H,d], lse [S,Qmax,H])
+        float64, NaN in rows at or past q_lens[s]."""
+        q, kp, vp = _f32(q), _f32(k_pages), _f32(v_pages)
+        pt = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
+        sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        ql = np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
+        S, Qmax, H, d = q.shape
+        num_pages, page_size = kp.shape[0], kp.shape[1]
+        assert kp.shape == (num_pages, page_size, H, d) and vp.shape == kp.shape
+        assert pt.shape[0] == S and sl.shape == (S,) and ql.shape == (S,)
+        o = np.full((S, Qmax, H, d), np.nan, dtype=np.float64)
+        lse = np.full((S, Qmax, H), np.nan, dtype=np.float64)
+        rc = self.lib.oracle_prefill_paged(
+            _p(q, ctypes.c_float), _p(kp, ctypes.c_float), _p(vp, ctypes.c_float),
+            _p(pt, ctypes.c_int32), _p(sl, ctypes.c_int32), _p(ql, ctypes.c_int32), S, Qmax, H,
+            d, page_size, pt.shape[1], num_pages, float(np.float32(scale)), int(mask_mode),
+            int(window), int(n_global), _p(o, ctypes.c_double), _p(lse, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_prefill_paged rejected its arguments")
+        return o, lse
+
     def decode_paged(self, q, k_pages, v_pages, page_table, seq_lens, scale):
         """Single-token decode against a paged cache, fp64.
 
@@ -218,3 +247,7 @@ def attention_backward(*args, **kw):
 
 def decode_paged(*args, **kw):
     return default().decode_paged(*args, **kw)
+
+
+def prefill_paged(*args, **kw):
+    return default().prefill_paged(*args, **kw)

@@ -385,3 +385,71 @@ int oracle_decode_paged(const float *q, const float *k_pages, const float *v_pag
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Paged multi-token (chunked) prefill: sequence s appends a chunk of q_lens[s] new tokens to
+ * a cache that then holds L_s = seq_lens[s] tokens (the chunk included), stored in pages as
+ * for oracle_decode_paged (the paged KV cache of the "ascend-transformer-boost" article,
+ * 场景二). The chunk's tokens are the newest ones, so query row i of sequence s sits at
+ * absolute position i + (L_s - q_lens[s]) and sees keys by `mode` exactly as in
+ * oracle_attention_rows (bottom-right alignment; mode 1 is causal). q: [S, Qmax, H, d];
+ * o: [S, Qmax, H, d]; lse: [S, Qmax, H]; rows i >= q_lens[s] are not written.
+ * Returns 0, or -1 on bad arguments (including a page id outside [0, num_pages) or a chunk
+ * longer than its sequence).
+ */
+int oracle_prefill_paged(const float *q, const float *k_pages, const float *v_pages,
+                         const int32_t *page_table, const int32_t *seq_lens,
+                         const int32_t *q_lens, int S, int Qmax, int H, int d, int page_size,
+                         int max_pages, long num_pages, double scale, int mode, long window,
+                         long n_global, double *o, double *lse)
+{
+    int failed = 0;
+    long r;
+    if (S < 1 || Qmax < 1 || H < 1 || d < 1 || page_size < 1 || max_pages < 1 ||
+        num_pages < 1 || mode < 0 || mode > 4)
+        return -1;
+    for (r = 0; r < S; ++r) {
+        long L = seq_lens[r], nq = q_lens[r], p;
+        if (L < 1 || L > (long)max_pages * page_size || nq < 0 || nq > Qmax || nq > L)
+            return -1;
+        for (p = 0; p < (L + page_size - 1) / page_size; ++p) {
+            int32_t id = page_table[r * max_pages + p];
+            if (id < 0 || id >= num_pages)
+                return -1;
+        }
+    }
+
+#pragma omp parallel
+    {
+        long Lmax = (long)max_pages * page_size;
+        double *s = (double *)malloc(sizeof(double) * (size_t)Lmax);
+        const float **kp = (const float **)malloc(sizeof(float *) * (size_t)Lmax);
+        const float **vp = (const float **)malloc(sizeof(float *) * (size_t)Lmax);
+        long t;
+        if (s == NULL || kp == NULL || vp == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (t = 0; t < (long)S * H; ++t) {
+                long sq = t / H, h = t % H, L = seq_lens[sq], nq = q_lens[sq], j, i;
+                for (j = 0; j < L; ++j) {  /* logical token j: page j / page_size, slot */
+                    long pg = j / page_size, slot = j - pg * page_size;
+                    size_t tok = (size_t)page_table[sq * max_pages + pg] * (size_t)page_size +
+                                 (size_t)slot;
+                    kp[j] = k_pages + (tok * (size_t)H + (size_t)h) * (size_t)d;
+                    vp[j] = v_pages + (tok * (size_t)H + (size_t)h) * (size_t)d;
+                }
+                for (i = 0; i < nq; ++i) {
+                    size_t row = ((size_t)sq * Qmax + (size_t)i) * H + (size_t)h;
+                    attend_row(q + row * d, kp, vp, L, d, scale, i + (L - nq), mode, window,
+                               n_global, NULL, s, o + row * d, lse + row);
+                }
+            }
+        }
+        free(s);
+        free((void *)kp);
+        free((void *)vp);
+    }
+    return failed ? -1 : 0;
+}

@@ -36,6 +36,13 @@ MUTANTS = {
                            "D += (double)gi[c] * (double)vb[c];"),
     "bwd_dq_uses_q": ("scale * ds * (double)kb[(size_t)j * d + c];",
                       "scale * ds * (double)qi[c];"),
+    "prefill_top_left": ("i + (L - nq), mode", "i, mode"),
+    "prefill_row_stride": ("((size_t)sq * Qmax + (size_t)i) * H + (size_t)h;",
+                           "((size_t)sq * Qmax + (size_t)i) * H;"),
+    "prefill_page_slot": ("slot = j - pg * page_size;", "slot = (j + 1) % page_size;"),
+    "prefill_value_head": ("vp[j] = v_pages + (tok * (size_t)H + (size_t)h)",
+                           "vp[j] = v_pages + (tok * (size_t)H + (size_t)0)"),
+    "prefill_chunk_shift": ("i + (L - nq), mode", "i + (L - nq) - 1, mode"),
 }
 
 

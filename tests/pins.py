@@ -623,9 +623,54 @@ def pin_backward_invariants(orc):
         assert all(np.all(x == 0) for x in z), n
 
 
+def pin_prefill_paged(orc):
+    """Chunked prefill against a paged cache: each sequence's newest q_lens[s] tokens attend
+    to its seq_lens[s] keys with bottom-right masks. Pinned to torch SDPA in float64 on the
+    contiguous keys (gathered before paging) with tril masks of the chunk's shape; a
+    different physical placement is bit-identical; a chunk of one token is single-token
+    decode; a whole-sequence chunk is the contiguous causal case."""
+    H, d, ps = 2, 8, 16
+    lens = [1, 16, 17, 40, 64, 33]
+    qls = [1, 5, 17, 12, 64, 0]
+    Qmax = 64
+    ks = [_rand((L, H, d), 4400 + i) for i, L in enumerate(lens)]
+    vs = [_rand((L, H, d), 4410 + i) for i, L in enumerate(lens)]
+    q = _rand((len(lens), Qmax, H, d), 4420)
+    kp, vp, pt = make_paged(ks, vs, ps, 9)
+    scale = float(np.float32(0.35))
+    for mode, W, G in [(1, 0, 0), (0, 0, 0), (2, 5, 3), (3, 4, 0), (4, 0, 7)]:
+        o, l = orc.prefill_paged(q, kp, vp, pt, np.array(lens, np.int32),
+                                 np.array(qls, np.int32), 0.35, mode, W, G)
+        for s, (L, nq) in enumerate(zip(lens, qls)):
+            assert np.all(np.isnan(o[s, nq:])) and np.all(np.isnan(l[s, nq:])), s
+            if nq == 0:
+                continue
+            qc = np.ascontiguousarray(q[s, :nq].transpose(1, 0, 2))[None]
+            kc = np.ascontiguousarray(ks[s].transpose(1, 0, 2))[None]
+            vc = np.ascontiguousarray(vs[s].transpose(1, 0, 2))[None]
+            m = band_mask(nq, L, mode, W, G)
+            ro, rl = library_attention_mask(qc, kc, vc, scale, m)
+            fin = m.any(dim=1).numpy()
+            got_o = o[s, :nq].transpose(1, 0, 2)
+            got_l = l[s, :nq].transpose(1, 0)
+            assert np.allclose(got_o[:, fin], ro[0][:, fin], rtol=1e-12, atol=1e-13), (mode, s)
+            assert np.allclose(got_l[:, fin], rl[0][:, fin], rtol=1e-12, atol=1e-13), (mode, s)
+            assert np.all(got_l[:, ~fin] == -np.inf) and np.all(got_o[:, ~fin] == 0), (mode, s)
+        kp2, vp2, pt2 = make_paged(ks, vs, ps, 10, spare=4)
+        o2, l2 = orc.prefill_paged(q, kp2, vp2, pt2, np.array(lens, np.int32),
+                                   np.array(qls, np.int32), 0.35, mode, W, G)
+        assert np.array_equal(o, o2, equal_nan=True) and np.array_equal(l, l2, equal_nan=True)
+    # one-token chunks are decode (the newest token sees every key)
+    ones = np.ones(len(lens), np.int32)
+    o, l = orc.prefill_paged(q, kp, vp, pt, np.array(lens, np.int32), ones, 0.35, 1)
+    do, dl = orc.decode_paged(np.ascontiguousarray(q[:, 0]), kp, vp, pt,
+                              np.array(lens, np.int32), 0.35)
+    assert np.array_equal(o[:, 0], do) and np.array_equal(l[:, 0], dl)
+
+
 ALL_PINS = [pin_library, pin_mpmath, pin_q_zero, pin_causal_row0, pin_onehot_edges,
             pin_rows_sum_to_one, pin_shift, pin_permutation, pin_split_merge,
             pin_mask_reductions, pin_empty_rows, pin_decode, pin_library_more_masks,
             pin_mpmath_more_masks, pin_q_zero_more_masks, pin_onehot_more_edges,
             pin_more_mask_reductions, pin_backward_library, pin_backward_finite_difference,
-            pin_backward_invariants]
+            pin_backward_invariants, pin_prefill_paged]
