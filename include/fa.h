@@ -179,6 +179,37 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     int num_pages, float scale, int dtype, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/*
+ * fa_prefill_paged -- multi-token (chunked) prefill against the paged KV cache of
+ * fa_decode_paged. The pages' inference loop (ascend-transformer-boost article, 场景二) feeds
+ * tokens into a layer whose KV cache is paged; a chunk of several new tokens per sequence is
+ * the multi-token form of that step. The chunk's K/V rows must already be in the cache: the
+ * chunk is the newest q_lens[s] of the seq_lens[s] cached tokens, so query row i of sequence
+ * s sits at absolute position i + seq_lens[s] - q_lens[s] and the masks of fa_mask apply
+ * with that bottom-right alignment (FA_MASK_CAUSAL: the chunk sees the whole history and
+ * itself causally).
+ *
+ *  q           [S, Qmax, H, d]  dtype: row i < q_lens[s] of sequence s is a query token
+ *  k_pages,
+ *  v_pages     [num_pages, page_size, H, d]  dtype (as fa_decode_paged)
+ *  page_table  [S, max_pages_per_seq] int32 (as fa_decode_paged)
+ *  seq_lens    [S] int32, each in [1, max_pages_per_seq * page_size]
+ *  q_lens      [S] int32, each in [0, min(Qmax, seq_lens[s])]
+ *  o           [S, Qmax, H, d]  dtype, written for rows i < q_lens[s] (others untouched)
+ *  lse         [S, Qmax, H] float32, written for the same rows (-inf: no visible key)
+ *  scale, mask_mode, window, n_global, dtype: as fa_forward (masks NONE .. PREFIX_LM).
+ *  Supported: page_size == 256; d in {64, 128}; dtype FA_F16 or FA_BF16; H <= 65535;
+ *  q, k_pages, v_pages and o 16-byte aligned. One kernel runs on `stream`; it reads no
+ *  page slot at or past seq_lens[s] and no table entry past ceil(seq_lens[s]/page_size).
+ *  Page ids outside [0, num_pages) are clamped into the pool (wrong values, never a read
+ *  outside it); the lengths are clamped to the ranges above.
+ */
+int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                     const int32_t *page_table, const int32_t *seq_lens, const int32_t *q_lens,
+                     void *o, float *lse, int page_size, int num_seqs, int Qmax, int H, int d,
+                     int max_pages_per_seq, int num_pages, float scale, int mask_mode,
+                     int window, int n_global, int dtype, void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

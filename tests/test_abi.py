@@ -147,3 +147,26 @@ def test_backward_workspace_bytes():
     # one float D_i and one float log2-scaled LSE per query row
     assert lib.fa_backward_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 2 * 4
     assert lib.fa_backward_workspace_bytes(1, 1, 0) == 0
+
+
+def pre(q=P, kp=P, vp=P, pt=P, sl=P, ql=P, o=P, lse=P, page=256, S=4, Qm=64, H=8, d=128,
+        maxp=8, npages=40, scale=0.088, mask=1, W=0, G=0, dtype=2):
+    return fa.load_library().fa_prefill_paged(q, kp, vp, pt, sl, ql, o, lse, page, S, Qm, H, d,
+                                              maxp, npages, scale, mask, W, G, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=N), fa.FA_ERR_NULL), (dict(kp=N), fa.FA_ERR_NULL), (dict(pt=N), fa.FA_ERR_NULL),
+    (dict(sl=N), fa.FA_ERR_NULL), (dict(ql=N), fa.FA_ERR_NULL), (dict(o=N), fa.FA_ERR_NULL),
+    (dict(lse=N), fa.FA_ERR_NULL),
+    (dict(S=0), fa.FA_ERR_SHAPE), (dict(Qm=0), fa.FA_ERR_SHAPE), (dict(H=0), fa.FA_ERR_SHAPE),
+    (dict(maxp=0), fa.FA_ERR_SHAPE), (dict(npages=0), fa.FA_ERR_SHAPE),
+    (dict(page=128), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(mask=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=2, W=0), fa.FA_ERR_SHAPE), (dict(mask=3, W=-1), fa.FA_ERR_SHAPE),
+    (dict(mask=4, G=-1), fa.FA_ERR_SHAPE), (dict(H=70000), fa.FA_ERR_SHAPE),
+    (dict(maxp=1 << 23), fa.FA_ERR_SHAPE), (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+    (dict(o=ctypes.c_void_p(0x1008)), fa.FA_ERR_UNSUPPORTED),
+])
+def test_prefill_paged_rejects_before_launch(kw, status):
+    assert pre(**kw) == status

@@ -1,0 +1,110 @@
+"""Parity of chunked prefill against a paged cache (fa_prefill_paged, through the C ABI) with
+the fp64 oracle, on the GPU.
+
+Each sequence's chunk (its newest q_lens[s] tokens) attends to its seq_lens[s] cached keys
+with bottom-right masks. Small cases compare every row of every chunk across ragged page
+tails, empty chunks, one-token chunks and whole-sequence chunks; the full-size chunked
+prefill workload compares whole sequences of sampled heads (heads and sequences are
+independent, so a slice is an exact sub-problem for the oracle). Unused page slots and spare
+pages hold NaN, and Q rows past each chunk hold NaN, so reading any of them shows. Rows past
+a chunk must be left as they were. Tolerances are those of the forward (gpu_util).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_forward_amd as fa
+import workloads
+from gpu_util import check, f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SENT = 7.0  # sentinel in rows no chunk covers
+
+
+def run_prefill(inp, scale, mask=(1, 0, 0)):
+    q, kp, vp, pt, sl, ql = to_dev(inp["q"], inp["k_pages"], inp["v_pages"],
+                                   inp["page_table"], inp["seq_lens"], inp["q_lens"])
+    S, Qmax, H, d = q.shape
+    out = torch.full_like(q, SENT)
+    lse = torch.full((S, Qmax, H), SENT, dtype=torch.float32, device=q.device)
+    fa.fa_prefill_paged(q, kp, vp, pt, sl, ql, scale, *mask, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def compare(out, lse, ro, rl, q_lens, dtype, label):
+    og, lg = out.cpu(), lse.cpu()
+    for s, nq in enumerate(int(x) for x in q_lens):
+        assert torch.all(og[s, nq:] == SENT) and torch.all(lg[s, nq:] == SENT), \
+            f"{label}: rows past chunk {s} were written"
+        if nq:
+            check(og[s, :nq], lg[s, :nq], ro[s, :nq], rl[s, :nq], dtype, f"{label} seq {s}")
+
+
+MASKS = [(1, 0, 0), (0, 0, 0), (2, 100, 5), (2, 300, 64), (3, 50, 0), (4, 0, 70)]
+CASES = [  # (seq_lens, q_lens, Qmax)
+    ([1, 16, 255, 256, 257, 700], [1, 16, 100, 256, 129, 300], 300),
+    ([513, 1000, 77, 300], [0, 1, 77, 33], 128),
+    ([2048, 1500], [600, 1500], 1500),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", MASKS, ids=lambda m: f"m{m[0]}w{m[1]}g{m[2]}")
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_prefill_paged_small(dtype, d, mask, case):
+    lens, qls, Qmax = CASES[case]
+    seed = zlib.crc32(repr(("pre", dtype, d, mask, case)).encode()) % 100000
+    H = 4 if d == 64 else 2
+    inp = workloads.gen_prefill_paged(len(lens), Qmax, H, d, dtype, seed, max_len=max(lens),
+                                      lens=lens, qlens=qls)
+    scale = workloads.default_scale(d)
+    out, lse = run_prefill(inp, scale, mask)
+    ro, rl = oracle.prefill_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
+                                  inp["seq_lens"], inp["q_lens"], scale, *mask)
+    compare(out, lse, ro, rl, inp["q_lens"], dtype, f"{dtype} d{d} mask{mask} case{case}")
+
+
+@pytest.mark.parametrize("mask", [(1, 0, 0), (2, 100, 5), (4, 0, 70)])
+def test_prefill_paged_matches_contiguous_forward(mask):
+    """The paged kernel is the forward kernel with paged addressing: on the same values a
+    chunk gives bitwise the results of fa_forward on the contiguous keys."""
+    lens, qls = [700, 257, 1024], [300, 257, 1]
+    inp = workloads.gen_prefill_paged(3, 300, 4, 128, "bf16", 4321, max_len=1024, lens=lens,
+                                      qlens=qls)
+    scale = workloads.default_scale(128)
+    out, lse = run_prefill(inp, scale, mask)
+    kp, vp, pt = inp["k_pages"], inp["v_pages"], inp["page_table"]
+    for s, (L, nq) in enumerate(zip(lens, qls)):
+        idx = torch.arange(L)
+        rows = pt[s, idx // 256].long() * 256 + idx % 256
+        k = kp.reshape(-1, 4, 128)[rows].permute(1, 0, 2)[None].contiguous()
+        v = vp.reshape(-1, 4, 128)[rows].permute(1, 0, 2)[None].contiguous()
+        q = inp["q"][s, :nq].permute(1, 0, 2)[None].contiguous()
+        qd, kd, vd = to_dev(q, k, v)
+        o2, l2 = fa.fa_forward(qd, kd, vd, scale, *mask)
+        torch.cuda.synchronize()
+        assert torch.equal(out[s, :nq], o2[0].permute(1, 0, 2)), s
+        assert torch.equal(lse[s, :nq], l2[0].permute(1, 0)), s
+
+
+def test_prefill_paged_full_size():
+    w, inp = workloads.gen_workload("prefill_paged_bf16")
+    scale = workloads.default_scale(w["d"])
+    mask = (w["mask"], w["window"], w["n_global"])
+    out, lse = run_prefill(inp, scale, mask)
+    assert not torch.isnan(out[out != SENT]).any()
+    for seqs, h in (([0, 5], 0), ([3], 31), ([7], 17)):
+        sel = torch.tensor(seqs)
+        q = inp["q"][sel][:, :, h:h + 1].contiguous()
+        kp = inp["k_pages"][:, :, h:h + 1].contiguous()
+        vp = inp["v_pages"][:, :, h:h + 1].contiguous()
+        ro, rl = oracle.prefill_paged(q, kp, vp, inp["page_table"][sel], inp["seq_lens"][sel],
+                                      inp["q_lens"][sel], scale, *mask)
+        compare(out[sel][:, :, h:h + 1], lse[sel][:, :, h:h + 1], ro, rl, inp["q_lens"][sel],
+                w["dtype"], f"full size seqs {seqs} head {h}")

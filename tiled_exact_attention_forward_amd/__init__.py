@@ -8,6 +8,7 @@ C ABI declared in include/fa.h. The functions carry the C names:
     fa_backward(q, k, v, o, lse, dout, ...)  gradients dQ, dK, dV
     fa_backward_workspace_bytes(...)
     fa_decode_paged(q, k_pages, ...)  single-token decode against a paged K/V cache
+    fa_prefill_paged(q, k_pages, ...) multi-token chunk per sequence against a paged cache
     fa_decode_paged_workspace_bytes(...)
     fa_status_string(status)
 
@@ -20,7 +21,7 @@ import math
 import os
 
 __all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_bytes",
-           "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+           "fa_decode_paged", "fa_prefill_paged", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
            "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
            "FA_MASK_WINDOW_GLOBAL", "FA_MASK_BAND", "FA_MASK_PREFIX_LM", "EXPORTED_SYMBOLS"]
@@ -30,7 +31,7 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_H
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_backward",
-                    "fa_backward_workspace_bytes", "fa_decode_paged",
+                    "fa_backward_workspace_bytes", "fa_decode_paged", "fa_prefill_paged",
                     "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_last_hip_error",
                     "fa_version")
 
@@ -77,6 +78,9 @@ def load_library():
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
                                     vp]
     lib.fa_decode_paged.restype = i
+    lib.fa_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i,
+                                     i, i, i, vp]
+    lib.fa_prefill_paged.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.restype = i
@@ -266,4 +270,37 @@ def fa_decode_paged(q, k_pages, v_pages, page_table, seq_lens, scale=None, out=N
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != FA_OK:
         raise FaError(rc, "fa_decode_paged")
+    return out, lse
+
+
+def fa_prefill_paged(q, k_pages, v_pages, page_table, seq_lens, q_lens, scale=None,
+                     mask_mode=FA_MASK_CAUSAL, window=0, n_global=0, out=None, lse=None,
+                     stream=None):
+    """Chunked prefill: q [S,Qmax,H,d] holds each sequence's newest q_lens[s] tokens of its
+    seq_lens[s] cached ones; pages [P,256,H,d]; page_table [S,max_pages] int32; seq_lens and
+    q_lens [S] int32 (all on the GPU). Returns (out [S,Qmax,H,d], lse [S,Qmax,H] float32);
+    rows at or past q_lens[s] are left as they were in `out` and `lse`."""
+    torch = _torch()
+    S, Qmax, H, d = q.shape
+    P, page_size = k_pages.shape[0], k_pages.shape[1]
+    if tuple(k_pages.shape) != (P, page_size, H, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages and v_pages must be [num_pages, page_size, H, d]")
+    max_pages = page_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.full((S, Qmax, H), float("-inf"), dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("out", out)):
+        _check_dev(name, t, q.dtype)
+    for name, t in (("page_table", page_table), ("seq_lens", seq_lens), ("q_lens", q_lens)):
+        _check_dev(name, t, torch.int32)
+    _check_dev("lse", lse, torch.float32)
+    rc = load_library().fa_prefill_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table), _ptr(seq_lens), _ptr(q_lens),
+        _ptr(out), _ptr(lse), page_size, S, Qmax, H, d, max_pages, P, float(scale),
+        int(mask_mode), int(window), int(n_global), _dtype_code(q), _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_prefill_paged")
     return out, lse

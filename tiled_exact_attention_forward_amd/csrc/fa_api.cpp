@@ -135,6 +135,38 @@ int fa_backward(const void *q, const void *k, const void *v, const void *o, cons
     return hip_status(teaf::launch_backward(a, (hipStream_t)stream));
 }
 
+int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                     const int32_t *page_table, const int32_t *seq_lens, const int32_t *q_lens,
+                     void *o, float *lse, int page_size, int num_seqs, int Qmax, int H, int d,
+                     int max_pages_per_seq, int num_pages, float scale, int mask_mode,
+                     int window, int n_global, int dtype, void *stream)
+{
+    if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !q_lens || !o || !lse)
+        return FA_ERR_NULL;
+    if (num_seqs < 1 || Qmax < 1 || H < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
+        page_size < 1)
+        return FA_ERR_SHAPE;
+    if (page_size != 256 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (mask_mode < FA_MASK_NONE || mask_mode > FA_MASK_PREFIX_LM) return FA_ERR_UNSUPPORTED;
+    if (mask_mode == FA_MASK_WINDOW_GLOBAL && (window < 1 || n_global < 0)) return FA_ERR_SHAPE;
+    if (mask_mode == FA_MASK_BAND && window < 0) return FA_ERR_SHAPE;
+    if (mask_mode == FA_MASK_PREFIX_LM && n_global < 0) return FA_ERR_SHAPE;
+    if (H > 65535 || (long long)max_pages_per_seq * page_size > (1ll << 30)) return FA_ERR_SHAPE;
+    if ((long long)num_seqs * H * ((Qmax + 127) / 128) > (long long)INT_MAX) return FA_ERR_SHAPE;
+    if (!(scale == scale)) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+        return FA_ERR_UNSUPPORTED;
+    const bool uses_w = mask_mode == FA_MASK_WINDOW_GLOBAL || mask_mode == FA_MASK_BAND;
+    const bool uses_g = mask_mode == FA_MASK_WINDOW_GLOBAL || mask_mode == FA_MASK_PREFIX_LM;
+    const int wc = uses_w ? std::min(window, 1 << 30) : 0;
+    const int gc = uses_g ? std::min(n_global, max_pages_per_seq * page_size) : 0;
+    teaf::PrefillArgs a{q, k_pages, v_pages, page_table, seq_lens, q_lens, o, lse, num_seqs,
+                        Qmax, H, d, max_pages_per_seq, num_pages, scale, mask_mode, wc, gc,
+                        dtype};
+    return hip_status(teaf::launch_prefill_paged(a, (hipStream_t)stream));
+}
+
 size_t fa_decode_paged_workspace_bytes(int num_seqs, int H, int d, int max_pages_per_seq,
                                        int page_size)
 {

@@ -332,18 +332,20 @@ __device__ __forceinline__ void ring_barrier()
 // Direct HBM-to-LDS loads of this wave's share of the K and V tile that starts at key kv0.
 // Load i of a tile (i < KL: K, else V) fills 1 KB, i.e. ROWS_PER_LOAD rows, of its LDS
 // tile; wave w issues loads w, w + NW, ... off[u]: this lane's byte offset in the tile.
+// Issue the loads of one K tile and one V tile (32 rows each) from HBM straight into LDS.
+// kt and vt point at the tiles' first rows; rest is the number of valid bytes from there
+// (the buffer range check returns zeros past it, so tail rows arrive as zeros); off[] holds
+// each lane's byte offsets, which carry the row stride and the LDS swizzle.
 template <typename C>
-__device__ __forceinline__ void issue_kv(const char *kbh, const char *vbh,
-                                         const unsigned (&off)[C::LPW], int kv0, int Nkv,
-                                         char *kdst, char *vdst, int wave)
+__device__ __forceinline__ void issue_kv_at(const char *kt, const char *vt,
+                                            const unsigned (&off)[C::LPW], int rest, char *kdst,
+                                            char *vdst, int wave)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    kv0 = __builtin_amdgcn_readfirstlane(kv0);
-    const int rest = (int)((unsigned)(Nkv - kv0) * C::ROWB);
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(kbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(vbh + (size_t)kv0 * C::ROWB), (short)0, rest, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kt), (short)0, rest, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vt), (short)0, rest, 0x00020000);
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u) {
         const int i = wave + C::NW * u;
@@ -355,6 +357,47 @@ __device__ __forceinline__ void issue_kv(const char *kbh, const char *vbh,
                                                      16, off[u], 0, 0, 0);
     }
 #endif
+}
+
+// Tiles of contiguous [N, D] rows (K and V of one batch-head): tile starting at key kv0.
+template <typename C>
+__device__ __forceinline__ void issue_kv(const char *kbh, const char *vbh,
+                                         const unsigned (&off)[C::LPW], int kv0, int Nkv,
+                                         char *kdst, char *vdst, int wave)
+{
+    kv0 = __builtin_amdgcn_readfirstlane(kv0);
+    const int rest = (int)((unsigned)(Nkv - kv0) * C::ROWB);
+    issue_kv_at<C>(kbh + (size_t)kv0 * C::ROWB, vbh + (size_t)kv0 * C::ROWB, off, rest, kdst,
+                   vdst, wave);
+}
+
+// A paged K/V cache: pages of kPageTokens tokens laid out [num_pages, kPageTokens, H, D];
+// logical token j of sequence s is slot j % kPageTokens of page table[s * max_pages +
+// j / kPageTokens]. Query chunks are [S, Qmax, H, D] (row i of sequence s at (s Qmax + i) H + h),
+// LSE [S, Qmax, H].
+constexpr int kPageTokens = 256;
+struct PagedKV {
+    const int32_t *table, *seq_lens, *q_lens;
+    int max_pages, num_pages, Qmax, H;
+};
+
+// The K and V tiles of keys [kv0, kv0 + 32) of head h of a paged sequence (a tile never
+// crosses a page). Page ids are clamped into the pool, so a corrupt table cannot send a
+// load outside it.
+template <typename C>
+__device__ __forceinline__ void issue_kv_paged(const char *kpool, const char *vpool,
+                                               const int32_t *seq_table, int num_pages, int H,
+                                               int h, const unsigned (&off)[C::LPW], int kv0,
+                                               int Nkv, char *kdst, char *vdst, int wave)
+{
+    kv0 = __builtin_amdgcn_readfirstlane(kv0);
+    int pid = __builtin_amdgcn_readfirstlane(seq_table[kv0 / kPageTokens]);
+    pid = min(max(pid, 0), num_pages - 1);
+    const size_t tok = (size_t)pid * kPageTokens + (size_t)(kv0 % kPageTokens);
+    const size_t at = (tok * (size_t)H + (size_t)h) * C::ROWB;
+    const int rows = min(Nkv - kv0, C::BN);
+    const int rest = rows * H * C::ROWB;
+    issue_kv_at<C>(kpool + at, vpool + at, off, rest, kdst, vdst, wave);
 }
 
 // Element mask of a 32-key score tile starting at kv0, for query row ip (lane half g):

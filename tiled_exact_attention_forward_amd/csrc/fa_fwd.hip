@@ -133,11 +133,15 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
     }
 }
 
-template <typename T, int D, int MASK, int NS, int NW>
+// PAGED: the query rows are a chunk of the newest tokens of sequence bh / H (head bh % H) and
+// K/V come from the page pool described by pg; Nq and Nkv are then that sequence's chunk
+// and cache lengths, read from pg (the arguments are ignored).
+template <typename T, int D, int MASK, int NS, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
-    int Nkv, float c, int W, int G, int nqt, const uint8_t *__restrict__ layout, int H)
+    int Nkv, float c, int W, int G, int nqt, const uint8_t *__restrict__ layout, int H,
+    const PagedKV pg)
 {
     using C = CfgSP<D, NS, NW>;
     using Op = Ops16<T>;
@@ -150,8 +154,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = L / nqt;
     const int q0 = (nqt - 1 - L % nqt) * BM;  // most-loaded query tiles first
+    // Row strides (elements) of Q and O, and where this workgroup's rows and LSE entries
+    // start. Lengths in a paged cache are clamped to what the table and the chunk can hold.
+    int rs = D;
+    size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D, lbase = (size_t)bh * Nq;
+    int lstride = 1, seq = 0, head = 0;
+    if constexpr (PAGED) {
+        seq = bh / pg.H;
+        head = bh % pg.H;
+        Nkv = min(__builtin_amdgcn_readfirstlane(pg.seq_lens[seq]), pg.max_pages * kPageTokens);
+        Nq = min(min(__builtin_amdgcn_readfirstlane(pg.q_lens[seq]), pg.Qmax), Nkv);
+        if (q0 >= Nq) return;  // the whole workgroup: this chunk is shorter
+        rs = pg.H * D;
+        qbase = ((size_t)seq * pg.Qmax * pg.H + head) * D;
+        kvbase = 0;
+        lbase = (size_t)seq * pg.Qmax * pg.H + head;
+        lstride = pg.H;
+    }
     const int delta = Nkv - Nq;
-    const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
 
     // Q^T fragments (B operand): lane (g, i) holds Q[row i][16kk + 8g .. +7]. The loads go
     // out back to back ahead of the first K/V tiles (padding rows read the last row) and are
@@ -165,7 +185,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     c = fmaxf(fabsf(c), 1.17549435e-38f);
     s16x8 qf[C::NKK];
     {
-        const uint16_t *qr = Q + qbase + (size_t)min(row, Nq - 1) * D + 8 * g;
+        const uint16_t *qr = Q + qbase + (size_t)min(row, Nq - 1) * rs + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = *(const s16x8 *)(qr + 16 * kk);
     }
@@ -234,6 +254,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
 
     const char *kbh = (const char *)(K + kvbase);
     const char *vbh = (const char *)(V + kvbase);
+    auto kslot = [&](int t) { return lds + (t % NS) * C::TILEB; };
+    auto vslot = [&](int t) { return lds + C::VREG + (t % NS) * C::TILEB; };
     // Load u of this wave fills rows r of the K (or V) tile; lane l lands in physical chunk
     // l % CHUNKS of row r = first + l / CHUNKS, so it fetches the logical chunk the swizzle
     // stores there. Offsets are relative to the tile's first key.
@@ -243,8 +265,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
         const int i = wave + NW * u;
         const int r = (i % C::KL) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
         const int pc = lane % C::CHUNKS;
-        off[u] = r * C::ROWB + 16 * (i < C::KL ? k_swz<D>(r, pc) : v_swz<D>(r, pc));
+        off[u] = r * (PAGED ? pg.H * C::ROWB : C::ROWB) +
+                 16 * (i < C::KL ? k_swz<D>(r, pc) : v_swz<D>(r, pc));
     }
+    const int32_t *seq_table = PAGED ? pg.table + (size_t)seq * pg.max_pages : nullptr;
+    auto load_tile = [&](int tl, int slot) {
+        if constexpr (PAGED)
+            issue_kv_paged<C>(kbh, vbh, seq_table, pg.num_pages, pg.H, head, off, tl * BN, Nkv,
+                              kslot(slot), vslot(slot), wave);
+        else
+            issue_kv<C>(kbh, vbh, off, tl * BN, Nkv, kslot(slot), vslot(slot), wave);
+    };
     int kofs[C::NKK], vofs[C::NDB];
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * k_swz<D>(li, 2 * kk + g);
@@ -256,16 +287,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
             vofs[db] = trow * C::ROWB + 16 * v_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
     }
 
-    auto kslot = [&](int t) { return lds + (t % NS) * C::TILEB; };
-    auto vslot = [&](int t) { return lds + C::VREG + (t % NS) * C::TILEB; };
-
     // Prologue: tiles 0 .. NS-2 in flight; wait for tiles 0 and 1.
     TileSchedule::Cursor ld = sch.begin();
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) {
         if (j < ntl) {
             const int tl = MASK == kBlockSparse ? bs_tile(j) : ld.t;
-            issue_kv<C>(kbh, vbh, off, tl * BN, Nkv, kslot(j), vslot(j), wave);
+            load_tile(tl, j);
             ld = sch.next(ld);
         }
     }
@@ -300,8 +328,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     auto load_ahead = [&](int t) {
         if (t + NS - 1 < ntl) {
             const int tl = MASK == kBlockSparse ? bs_tile(t + NS - 1) : ld.t;
-            issue_kv<C>(kbh, vbh, off, tl * BN, Nkv, kslot(t + NS - 1), vslot(t + NS - 1),
-                        wave);
+            load_tile(tl, t + NS - 1);
             ld = sch.next(ld);
         }
     };
@@ -338,7 +365,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const float lt = half_swap_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row < Nq) {
-        uint16_t *orow = O + qbase + (size_t)row * D;
+        uint16_t *orow = O + qbase + (size_t)row * rs;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
@@ -349,7 +376,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
             }
         }
         if (g == 0)
-            LSE[(size_t)bh * Nq + row] =
+            LSE[lbase + (size_t)row * lstride] =
                 lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     }
 }
@@ -501,7 +528,7 @@ hipError_t launch16(const FwdArgs &a, hipStream_t s)
     using C = CfgSP<D, kStages, kWaves>;
     const int nqt = (a.Nq + C::BM - 1) / C::BM;
     const long nblk = (long)nqt * a.B * a.H;
-    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves>;
+    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves, false>;
     // block sparse: wave counts and the key-block list (2 bytes a block) after the ring
     const int lds = MASK == kBlockSparse ? C::LDS_BYTES + 16 + 2 * kMaxKeyBlocks : C::LDS_BYTES;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -510,8 +537,40 @@ hipError_t launch16(const FwdArgs &a, hipStream_t s)
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), lds, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        (uint16_t *)a.o, a.lse, a.Nq, a.Nkv, a.scale * kLog2e, a.window,
-                       a.n_global, nqt, a.layout, a.H);
+                       a.n_global, nqt, a.layout, a.H, PagedKV{});
     return hipGetLastError();
+}
+
+// Chunked prefill against a paged cache: one workgroup per (sequence, head, 128-row tile of
+// the longest chunk); workgroups past their own sequence's chunk return at once.
+template <typename T, int D, int MASK>
+hipError_t launch16_paged(const PrefillArgs &a, hipStream_t s)
+{
+    using C = CfgSP<D, kStages, kWaves>;
+    const int nqt = (a.Qmax + C::BM - 1) / C::BM;
+    const long nblk = (long)nqt * a.S * a.H;
+    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves, true>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    const PagedKV pg{a.page_table, a.seq_lens, a.q_lens, a.max_pages, a.num_pages, a.Qmax, a.H};
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), C::LDS_BYTES, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k_pages,
+                       (const uint16_t *)a.v_pages, (uint16_t *)a.o, a.lse, 0, 0,
+                       a.scale * kLog2e, a.window, a.n_global, nqt, nullptr, a.H, pg);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch16_paged_mask(const PrefillArgs &a, hipStream_t s)
+{
+    switch (a.mask) {
+    case 0: return launch16_paged<T, D, 0>(a, s);
+    case 1: return launch16_paged<T, D, 1>(a, s);
+    case 2: return launch16_paged<T, D, 2>(a, s);
+    case 3: return launch16_paged<T, D, 3>(a, s);
+    default: return launch16_paged<T, D, 4>(a, s);
+    }
 }
 
 template <int D, int MASK>
@@ -561,6 +620,16 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t s)
     if (a.dtype == 1)
         return a.d == 64 ? launch16_mask<_Float16, 64>(a, s) : launch16_mask<_Float16, 128>(a, s);
     return a.d == 64 ? launch16_mask<__bf16, 64>(a, s) : launch16_mask<__bf16, 128>(a, s);
+}
+
+hipError_t launch_prefill_paged(const PrefillArgs &a, hipStream_t s)
+{
+    (void)hipGetLastError();
+    if (a.dtype == 1)
+        return a.d == 64 ? launch16_paged_mask<_Float16, 64>(a, s)
+                         : launch16_paged_mask<_Float16, 128>(a, s);
+    return a.d == 64 ? launch16_paged_mask<__bf16, 64>(a, s)
+                     : launch16_paged_mask<__bf16, 128>(a, s);
 }
 
 }  // namespace teaf

@@ -46,6 +46,18 @@ inline int decode_workspace_splits(int max_pages, int page_size)
     return (int)((tokens + kDecodeMinSplit - 1) / kDecodeMinSplit);
 }
 
+// Chunked prefill against a paged cache (pages of 256 tokens): q and o [S, Qmax, H, d],
+// lse [S, Qmax, H]; sequence s's chunk is its newest q_lens[s] of seq_lens[s] tokens.
+struct PrefillArgs {
+    const void *q, *k_pages, *v_pages;
+    const int32_t *page_table, *seq_lens, *q_lens;
+    void *o;
+    float *lse;
+    int S, Qmax, H, d, max_pages, num_pages;
+    float scale;
+    int mask, window, n_global, dtype;
+};
+
 struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
@@ -64,5 +76,6 @@ inline size_t backward_workspace_floats(int B, int H, int Nq)
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_prefill_paged(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace teaf

@@ -9,6 +9,8 @@ Recipe (every draw from one torch CPU generator seeded per workload):
     (round to nearest even);
   * backward: dO [B,H,Nq,d] from its own generator (gen_dout), float32 standard normals
     cast to the run's dtype;
+  * chunked prefill (paged): Q [S,Qmax,H,d] (rows past each chunk NaN), the chunk lengths,
+    then a seed for the paged cache, drawn like decode's;
   * paged decode: Q [S,H,d], then the S sequence lengths uniform in [len_lo, len_hi], then a
     random permutation of the physical page ids, then the K and V page pools
     [num_pages, page_size, H, d]. Slots past a sequence's length in its last page and the
@@ -45,6 +47,10 @@ WORKLOADS = {
     "blocksparse_bf16": dict(kind="prefill", B=1, H=32, Nq=16384, Nkv=16384, d=128,
                              dtype="bf16", mask=5, window=0, n_global=0, input_scale=1.0,
                              seed=8, block=128, density=0.125),
+    "prefill_paged_bf16": dict(kind="prefill_paged", S=8, Qmax=1024, H=32, d=128,
+                               dtype="bf16", page_size=256, len_lo=4096, len_hi=8192,
+                               max_len=8192, q_lo=512, q_hi=1024, spare_pages=4, mask=1,
+                               window=0, n_global=0, seed=9),
     "decode_f16": dict(kind="decode", S=8, H=32, d=128, dtype="f16", page_size=256,
                        len_lo=4096, len_hi=8192, max_len=8192, spare_pages=4, seed=5),
 }
@@ -136,6 +142,30 @@ def gen_decode(S, H, d, dtype, seed, page_size=256, len_lo=4096, len_hi=8192, ma
                 max_pages=max_pages)
 
 
+def gen_prefill_paged(S, Qmax, H, d, dtype, seed, page_size=256, len_lo=4096, len_hi=8192,
+                      max_len=None, q_lo=1, q_hi=None, spare_pages=4, lens=None, qlens=None):
+    """Chunked prefill inputs: the paged cache of gen_decode (same recipe and NaN poisoning)
+    plus a chunk per sequence. Draw order: Q [S,Qmax,H,d], then the S chunk lengths uniform
+    in [q_lo, min(q_hi, Qmax)] (each then capped at its sequence length), then the paged
+    cache exactly as gen_decode draws it. Q rows at or past a sequence's chunk hold NaN.
+    `lens`/`qlens` override the drawn lengths (the draws still happen)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    t = DTYPES[dtype]
+    q = torch.randn((S, Qmax, H, d), generator=g, dtype=torch.float32)
+    hi = Qmax if q_hi is None else min(q_hi, Qmax)
+    qdrawn = torch.randint(q_lo, hi + 1, (S,), generator=g, dtype=torch.int64)
+    cache = gen_decode(S, H, d, dtype, int(torch.randint(0, 2 ** 31 - 1, (1,), generator=g)),
+                       page_size, len_lo, len_hi, max_len, spare_pages, lens)
+    L = cache["seq_lens"].to(torch.int64)
+    ql = qdrawn if qlens is None else torch.as_tensor(qlens, dtype=torch.int64)
+    ql = torch.minimum(ql, L)
+    for s in range(S):
+        q[s, int(ql[s]):] = float("nan")
+    cache["q"] = q.to(t)
+    cache["q_lens"] = ql.to(torch.int32)
+    return cache
+
+
 def gen_workload(name, **override):
     """Inputs of a named workload (overrides replace any field, e.g. a smaller N)."""
     w = dict(WORKLOADS[name])
@@ -148,6 +178,12 @@ def gen_workload(name, **override):
             out["layout"] = gen_layout(w["H"], w["Nq"], w["Nkv"], w["block"], w["density"],
                                        w["seed"] + 1000)
         return w, out
+    if w["kind"] == "prefill_paged":
+        inp = gen_prefill_paged(w["S"], w["Qmax"], w["H"], w["d"], w["dtype"], w["seed"],
+                                w["page_size"], w["len_lo"], w["len_hi"], w.get("max_len"),
+                                w.get("q_lo", 1), w.get("q_hi"), w.get("spare_pages", 4),
+                                w.get("lens"), w.get("qlens"))
+        return w, inp
     inp = gen_decode(w["S"], w["H"], w["d"], w["dtype"], w["seed"], w["page_size"],
                      w["len_lo"], w["len_hi"], w.get("max_len"), w.get("spare_pages", 4),
                      w.get("lens"))
