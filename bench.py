@@ -7,7 +7,8 @@ One step is one call of the tiled attention forward (query-tile decomposition, Q
 tile stream, QK^T, scale and mask, online softmax, PV and the epilogue) over the dense bf16
 workload B=4 H=32 N=1024 d=128, the configuration the throughput metric is quoted on. The
 other workloads (fp16 dense, causal, sliding window + global keys, paged decode) are timed in
-the same run and reported under "workloads". Prints one JSON line.
+the same run and reported under "workloads", with chunked prefill against the paged cache and
+the backward pass (dQ, dK, dV) of the dense and causal workloads. Prints one JSON line.
 
 Throughput counts 4*d FLOPs per visible (query, key) pair (QK^T and PV), with the exact pair
 count of the mask (not whole tiles); decode counts algorithmic HBM bytes (K and V of every
@@ -31,7 +32,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PAGES_BF16_TFLOPS = 1.25    # pages' Ascend 910 bf16 time for this workload, as TFLOP/s
-KERNEL_SOURCES = ["tiled_exact_attention_forward_amd/csrc/fa_fwd.hip",
+KERNEL_SOURCES = ["tiled_exact_attention_forward_amd/csrc/fa_device.h",
+                  "tiled_exact_attention_forward_amd/csrc/fa_fwd.hip",
+                  "tiled_exact_attention_forward_amd/csrc/fa_bwd.hip",
                   "tiled_exact_attention_forward_amd/csrc/fa_decode.hip"]
 
 
@@ -174,6 +177,67 @@ def bench_prefill(name, steps, warmup, torch, fa, workloads, cold_calls=20):
                 cold_ms=cold, cold_tflops=flops / (cold[0] * 1e-3) / 1e12)
 
 
+def paged_prefill_pairs(w, seq_lens, q_lens):
+    """Visible (query, key) pairs of a chunked prefill: chunk row i of sequence s is at
+    absolute position i + L_s - n_s, with the workload's mask over L_s keys."""
+    total = 0
+    for L, n in zip(np.asarray(seq_lens, np.int64), np.asarray(q_lens, np.int64)):
+        if n > 0:
+            total += int(visible_counts(int(n), int(L), w["mask"], w["window"],
+                                        w["n_global"]).sum())
+    return total * w["H"]
+
+
+def bench_prefill_paged(name, steps, warmup, torch, fa, workloads, cold_calls=20):
+    w, inp = workloads.gen_workload(name)
+    dev = torch.device("cuda:0")
+    q, kp, vp, pt, sl, ql = (inp[x].to(dev) for x in ("q", "k_pages", "v_pages", "page_table",
+                                                      "seq_lens", "q_lens"))
+    o = torch.zeros_like(q)
+    lse = torch.zeros(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = workloads.default_scale(w["d"])
+    mask = (w["mask"], w["window"], w["n_global"])
+
+    def step():
+        fa.fa_prefill_paged(q, kp, vp, pt, sl, ql, scale, *mask, out=o, lse=lse)
+
+    ms, wall = time_calls(step, steps, warmup, torch)
+    cold = time_cold(step, cold_calls, torch) if cold_calls else (ms, ms, ms)
+    pairs = paged_prefill_pairs(w, inp["seq_lens"], inp["q_lens"])
+    flops = 4 * w["d"] * pairs
+    return dict(workload=name, w=w, ms=ms, wall_s=wall, flops=flops, pairs=pairs,
+                tflops=flops / (ms * 1e-3) / 1e12, cold_ms=cold,
+                cold_tflops=flops / (cold[0] * 1e-3) / 1e12,
+                seq_lens=[int(x) for x in inp["seq_lens"]],
+                q_lens=[int(x) for x in inp["q_lens"]])
+
+
+def bench_backward(name, steps, warmup, torch, fa, workloads, cold_calls=20):
+    """One fa_backward call (row statistics, dK/dV, dQ kernels) on a prefill workload, with
+    O and LSE from one forward call made before the timed region."""
+    w, inp = workloads.gen_workload(name)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    do = workloads.gen_dout(tuple(q.shape), w["dtype"], w["seed"] + 500).to(dev)
+    scale = workloads.default_scale(w["d"])
+    mask = (w["mask"], w["window"], w["n_global"])
+    o, lse = fa.fa_forward(q, k, v, scale, *mask)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((fa.fa_backward_workspace_bytes(w["B"], w["H"], w["Nq"]),),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fa_backward(q, k, v, o, lse, do, scale, *mask, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    ms, wall = time_calls(step, steps, warmup, torch)
+    cold = time_cold(step, cold_calls, torch) if cold_calls else (ms, ms, ms)
+    fwd_flops, pairs = prefill_flops(w)
+    flops = fwd_flops // 4 * 10  # 10 d per visible pair: S, dP, dV, dK, dQ
+    return dict(workload=name, w=w, ms=ms, wall_s=wall, flops=flops, pairs=pairs,
+                tflops=flops / (ms * 1e-3) / 1e12, cold_ms=cold,
+                cold_tflops=flops / (cold[0] * 1e-3) / 1e12)
+
+
 def bench_decode(name, steps, warmup, torch, fa, workloads, cold_calls=20):
     w, inp = workloads.gen_workload(name)
     dev = torch.device("cuda:0")
@@ -244,6 +308,8 @@ def main():
                     help="only run plain device copies of MIB MiB (for HBM counter scaling)")
     ap.add_argument("--profile-workload", default=None,
                     help="only run this workload for --steps calls (for profilers); no JSON")
+    ap.add_argument("--profile-backward", action="store_true",
+                    help="with --profile-workload: time the backward pass instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -270,7 +336,10 @@ def main():
         return
     if args.profile_workload:
         kind = workloads.WORKLOADS[args.profile_workload]["kind"]
-        fn = bench_prefill if kind == "prefill" else bench_decode
+        fn = {"prefill": bench_prefill, "decode": bench_decode,
+              "prefill_paged": bench_prefill_paged}[kind]
+        if args.profile_backward:
+            fn = bench_backward
         r = fn(args.profile_workload, args.steps, args.warmup, torch, fa, workloads, cold_calls=0)
         print(f"[bench] {args.profile_workload}: {r['ms'] * 1e3:.1f} us per call", file=sys.stderr)
         return
@@ -292,6 +361,30 @@ def main():
                                 cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
                                 cold_tflops=round(r["cold_tflops"], 2))
             print(f"[bench] {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
+        r = bench_prefill_paged("prefill_paged_bf16", max(10, args.steps // 4),
+                                max(3, args.warmup // 4), torch, fa, workloads)
+        others["prefill_paged_bf16"] = dict(
+            us=round(r["ms"] * 1e3, 2), tflops=round(r["tflops"], 2),
+            frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), visible_pairs=r["pairs"],
+            cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
+            cold_tflops=round(r["cold_tflops"], 2), seq_lens=r["seq_lens"], q_lens=r["q_lens"],
+            note="chunked prefill against the paged cache, causal bottom-right")
+        print(f"[bench] prefill_paged_bf16: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del r
+        for name in ("dense_bf16", "causal_bf16"):
+            r = bench_backward(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch,
+                               fa, workloads)
+            others["backward_" + name] = dict(
+                us=round(r["ms"] * 1e3, 2), tflops=round(r["tflops"], 2),
+                frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), visible_pairs=r["pairs"],
+                cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
+                cold_tflops=round(r["cold_tflops"], 2),
+                note="fa_backward (3 kernels); 10*d FLOPs per visible pair")
+            print(f"[bench] backward {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
             del r
             torch.cuda.empty_cache()

@@ -56,6 +56,9 @@ class Oracle:
             ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_long, ctypes.c_long, f64p,
             f64p, f64p]
         lib.oracle_attention_backward.restype = ctypes.c_int
+        lib.oracle_merge_lse.argtypes = [f32p, f32p, f32p, f32p, ctypes.c_long, ctypes.c_int,
+                                         f64p, f64p]
+        lib.oracle_merge_lse.restype = None
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -172,6 +175,38 @@ class Oracle:
             raise ValueError("oracle_prefill_paged rejected its arguments")
         return o, lse
 
+    def merge_lse(self, o_a, lse_a, o_b, lse_b):
+        """Merge two attention results over disjoint key sets (same rows), fp64.
+
+        o_*: [..., d]; lse_*: [...] (natural log). Returns (o, lse) float64 of those shapes.
+        """
+        oa, ob, la, lb = _f32(o_a), _f32(o_b), _f32(lse_a), _f32(lse_b)
+        assert oa.shape == ob.shape and la.shape == lb.shape == oa.shape[:-1]
+        d = oa.shape[-1]
+        rows = int(np.prod(la.shape))
+        o = np.empty(oa.shape, np.float64)
+        lse = np.empty(la.shape, np.float64)
+        self.lib.oracle_merge_lse(_p(oa, ctypes.c_float), _p(la, ctypes.c_float),
+                                  _p(ob, ctypes.c_float), _p(lb, ctypes.c_float), rows, d,
+                                  _p(o, ctypes.c_double), _p(lse, ctypes.c_double))
+        return o, lse
+
+    def multimodal(self, q_img, k_img, v_img, q_txt, k_txt, v_txt, scale):
+        """Attention of one image-text sequence with the article's multimodal pattern, fp64:
+        image tokens attend to all image tokens only; text tokens attend to all image tokens
+        and causally to text tokens (ascend-transformer-boost article, 场景四). On the
+        sequence [image; text] that is the prefix-LM mask with the image as the prefix, one
+        call of the plain definition. Inputs [B,H,N_img|N_txt,d]. Returns (o_img, lse_img,
+        o_txt, lse_txt) float64."""
+        qi, ki, vi = _f32(q_img), _f32(k_img), _f32(v_img)
+        qt, kt, vt = _f32(q_txt), _f32(k_txt), _f32(v_txt)
+        n_img = qi.shape[2]
+        q = np.concatenate([qi, qt], axis=2)
+        k = np.concatenate([ki, kt], axis=2)
+        v = np.concatenate([vi, vt], axis=2)
+        o, lse = self.attention(q, k, v, scale, 4, 0, n_img)
+        return o[:, :, :n_img], lse[:, :, :n_img], o[:, :, n_img:], lse[:, :, n_img:]
+
     def decode_paged(self, q, k_pages, v_pages, page_table, seq_lens, scale):
         """Single-token decode against a paged cache, fp64.
 
@@ -251,3 +286,11 @@ def decode_paged(*args, **kw):
 
 def prefill_paged(*args, **kw):
     return default().prefill_paged(*args, **kw)
+
+
+def merge_lse(*args, **kw):
+    return default().merge_lse(*args, **kw)
+
+
+def multimodal(*args, **kw):
+    return default().multimodal(*args, **kw)

@@ -453,3 +453,37 @@ int oracle_prefill_paged(const float *q, const float *k_pages, const float *v_pa
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Merge of two attention results over disjoint key sets A and B of the same query rows.
+ * With the row statistic lse = ln sum exp(score) over each set, the union has
+ *   lse = ln(exp(lse_a) + exp(lse_b)),  o = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b,
+ * which is how the "ascend-transformer-boost" article (场景四) can run the text queries'
+ * attention to text keys and to image keys as separate calls and still get the result of
+ * one call over both. A set without keys has lse = -inf and weight 0; a row with no key in
+ * either set stays o = 0, lse = -inf. Inputs are the values the device holds (float32
+ * copies); o_a, o_b, o: rows x d; lse_*: rows.
+ */
+void oracle_merge_lse(const float *o_a, const float *lse_a, const float *o_b,
+                      const float *lse_b, long rows, int d, double *o, double *lse)
+{
+    long r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        double la = lse_a[r], lb = lse_b[r], m = la > lb ? la : lb, wa, wb, t;
+        int c;
+        if (m == -INFINITY) {
+            for (c = 0; c < d; ++c)
+                o[(size_t)r * d + c] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
+        wa = exp(la - m);
+        wb = exp(lb - m);
+        t = wa + wb;
+        for (c = 0; c < d; ++c)
+            o[(size_t)r * d + c] = (wa * (double)o_a[(size_t)r * d + c] +
+                                    wb * (double)o_b[(size_t)r * d + c]) / t;
+        lse[r] = m + log(t);
+    }
+}

@@ -43,6 +43,9 @@ MUTANTS = {
     "prefill_value_head": ("vp[j] = v_pages + (tok * (size_t)H + (size_t)h)",
                            "vp[j] = v_pages + (tok * (size_t)H + (size_t)0)"),
     "prefill_chunk_shift": ("i + (L - nq), mode", "i + (L - nq) - 1, mode"),
+    "merge_weight_swap": ("wa = exp(la - m);", "wa = exp(lb - m);"),
+    "merge_lse_no_max": ("lse[r] = m + log(t);", "lse[r] = log(t);"),
+    "merge_not_normalised": ("o_b[(size_t)r * d + c]) / t;", "o_b[(size_t)r * d + c]);"),
 }
 
 

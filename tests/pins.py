@@ -668,9 +668,78 @@ def pin_prefill_paged(orc):
     assert np.array_equal(o[:, 0], do) and np.array_equal(l[:, 0], dl)
 
 
+def multimodal_mask(n_img, n_txt):
+    """The article's multimodal visibility written block by block: image->image all,
+    image->text none, text->image all, text->text causal (tril)."""
+    n = n_img + n_txt
+    m = torch.zeros(n, n, dtype=torch.bool)
+    m[:n_img, :n_img] = True
+    m[n_img:, :n_img] = True
+    m[n_img:, n_img:] = torch.tril(torch.ones(n_txt, n_txt, dtype=torch.bool))
+    return m
+
+
+def pin_merge_lse(orc):
+    """Merging the results over two disjoint key sets (an arbitrary split, not contiguous)
+    gives torch SDPA over their union; an empty side leaves the other unchanged; two empty
+    sides give O = 0, LSE = -inf; the merge is symmetric."""
+    q = _rand((2, 2, 11, 8), 4500) * 2
+    k = _rand((2, 2, 37, 8), 4501) * 2
+    v = _rand((2, 2, 37, 8), 4502)
+    scale = float(np.float32(0.45))
+    pick = torch.from_numpy(np.random.default_rng(4503).random(37) < 0.4)
+    ma = pick[None, :].expand(11, 37).clone()
+    mb = ~ma
+    oa, la = library_attention_mask(q, k, v, scale, ma)
+    ob, lb = library_attention_mask(q, k, v, scale, mb)
+    ro, rl = library_attention_mask(q, k, v, scale, torch.ones(11, 37, dtype=torch.bool))
+    # the merge reads float32 inputs; give it exactly representable values of the parts
+    oa32, la32, ob32, lb32 = (np.asarray(x, np.float32) for x in (oa, la, ob, lb))
+    o, l = orc.merge_lse(oa32, la32, ob32, lb32)
+    # rounding the parts to float32 moves each lse by at most |lse| 2^-24 and each weight by
+    # a relative 2 |lse| 2^-24, so the union is met to within a few of those
+    eps = 4 * 2.0 ** -24 * max(np.abs(la).max(), np.abs(lb).max(), 1.0)
+    assert np.abs(l - rl).max() <= eps
+    assert np.abs(o - ro).max() <= 4 * eps * max(np.abs(ro).max(), 1.0)
+    o2, l2 = orc.merge_lse(ob32, lb32, oa32, la32)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    ninf = np.full_like(la32, -np.inf)
+    o3, l3 = orc.merge_lse(oa32, la32, np.zeros_like(ob32), ninf)
+    assert np.array_equal(o3, oa32.astype(np.float64)) and np.array_equal(l3, la32)
+    o4, l4 = orc.merge_lse(np.zeros_like(oa32), ninf, np.zeros_like(ob32), ninf)
+    assert np.all(o4 == 0) and np.all(l4 == -np.inf)
+
+
+def pin_multimodal(orc):
+    """The multimodal oracle against torch SDPA with the block-by-block multimodal mask, and
+    against the article's three-call split (image full, text causal, text to image)
+    merged by log-sum-exp."""
+    B, H, ni, nt, d = 1, 2, 9, 14, 8
+    qi, ki, vi = (_rand((B, H, ni, d), 4600 + i) for i in range(3))
+    qt, kt, vt = (_rand((B, H, nt, d), 4610 + i) for i in range(3))
+    scale = float(np.float32(0.4))
+    oi, li, ot, lt = orc.multimodal(qi, ki, vi, qt, kt, vt, scale)
+    q = np.concatenate([qi, qt], 2)
+    k = np.concatenate([ki, kt], 2)
+    v = np.concatenate([vi, vt], 2)
+    ro, rl = library_attention_mask(q, k, v, scale, multimodal_mask(ni, nt))
+    assert np.allclose(oi, ro[:, :, :ni], rtol=1e-12, atol=1e-13)
+    assert np.allclose(ot, ro[:, :, ni:], rtol=1e-12, atol=1e-13)
+    assert np.allclose(li, rl[:, :, :ni], rtol=1e-12, atol=1e-13)
+    assert np.allclose(lt, rl[:, :, ni:], rtol=1e-12, atol=1e-13)
+    o1, l1 = library_attention_mask(qi, ki, vi, scale, torch.ones(ni, ni, dtype=torch.bool))
+    o2, l2 = library_attention_mask(qt, kt, vt, scale, torch.tril(torch.ones(nt, nt,
+                                                                             dtype=torch.bool)))
+    o3, l3 = library_attention_mask(qt, ki, vi, scale, torch.ones(nt, ni, dtype=torch.bool))
+    assert np.allclose(oi, o1, rtol=1e-12, atol=1e-13) and np.allclose(li, l1, rtol=1e-12)
+    lm = np.logaddexp(l2, l3)
+    om = np.exp(l2 - lm)[..., None] * o2 + np.exp(l3 - lm)[..., None] * o3
+    assert np.allclose(ot, om, rtol=1e-12, atol=1e-13) and np.allclose(lt, lm, rtol=1e-12)
+
+
 ALL_PINS = [pin_library, pin_mpmath, pin_q_zero, pin_causal_row0, pin_onehot_edges,
             pin_rows_sum_to_one, pin_shift, pin_permutation, pin_split_merge,
             pin_mask_reductions, pin_empty_rows, pin_decode, pin_library_more_masks,
             pin_mpmath_more_masks, pin_q_zero_more_masks, pin_onehot_more_edges,
             pin_more_mask_reductions, pin_backward_library, pin_backward_finite_difference,
-            pin_backward_invariants, pin_prefill_paged]
+            pin_backward_invariants, pin_prefill_paged, pin_merge_lse, pin_multimodal]

@@ -52,3 +52,12 @@ def test_workload_flop_counts():
     assert pairs == 32 * 66976800
     _, pairs = bench.prefill_flops(workloads.WORKLOADS["causal_bf16"])
     assert pairs == 4 * 32 * 4096 * 4097 // 2
+
+
+def test_paged_prefill_pair_count():
+    """Chunk row i of a sequence with L keys and an n-token chunk sees i + L - n + 1 keys
+    (causal); the count is checked against the closed form summed over the chunk."""
+    w = dict(mask=1, window=0, n_global=0, H=3)
+    lens, qls = [700, 256, 1], [300, 0, 1]
+    want = 3 * sum(sum(i + L - n + 1 for i in range(n)) for L, n in zip(lens, qls))
+    assert bench.paged_prefill_pairs(w, lens, qls) == want
