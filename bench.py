@@ -7,8 +7,9 @@ One step is one call of the tiled attention forward (query-tile decomposition, Q
 tile stream, QK^T, scale and mask, online softmax, PV and the epilogue) over the dense bf16
 workload B=4 H=32 N=1024 d=128, the configuration the throughput metric is quoted on. The
 other workloads (fp16 dense, causal, sliding window + global keys, paged decode) are timed in
-the same run and reported under "workloads", with chunked prefill against the paged cache and
-the backward pass (dQ, dK, dV) of the dense and causal workloads. Prints one JSON line.
+the same run and reported under "workloads", with chunked prefill against the paged cache,
+multimodal attention (three calls merged by log-sum-exp, beside one prefix-LM call) and the
+backward pass (dQ, dK, dV) of the dense and causal workloads. Prints one JSON line.
 
 Throughput counts 4*d FLOPs per visible (query, key) pair (QK^T and PV), with the exact pair
 count of the mask (not whole tiles); decode counts algorithmic HBM bytes (K and V of every
@@ -35,7 +36,8 @@ PAGES_BF16_TFLOPS = 1.25    # pages' Ascend 910 bf16 time for this workload, as 
 KERNEL_SOURCES = ["tiled_exact_attention_forward_amd/csrc/fa_device.h",
                   "tiled_exact_attention_forward_amd/csrc/fa_fwd.hip",
                   "tiled_exact_attention_forward_amd/csrc/fa_bwd.hip",
-                  "tiled_exact_attention_forward_amd/csrc/fa_decode.hip"]
+                  "tiled_exact_attention_forward_amd/csrc/fa_decode.hip",
+                  "tiled_exact_attention_forward_amd/csrc/fa_merge.hip"]
 
 
 # ----------------------------------------------------------------- accounting
@@ -212,6 +214,45 @@ def bench_prefill_paged(name, steps, warmup, torch, fa, workloads, cold_calls=20
                 q_lens=[int(x) for x in inp["q_lens"]])
 
 
+def multimodal_pairs(w):
+    """Visible pairs of the multimodal pattern per (b, h): image x image, text x image, and
+    text x text causally."""
+    ni, nt = w["n_img"], w["n_txt"]
+    return (ni * ni + nt * ni + nt * (nt + 1) // 2) * w["B"] * w["H"]
+
+
+def bench_multimodal(name, steps, warmup, torch, fa, workloads, cold_calls=20):
+    """The three-call split with its merge (fa_multimodal_forward) and, for comparison, one
+    prefix-LM call over [image; text] (the unified mask)."""
+    w, inp = workloads.gen_workload(name)
+    dev = torch.device("cuda:0")
+    qi, ki, vi, qt, kt, vt = (inp[x].to(dev) for x in ("q_img", "k_img", "v_img", "q_txt",
+                                                       "k_txt", "v_txt"))
+    scale = workloads.default_scale(w["d"])
+    code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16}[w["dtype"]]
+    ws = torch.empty((fa.fa_multimodal_workspace_bytes(w["B"], w["H"], w["n_txt"], w["d"],
+                                                       code),), dtype=torch.uint8, device=dev)
+
+    def split():
+        fa.fa_multimodal_forward(qi, ki, vi, qt, kt, vt, scale, workspace=ws)
+
+    q, k, v = (torch.cat([a, b], dim=2).contiguous() for a, b in ((qi, qt), (ki, kt), (vi, vt)))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def unified():
+        fa.fa_forward(q, k, v, scale, fa.FA_MASK_PREFIX_LM, 0, w["n_img"], out=o, lse=lse)
+
+    ms, wall = time_calls(split, steps, warmup, torch)
+    ms_u, _ = time_calls(unified, steps, warmup, torch)
+    cold = time_cold(split, cold_calls, torch) if cold_calls else (ms, ms, ms)
+    pairs = multimodal_pairs(w)
+    flops = 4 * w["d"] * pairs
+    return dict(workload=name, w=w, ms=ms, wall_s=wall, ms_unified=ms_u, flops=flops,
+                pairs=pairs, tflops=flops / (ms * 1e-3) / 1e12,
+                tflops_unified=flops / (ms_u * 1e-3) / 1e12, cold_ms=cold)
+
+
 def bench_backward(name, steps, warmup, torch, fa, workloads, cold_calls=20):
     """One fa_backward call (row statistics, dK/dV, dQ kernels) on a prefill workload, with
     O and LSE from one forward call made before the timed region."""
@@ -337,7 +378,7 @@ def main():
     if args.profile_workload:
         kind = workloads.WORKLOADS[args.profile_workload]["kind"]
         fn = {"prefill": bench_prefill, "decode": bench_decode,
-              "prefill_paged": bench_prefill_paged}[kind]
+              "prefill_paged": bench_prefill_paged, "multimodal": bench_multimodal}[kind]
         if args.profile_backward:
             fn = bench_backward
         r = fn(args.profile_workload, args.steps, args.warmup, torch, fa, workloads, cold_calls=0)
@@ -374,6 +415,20 @@ def main():
             note="chunked prefill against the paged cache, causal bottom-right")
         print(f"[bench] prefill_paged_bf16: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+        del r
+        r = bench_multimodal("multimodal_bf16", max(10, args.steps // 4),
+                             max(3, args.warmup // 4), torch, fa, workloads)
+        others["multimodal_bf16"] = dict(
+            us=round(r["ms"] * 1e3, 2), tflops=round(r["tflops"], 2),
+            frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), visible_pairs=r["pairs"],
+            unified_us=round(r["ms_unified"] * 1e3, 2),
+            unified_tflops=round(r["tflops_unified"], 2),
+            split_speedup=round(r["ms_unified"] / r["ms"], 3),
+            cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
+            note="three calls (image full, text causal, text to image) + LSE merge; unified_*: "
+                 "one prefix-LM call over [image; text]")
+        print(f"[bench] multimodal_bf16: split {r['ms'] * 1e3:.1f} us, unified "
+              f"{r['ms_unified'] * 1e3:.1f} us", file=sys.stderr, flush=True)
         del r
         for name in ("dense_bf16", "causal_bf16"):
             r = bench_backward(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch,

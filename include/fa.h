@@ -149,6 +149,51 @@ int fa_backward(const void *q, const void *k, const void *v, const void *o, cons
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fa_merge_lse -- combine two attention results over disjoint key sets of the same query
+ * rows: lse = ln(e^lse_a + e^lse_b), o = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b. This
+ * is the step that lets the "ascend-transformer-boost" article (场景四) compute one
+ * attention as separate calls over parts of the keys. A side with lse = -inf contributes
+ * nothing; a row with -inf on both sides gets o = 0, lse = -inf.
+ *
+ *  o_a, o_b, o   [rows, d] dtype (o may alias o_a or o_b)
+ *  lse_a, lse_b, lse  [rows] float32, natural log (lse may alias lse_a or lse_b)
+ *  Supported: d in {64, 128}; dtype FA_F32, FA_F16, FA_BF16; rows >= 1; o_a, o_b, o
+ *  16-byte aligned. Arithmetic in float32; o is rounded to dtype once.
+ */
+int fa_merge_lse(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b,
+                 void *o, float *lse, long long rows, int d, int dtype, void *stream);
+
+/*
+ * fa_multimodal_forward -- attention of image and text tokens with the multimodal pattern
+ * of the "ascend-transformer-boost" article (场景四): image tokens attend to all image
+ * tokens and no text; text tokens attend to all image tokens and causally to text tokens.
+ * As the article does, this runs three regular attention calls, none with an irregular
+ * mask, and merges by log-sum-exp:
+ *   1. image queries x image keys, no mask        -> o_img, lse_img
+ *   2. text queries x text keys, causal           -> o_txt, lse_txt
+ *   3. text queries x image keys, no mask         -> workspace
+ *   4. fa_merge_lse of 2 and 3 into o_txt, lse_txt.
+ * The result equals (up to rounding) one call over [image; text] with FA_MASK_PREFIX_LM
+ * and n_global = n_img.
+ *
+ *  q_img, k_img, v_img  [B, H, n_img, d] dtype;  q_txt, k_txt, v_txt  [B, H, n_txt, d]
+ *  o_img [B, H, n_img, d], lse_img [B, H, n_img]; o_txt [B, H, n_txt, d],
+ *  lse_txt [B, H, n_txt]: written (lse float32).
+ *  workspace  at least fa_multimodal_workspace_bytes(B, H, n_txt, d, dtype) bytes,
+ *             16-byte aligned, no initialisation needed (the text-to-image partial result).
+ *  Supported: as fa_forward for each call (d in {64, 128}; FA_F32, FA_F16, FA_BF16).
+ *  All argument checks of the four steps run before the first launch; the four kernels
+ *  are enqueued in order on `stream`.
+ */
+size_t fa_multimodal_workspace_bytes(int B, int H, int n_txt, int d, int dtype);
+
+int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_img,
+                          const void *q_txt, const void *k_txt, const void *v_txt, void *o_img,
+                          float *lse_img, void *o_txt, float *lse_txt, int B, int H, int n_img,
+                          int n_txt, int d, float scale, int dtype, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * Paged single-token decode ("ascend-transformer-boost" article, 场景二: KV cache split
  * into fixed pages of 256 tokens, a new page per overflow, no reallocation; the attention
  * reads history K/V through the page layout). Each sequence has one query token at the

@@ -170,3 +170,49 @@ def pre(q=P, kp=P, vp=P, pt=P, sl=P, ql=P, o=P, lse=P, page=256, S=4, Qm=64, H=8
 ])
 def test_prefill_paged_rejects_before_launch(kw, status):
     assert pre(**kw) == status
+
+
+def mrg(oa=P, la=P, ob=P, lb=P, o=P, l=P, rows=10, d=128, dtype=2):
+    return fa.load_library().fa_merge_lse(oa, la, ob, lb, o, l, rows, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(oa=N), fa.FA_ERR_NULL), (dict(lb=N), fa.FA_ERR_NULL), (dict(o=N), fa.FA_ERR_NULL),
+    (dict(l=N), fa.FA_ERR_NULL), (dict(rows=0), fa.FA_ERR_SHAPE),
+    (dict(rows=1 << 41), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=4), fa.FA_ERR_UNSUPPORTED), (dict(ob=ctypes.c_void_p(0x1004)),
+                                             fa.FA_ERR_UNSUPPORTED),
+])
+def test_merge_rejects_before_launch(kw, status):
+    assert mrg(**kw) == status
+
+
+def mm(qi=P, ki=P, vi=P, qt=P, kt=P, vt=P, oi=P, li=P, ot=P, lt=P, B=1, H=2, ni=9, nt=14, d=64,
+       scale=0.1, dtype=2, ws=P, wsb=None):
+    lib = fa.load_library()
+    if wsb is None:
+        wsb = lib.fa_multimodal_workspace_bytes(B, H, nt, d, dtype)
+    return lib.fa_multimodal_forward(qi, ki, vi, qt, kt, vt, oi, li, ot, lt, B, H, ni, nt, d,
+                                     scale, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qi=N), fa.FA_ERR_NULL), (dict(vt=N), fa.FA_ERR_NULL), (dict(lt=N), fa.FA_ERR_NULL),
+    (dict(oi=N), fa.FA_ERR_NULL), (dict(ni=0), fa.FA_ERR_SHAPE), (dict(nt=0), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED), (dict(dtype=9), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=N), fa.FA_ERR_WORKSPACE), (dict(wsb=64), fa.FA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x1001)), fa.FA_ERR_WORKSPACE),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+])
+def test_multimodal_rejects_before_launch(kw, status):
+    assert mm(**kw) == status
+
+
+def test_multimodal_workspace_bytes():
+    lib = fa.load_library()
+    rows = 2 * 3 * 100
+    # the text-to-image partial output (rounded up to 256 bytes) and its row LSE
+    assert lib.fa_multimodal_workspace_bytes(2, 3, 100, 128, 2) == \
+        ((rows * 128 * 2 + 255) // 256) * 256 + rows * 4
+    assert lib.fa_multimodal_workspace_bytes(2, 3, 100, 64, 0) == \
+        ((rows * 64 * 4 + 255) // 256) * 256 + rows * 4

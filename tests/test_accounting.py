@@ -61,3 +61,11 @@ def test_paged_prefill_pair_count():
     lens, qls = [700, 256, 1], [300, 0, 1]
     want = 3 * sum(sum(i + L - n + 1 for i in range(n)) for L, n in zip(lens, qls))
     assert bench.paged_prefill_pairs(w, lens, qls) == want
+
+
+def test_multimodal_pair_count():
+    """Image rows see the image; text rows see the image and earlier text: the same count
+    as the prefix-LM mask over [image; text] with the image as prefix."""
+    w = dict(n_img=5, n_txt=7, B=2, H=3)
+    want = int(bench.visible_counts(12, 12, 4, 0, 5).sum()) * 6
+    assert bench.multimodal_pairs(w) == want

@@ -9,6 +9,9 @@ C ABI declared in include/fa.h. The functions carry the C names:
     fa_backward_workspace_bytes(...)
     fa_decode_paged(q, k_pages, ...)  single-token decode against a paged K/V cache
     fa_prefill_paged(q, k_pages, ...) multi-token chunk per sequence against a paged cache
+    fa_merge_lse(o_a, lse_a, o_b, lse_b, ...)  merge results over disjoint key sets
+    fa_multimodal_forward(...)        image/text attention as three calls plus a merge
+    fa_multimodal_workspace_bytes(...)
     fa_decode_paged_workspace_bytes(...)
     fa_status_string(status)
 
@@ -21,7 +24,8 @@ import math
 import os
 
 __all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_bytes",
-           "fa_decode_paged", "fa_prefill_paged", "fa_decode_paged_workspace_bytes",
+           "fa_decode_paged", "fa_prefill_paged", "fa_merge_lse", "fa_multimodal_forward",
+           "fa_multimodal_workspace_bytes", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
            "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
            "FA_MASK_WINDOW_GLOBAL", "FA_MASK_BAND", "FA_MASK_PREFIX_LM", "EXPORTED_SYMBOLS"]
@@ -32,6 +36,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_backward",
                     "fa_backward_workspace_bytes", "fa_decode_paged", "fa_prefill_paged",
+                    "fa_merge_lse", "fa_multimodal_forward", "fa_multimodal_workspace_bytes",
                     "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_last_hip_error",
                     "fa_version")
 
@@ -81,6 +86,13 @@ def load_library():
     lib.fa_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i,
                                      i, i, i, vp]
     lib.fa_prefill_paged.restype = i
+    lib.fa_merge_lse.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_longlong, i, i, vp]
+    lib.fa_merge_lse.restype = i
+    lib.fa_multimodal_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_multimodal_workspace_bytes.restype = sz
+    lib.fa_multimodal_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                          f, i, vp, sz, vp]
+    lib.fa_multimodal_forward.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.restype = i
@@ -304,3 +316,66 @@ def fa_prefill_paged(q, k_pages, v_pages, page_table, seq_lens, q_lens, scale=No
     if rc != FA_OK:
         raise FaError(rc, "fa_prefill_paged")
     return out, lse
+
+
+def fa_merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse=None, stream=None):
+    """Merge attention results over disjoint key sets: o_* [..., d], lse_* [...] float32
+    (GPU). Returns (out, lse); out/lse may be o_a/lse_a for an in-place merge."""
+    torch = _torch()
+    d = o_a.shape[-1]
+    if tuple(o_b.shape) != tuple(o_a.shape) or tuple(lse_a.shape) != tuple(o_a.shape[:-1]) \
+            or tuple(lse_b.shape) != tuple(lse_a.shape):
+        raise ValueError("o_a, o_b [..., d] and lse_a, lse_b [...] must match")
+    out = torch.empty_like(o_a) if out is None else out
+    lse = torch.empty_like(lse_a) if lse is None else lse
+    for name, t in (("o_a", o_a), ("o_b", o_b), ("out", out)):
+        _check_dev(name, t, o_a.dtype)
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b), ("lse", lse)):
+        _check_dev(name, t, torch.float32)
+    rc = load_library().fa_merge_lse(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out),
+                                     _ptr(lse), lse_a.numel(), d, _dtype_code(o_a),
+                                     _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_merge_lse")
+    return out, lse
+
+
+def fa_multimodal_workspace_bytes(B, H, n_txt, d, dtype_code):
+    return int(load_library().fa_multimodal_workspace_bytes(int(B), int(H), int(n_txt), int(d),
+                                                            int(dtype_code)))
+
+
+def fa_multimodal_forward(q_img, k_img, v_img, q_txt, k_txt, v_txt, scale=None, workspace=None,
+                          stream=None):
+    """Image/text attention (image sees image; text sees image and earlier text) as three
+    attention calls and a log-sum-exp merge. Inputs [B,H,n,d] on the GPU. Returns
+    (o_img, lse_img, o_txt, lse_txt)."""
+    torch = _torch()
+    B, H, n_img, d = q_img.shape
+    n_txt = q_txt.shape[2]
+    for name, t, n in (("k_img", k_img, n_img), ("v_img", v_img, n_img),
+                       ("q_txt", q_txt, n_txt), ("k_txt", k_txt, n_txt),
+                       ("v_txt", v_txt, n_txt)):
+        if tuple(t.shape) != (B, H, n, d):
+            raise ValueError(f"{name} must be [B,H,{n},d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_img, o_txt = torch.empty_like(q_img), torch.empty_like(q_txt)
+    lse_img = torch.empty((B, H, n_img), dtype=torch.float32, device=q_img.device)
+    lse_txt = torch.empty((B, H, n_txt), dtype=torch.float32, device=q_img.device)
+    code = _dtype_code(q_img)
+    need = fa_multimodal_workspace_bytes(B, H, n_txt, d, code)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q_img.device)
+    for name, t in (("q_img", q_img), ("k_img", k_img), ("v_img", v_img), ("q_txt", q_txt),
+                    ("k_txt", k_txt), ("v_txt", v_txt)):
+        _check_dev(name, t, q_img.dtype)
+    _check_dev("workspace", workspace)
+    rc = load_library().fa_multimodal_forward(
+        _ptr(q_img), _ptr(k_img), _ptr(v_img), _ptr(q_txt), _ptr(k_txt), _ptr(v_txt),
+        _ptr(o_img), _ptr(lse_img), _ptr(o_txt), _ptr(lse_txt), B, H, n_img, n_txt, d,
+        float(scale), code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_multimodal_forward")
+    return o_img, lse_img, o_txt, lse_txt

@@ -42,9 +42,14 @@ const char *fa_status_string(int status)
     }
 }
 
-int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-               int Nq, int Nkv, int d, float scale, int mask_mode, int window, int n_global,
-               int dtype, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Checks of one forward call; on success fills *a (window and prefix counts clamped).
+int check_forward(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                  int H, int Nq, int Nkv, int d, float scale, int mask_mode, int window,
+                  int n_global, int dtype, teaf::FwdArgs *a)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return FA_ERR_SHAPE;
@@ -68,8 +73,79 @@ int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse,
     const bool uses_g = mask_mode == FA_MASK_WINDOW_GLOBAL || mask_mode == FA_MASK_PREFIX_LM;
     const int wc = uses_w ? (int)std::min<long long>(window, (long long)Nq + Nkv) : 0;
     const int gc = uses_g ? std::min(n_global, Nkv) : 0;
-    teaf::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nkv, d, scale, mask_mode, wc, gc, dtype};
+    *a = teaf::FwdArgs{q, k, v, o, lse, B, H, Nq, Nkv, d, scale, mask_mode, wc, gc, dtype};
+    return FA_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int Nq, int Nkv, int d, float scale, int mask_mode, int window, int n_global,
+               int dtype, void *stream)
+{
+    teaf::FwdArgs a;
+    const int st = check_forward(q, k, v, o, lse, B, H, Nq, Nkv, d, scale, mask_mode, window,
+                                 n_global, dtype, &a);
+    if (st != FA_OK) return st;
     return hip_status(teaf::launch_forward(a, (hipStream_t)stream));
+}
+
+int fa_merge_lse(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b,
+                 void *o, float *lse, long long rows, int d, int dtype, void *stream)
+{
+    if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return FA_ERR_NULL;
+    if (rows < 1 || rows > (1ll << 40)) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (rows * (d / (16 / (long long)elem_bytes(dtype))) / 256 >= (long long)UINT_MAX)
+        return FA_ERR_SHAPE;
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
+    teaf::MergeArgs a{o_a, lse_a, o_b, lse_b, o, lse, (long)rows, d, dtype};
+    return hip_status(teaf::launch_merge(a, (hipStream_t)stream));
+}
+
+size_t fa_multimodal_workspace_bytes(int B, int H, int n_txt, int d, int dtype)
+{
+    if (B < 1 || H < 1 || n_txt < 1 || d < 1) return 0;
+    const size_t rows = (size_t)B * H * n_txt;
+    return align256(rows * d * elem_bytes(dtype)) + rows * sizeof(float);
+}
+
+int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_img,
+                          const void *q_txt, const void *k_txt, const void *v_txt, void *o_img,
+                          float *lse_img, void *o_txt, float *lse_txt, int B, int H, int n_img,
+                          int n_txt, int d, float scale, int dtype, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    teaf::FwdArgs img, txt, cross;
+    int st = check_forward(q_img, k_img, v_img, o_img, lse_img, B, H, n_img, n_img, d, scale,
+                           FA_MASK_NONE, 0, 0, dtype, &img);
+    if (st != FA_OK) return st;
+    st = check_forward(q_txt, k_txt, v_txt, o_txt, lse_txt, B, H, n_txt, n_txt, d, scale,
+                       FA_MASK_CAUSAL, 0, 0, dtype, &txt);
+    if (st != FA_OK) return st;
+    if (!workspace || workspace_bytes < fa_multimodal_workspace_bytes(B, H, n_txt, d, dtype) ||
+        !aligned16(workspace))
+        return FA_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * H * n_txt;
+    char *ws = (char *)workspace;
+    float *lse_x = (float *)(ws + align256(rows * d * elem_bytes(dtype)));
+    st = check_forward(q_txt, k_img, v_img, ws, lse_x, B, H, n_txt, n_img, d, scale,
+                       FA_MASK_NONE, 0, 0, dtype, &cross);
+    if (st != FA_OK) return st;
+    const teaf::MergeArgs mg{o_txt, lse_txt, ws, lse_x, o_txt, lse_txt, (long)rows, d, dtype};
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = teaf::launch_forward(img, s);
+    if (e == hipSuccess) e = teaf::launch_forward(txt, s);
+    if (e == hipSuccess) e = teaf::launch_forward(cross, s);
+    if (e == hipSuccess) e = teaf::launch_merge(mg, s);
+    return hip_status(e);
 }
 
 int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -58,6 +58,19 @@ struct PrefillArgs {
     int mask, window, n_global, dtype;
 };
 
+// Merge of two attention results over disjoint key sets: rows x d outputs (dtype) and row
+// log-sum-exps (float32); o and lse may alias o_a and lse_a.
+struct MergeArgs {
+    const void *o_a;
+    const float *lse_a;
+    const void *o_b;
+    const float *lse_b;
+    void *o;
+    float *lse;
+    long rows;
+    int d, dtype;
+};
+
 struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
@@ -77,5 +90,6 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
 }  // namespace teaf

@@ -11,6 +11,8 @@ Recipe (every draw from one torch CPU generator seeded per workload):
     cast to the run's dtype;
   * chunked prefill (paged): Q [S,Qmax,H,d] (rows past each chunk NaN), the chunk lengths,
     then a seed for the paged cache, drawn like decode's;
+  * multimodal: the image's Q, K, V like prefill with the workload seed, then the text's
+    with seed + 1;
   * paged decode: Q [S,H,d], then the S sequence lengths uniform in [len_lo, len_hi], then a
     random permutation of the physical page ids, then the K and V page pools
     [num_pages, page_size, H, d]. Slots past a sequence's length in its last page and the
@@ -51,6 +53,8 @@ WORKLOADS = {
                                dtype="bf16", page_size=256, len_lo=4096, len_hi=8192,
                                max_len=8192, q_lo=512, q_hi=1024, spare_pages=4, mask=1,
                                window=0, n_global=0, seed=9),
+    "multimodal_bf16": dict(kind="multimodal", B=4, H=32, n_img=576, n_txt=2048, d=128,
+                            dtype="bf16", input_scale=1.0, seed=10),
     "decode_f16": dict(kind="decode", S=8, H=32, d=128, dtype="f16", page_size=256,
                        len_lo=4096, len_hi=8192, max_len=8192, spare_pages=4, seed=5),
 }
@@ -166,6 +170,14 @@ def gen_prefill_paged(S, Qmax, H, d, dtype, seed, page_size=256, len_lo=4096, le
     return cache
 
 
+def gen_multimodal(B, H, n_img, n_txt, d, dtype, seed, input_scale=1.0):
+    """Image and text attention inputs: the image's Q, K, V [B,H,n_img,d] drawn like
+    gen_prefill with `seed`, then the text's Q, K, V [B,H,n_txt,d] with seed + 1."""
+    qi, ki, vi = gen_prefill(B, H, n_img, n_img, d, dtype, seed, input_scale)
+    qt, kt, vt = gen_prefill(B, H, n_txt, n_txt, d, dtype, seed + 1, input_scale)
+    return dict(q_img=qi, k_img=ki, v_img=vi, q_txt=qt, k_txt=kt, v_txt=vt)
+
+
 def gen_workload(name, **override):
     """Inputs of a named workload (overrides replace any field, e.g. a smaller N)."""
     w = dict(WORKLOADS[name])
@@ -178,6 +190,9 @@ def gen_workload(name, **override):
             out["layout"] = gen_layout(w["H"], w["Nq"], w["Nkv"], w["block"], w["density"],
                                        w["seed"] + 1000)
         return w, out
+    if w["kind"] == "multimodal":
+        return w, gen_multimodal(w["B"], w["H"], w["n_img"], w["n_txt"], w["d"], w["dtype"],
+                                 w["seed"], w.get("input_scale", 1.0))
     if w["kind"] == "prefill_paged":
         inp = gen_prefill_paged(w["S"], w["Qmax"], w["H"], w["d"], w["dtype"], w["seed"],
                                 w["page_size"], w["len_lo"], w["len_hi"], w.get("max_len"),
