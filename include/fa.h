@@ -135,8 +135,8 @@ int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o
  *                 rounded to dtype) with float32 accumulation; the outputs are rounded
  *                 once at the end.
  *  workspace      device buffer of at least fa_backward_workspace_bytes(B, H, Nq) bytes
- *                 (per-row D and log2-scaled LSE); contents need no initialisation; 16-byte
- *                 aligned.
+ *                 (per-row D and log2-scaled LSE, grouped by 32-row tile); contents need no
+ *                 initialisation; 16-byte aligned.
  *  Supported: d in {64, 128}; masks FA_MASK_NONE .. FA_MASK_PREFIX_LM; sizes as fa_forward.
  *  Three kernels run on `stream` (row statistics, then dK/dV, then dQ); no atomics, so the
  *  results are bitwise reproducible. All tensor pointers need 16-byte alignment.

@@ -144,8 +144,8 @@ def test_backward_rejects_before_launch(kw, status):
 
 def test_backward_workspace_bytes():
     lib = fa.load_library()
-    # one float D_i and one float log2-scaled LSE per query row
-    assert lib.fa_backward_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 2 * 4
+    # per 32-row tile of each (b, h): 32 log2-scaled LSE values and 32 values of D (floats)
+    assert lib.fa_backward_workspace_bytes(2, 3, 100) == 2 * 3 * 4 * 64 * 4
     assert lib.fa_backward_workspace_bytes(1, 1, 0) == 0
 
 

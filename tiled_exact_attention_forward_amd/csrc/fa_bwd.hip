@@ -9,8 +9,9 @@
 //
 // gfx950 mapping: three kernels, no atomics (results are deterministic).
 //  * bwd_rowdot_kernel: D_i = sum_c dO_ic O_ic and the log2-domain row statistic
-//    L_i = LSE_i log2 e (+inf for a row without a visible key, so its P is 0).
-//  * bwd_dkdv_kernel: a workgroup owns 128 keys (4 waves x 32) with their K and V rows in
+//    L_i = LSE_i log2 e (+inf for a row without a visible key, so its P is 0), stored per
+//    32-row tile so that one 256-byte load brings a tile's statistics.
+//  * bwd_dkdv_kernel: a workgroup owns 256 keys (4 waves x 64) with their K and V rows in
 //    registers and walks the 32-row query tiles that can see them. It computes S = Q K^T and
 //    dP = dO V^T with lanes indexed by key, so that P and dS convert in place into the B
 //    operand of dV^T += dO^T P and dK^T += Q^T dS; Q^T and dO^T come from LDS through
@@ -18,30 +19,48 @@
 //  * bwd_dq_kernel: a workgroup owns 128 query rows (4 waves x 32) with Q and dO in
 //    registers and walks the visible 32-key tiles like the forward pass: S^T = K Q^T and
 //    dP^T = V dO^T with lanes indexed by row, then dQ^T += K^T dS^T.
-// Tiles stream from HBM to LDS with buffer_load ... lds into two stages. Scores, P, dS and
-// all accumulators are fp32; P and dS are rounded to the input type for the products.
+// Tiles stream from HBM to LDS with buffer_load ... lds (a 4-slot ring for dK/dV, two
+// stages for dQ). Scores, P, dS and all accumulators are fp32; P and dS are rounded to the
+// input type for the products.
 #include "fa_device.h"
 
 namespace teaf {
 namespace {
 
-// Two-stage tiles of 32 rows, 4 waves: the same layout arithmetic as the forward's ring.
+// Q/dO tiles of 32 rows stream through a 4-slot ring (like the forward's K/V ring; the
+// "K" half of the ring holds Q, the "V" half dO). Each slot also holds the tile's row
+// statistics: 32 L values then 32 D values (256 bytes).
+constexpr int kBwdStages = 4;
 template <int D>
-using CfgBD = CfgSP<D, 2, 4>;
+using CfgBD = CfgSP<D, kBwdStages, 4>;
+constexpr int kStatsBytes = 256;
 
-// D_i and L_i for every row: 16 lanes per row, 8 elements each for d = 128 (4 for d = 64).
+// Row statistics are stored per 32-row tile of each (b, h): [L_0..L_31, D_0..D_31], so one
+// 256-byte load brings a tile's statistics. Rows past Nq hold L = +inf (P = 0) and D = 0.
+__host__ __device__ inline size_t stats_index(size_t bh, int nt32, int row)
+{
+    return ((size_t)bh * nt32 + (size_t)(row >> 5)) * 64 + (size_t)(row & 31);
+}
+
+// D_i and L_i for every row (padding rows of the last tile included): 16 lanes per row, 8
+// elements each for d = 128 (4 for d = 64).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restrict__ O,
                                                          const uint16_t *__restrict__ dO,
                                                          const float *__restrict__ LSE,
-                                                         float *__restrict__ Drow,
-                                                         float *__restrict__ Lrow, long rows)
+                                                         float *__restrict__ ST, int Nq,
+                                                         int nt32, long padded_rows)
 {
     constexpr int PER = D / 16;
-    const long r = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const long pr = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int part = threadIdx.x & 15;
+    const long per_bh = (long)nt32 * 32;
+    const long bh = pr / per_bh;
+    const int rr = (int)(pr % per_bh);
+    const bool valid = pr < padded_rows && rr < Nq;
     float acc = 0.f;
-    if (r < rows) {
+    if (valid) {
+        const size_t r = (size_t)bh * Nq + rr;
         const uint16_t *o = O + r * D + part * PER;
         const uint16_t *g = dO + r * D + part * PER;
 #pragma unroll
@@ -51,13 +70,18 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restr
             acc = __builtin_fmaf((float)a, (float)b, acc);
         }
     }
-    // sum over the 16 lanes of a row (DPP-free butterfly through lane shuffles)
+    // sum over the 16 lanes of a row
 #pragma unroll
     for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
-    if (r < rows && part == 0) {
-        Drow[r] = acc;
-        const float lse = LSE[r];
-        Lrow[r] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    if (pr < padded_rows && part == 0) {
+        const size_t at = stats_index(bh, nt32, rr);
+        float l = INFINITY;
+        if (valid) {
+            const float lse = LSE[(size_t)bh * Nq + rr];
+            l = lse == -INFINITY ? INFINITY : lse * kLog2e;
+        }
+        ST[at] = l;
+        ST[at + 32] = valid ? acc : 0.f;
     }
 }
 
@@ -73,6 +97,23 @@ __device__ __forceinline__ int tr_ofs(int lane, int h, int db)
     const int trow = 8 * h + 4 * g + ((lane & 15) >> 2);
     const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     return trow * ROWB + 16 * k_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
+}
+
+// acc += a * b on the matrix cores with acc held in accumulation registers (AGPRs). The dK/dV
+// kernel keeps 256 accumulator values per lane for a whole key block; pinning them to the
+// AGPR file leaves the VGPRs to S and dP, which the compiler would otherwise move through
+// the same AGPRs on every tile (this file is built so that the compiler's own MFMAs use
+// VGPR destinations). The compiler does not see these as MFMAs, so the hazards it would
+// handle are covered here: s_nop 2 gives at least the wait states a vector write of a or
+// b needs before a matrix read of it, and the accumulators are read only after the
+// kernel's loop ends with padding of its own.
+template <typename T>
+__device__ __forceinline__ void mma_agpr(f32x16 &acc, s16x8 a, s16x8 b)
+{
+    if constexpr (__is_same(T, __bf16))
+        __asm__("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        __asm__("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Rows that may see keys [k0, k1] (a superset; the element mask decides).
@@ -96,17 +137,56 @@ __device__ __forceinline__ void rows_seeing(int k0, int k1, int Nq, int Nkv, int
     lo = max(lo, 0);
 }
 
+// Visible rows of one key as a range of tile-row offsets: with the lane's rows at positions
+// i0 + c (c = 8(e/4) + e%4, compile-time per element), key j is visible from row c when
+// lo <= c <= hi. Equivalent to key_visible for masks 1-4.
+template <int MASK>
+__device__ __forceinline__ void key_row_range(int j, int i0, int W, int G, int &lo, int &hi)
+{
+    const int a = j - i0;  // c >= a  <=>  j <= i0 + c (causal)
+    lo = a;
+    hi = INT_MAX;
+    if (MASK == 2 && j >= G) hi = a + W - 1;  // i - j < W
+    if (MASK == 3) {
+        lo = a - W;
+        hi = a + W;
+    }
+    if (MASK == 4 && j < G) lo = INT_MIN;
+}
+
+// True when every key in [k0, k1] is visible from every position in [i0, i1].
+template <int MASK>
+__device__ __forceinline__ bool block_visible(int i0, int i1, int k0, int k1, int W, int G)
+{
+    if (MASK == 0) return true;
+    if (MASK == 1) return k1 <= i0;
+    if (MASK == 2) return k1 <= i0 && (i1 - k0 < W || k1 < G);
+    if (MASK == 3) return k0 >= i1 - W && k1 <= i0 + W;
+    return k1 <= i0 || k1 < G;
+}
+
+// dK and dV. A workgroup owns 256 keys, 64 per wave in two 32-key halves. K fragments stay in
+// registers and V rows in LDS (64 KB, loaded once; registers go to the dK/dV accumulators);
+// each Q or dO fragment read from LDS feeds both halves, which halves the LDS reads per
+// MFMA against 32 keys per wave. Per 32-row tile:
+//   S = Q K^T, dP = dO V^T           (lanes indexed by key: lane (g, key) holds rows
+//                                     8(e/4) + 4g + e%4 of each half)
+//   P = 2^(c S - L), dS = P (dP - D) (elementwise, fp32)
+//   dV^T += dO^T P, dK^T += Q^T dS   (P, dS converted in place into B operands; dO^T and Q^T
+//                                     read transposed from LDS)
+// The MFMA order (S of both halves, then dP while the exponentials of P run, then dV while
+// dS is formed, then dK) lets one wave per SIMD overlap its vector and matrix work.
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ Drow, const float *__restrict__ Lrow, uint16_t *__restrict__ dK,
-    uint16_t *__restrict__ dV, int Nq, int Nkv, float c, float scale, int W, int G, int nkt)
+    const float *__restrict__ ST, uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int Nq,
+    int Nkv, float c, float scale, int W, int G, int nkt, int nt32)
 {
     using C = CfgBD<D>;
     using Op = Ops16<T>;
-    constexpr int BN = 32, NKK = C::NKK, NDB = C::NDB;
-    constexpr int STATS = C::LDS_BYTES;  // per stage: 32 L values then 32 D values
+    constexpr int BN = 32, NKK = C::NKK, NDB = C::NDB, NS = kBwdStages, LPW = C::LPW;
+    constexpr int KPB = 256;  // keys per workgroup
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char *const lds = (char *)smem;
 
@@ -115,30 +195,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int g = lane >> 5, li = lane & 31;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = L / nkt;
-    const int k0 = (L % nkt) * 128;
-    const int key = k0 + wave * 32 + li;
+    const int k0 = (L % nkt) * KPB;
+    const int kw = k0 + wave * 64;  // this wave's first key
     const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
+    const int delta = Nkv - Nq;
 
-    // K and V rows of this lane's key as MFMA fragments (keys past Nkv read as zeros).
-    s16x8 kf[NKK], vf[NKK];
+    // K rows of this lane's two keys as MFMA fragments (keys past Nkv read as zeros).
+    s16x8 kf[2][NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        if (key < Nkv) {
-            kf[kk] = *(const s16x8 *)(K + kvbase + (size_t)key * D + 16 * kk + 8 * g);
-            vf[kk] = *(const s16x8 *)(V + kvbase + (size_t)key * D + 16 * kk + 8 * g);
-        } else {
-            kf[kk] = vf[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int h = 0; h < 2; ++h) {
+        const int key = kw + 32 * h + li;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            kf[h][kk] = key < Nkv
+                            ? *(const s16x8 *)(K + kvbase + (size_t)key * D + 16 * kk + 8 * g)
+                            : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    // V rows of this wave's 64 keys go to LDS (after the ring and the statistics) with the K
+    // swizzle, each wave loading its own rows, zero past Nkv.
+    char *const vl = lds + C::LDS_BYTES + NS * kStatsBytes;
+#if defined(__HIP_DEVICE_COMPILE__)
+    {
+        const int rows = min(max(Nkv - kw, 0), 64);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(V + kvbase + (size_t)min(kw, Nkv - 1) * D), (short)0,
+            rows * C::ROWB, 0x00020000);
+        constexpr int VLOADS = 64 * C::ROWB / 1024;  // wave-wide 1 KB loads for 64 rows
+#pragma unroll
+        for (int u = 0; u < VLOADS; ++u) {
+            const int r = u * C::ROWS_PER_LOAD + lane / C::CHUNKS;
+            const unsigned vo = r * C::ROWB + 16 * k_swz<D>(r, lane % C::CHUNKS);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vr, (lds_void *)(vl + (wave * 64 + u * C::ROWS_PER_LOAD) * C::ROWB), 16, vo, 0,
+                0, 0);
         }
     }
-    f32x16 dkt[NDB], dvt[NDB];
+#endif
+    f32x16 dkt[2][NDB], dvt[2][NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) dkt[db] = dvt[db] = f32x16{};
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dkt[h][db] = dvt[h][db] = f32x16{};
 
-    // Q and dO tiles (32 rows) go to LDS like the forward's K and V tiles, both with the K
-    // swizzle (read row-wise for S and dP, transposed for dK and dV).
-    unsigned off[C::LPW];
+    // Q and dO tiles go to LDS like the forward's K tiles (K swizzle for both: read
+    // row-wise for S and dP, transposed for dK and dV).
+    unsigned off[LPW];
 #pragma unroll
-    for (int u = 0; u < C::LPW; ++u) {
+    for (int u = 0; u < LPW; ++u) {
         const int i = wave + C::NW * u;
         const int r = (i % C::KL) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
         off[u] = r * C::ROWB + 16 * k_swz<D>(r, lane % C::CHUNKS);
@@ -151,115 +254,193 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) tro[h][db] = tr_ofs<D>(lane, h, db);
+    const char *const vw = vl + wave * 64 * C::ROWB;  // this wave's V rows
 
     int rlo, rhi;
-    rows_seeing<MASK>(k0, min(k0 + 127, Nkv - 1), Nq, Nkv, W, G, rlo, rhi);
-    const int t0 = rlo / BN, t1 = rhi > rlo ? (rhi + BN - 1) / BN : t0;
+    rows_seeing<MASK>(k0, min(k0 + KPB - 1, Nkv - 1), Nq, Nkv, W, G, rlo, rhi);
+    const int t0 = rlo / BN;
+    const int ntl = rhi > rlo ? (rhi + BN - 1) / BN - t0 : 0;
     const char *qb = (const char *)(Q + qbase);
     const char *gb = (const char *)(dO + qbase);
-    auto qslot = [&](int n) { return lds + (n & 1) * C::TILEB; };
-    auto gslot = [&](int n) { return lds + C::VREG + (n & 1) * C::TILEB; };
-    auto sslot = [&](int n) { return (float *)(lds + STATS + (n & 1) * 256); };
-    // Statistics of the next tile travel through registers (loaded at the start of a step,
-    // written to LDS at its end) so that no wait for them sits in the step.
-    float nl = 0.f, nd = 0.f;
-    auto load_stats = [&](int t) {
-        const int row = t * BN + (lane & 31);
-        nl = 0.f;
-        nd = 0.f;
-        if (wave == 0 && row < Nq) {  // rows past Nq: L = 0, D = 0 (their dO is zero)
-            nl = Lrow[(size_t)bh * Nq + row];
-            nd = Drow[(size_t)bh * Nq + row];
-        }
+    const float *stb = ST + (size_t)bh * nt32 * 64;
+    auto qslot = [&](int n) { return lds + (n % NS) * C::TILEB; };
+    auto gslot = [&](int n) { return lds + C::VREG + (n % NS) * C::TILEB; };
+    auto sslot = [&](int n) { return lds + C::LDS_BYTES + (n % NS) * kStatsBytes; };
+    // Tile n of the stream (rows (t0 + n) * 32 ..): its Q and dO share of this wave, and the
+    // tile's statistics (every wave loads the same 256 bytes to the same place, so each
+    // wave's own wait covers them). Every step issues a load so that every wait has the same
+    // count; past the last tile the loads have an empty range (they only write zeros into
+    // the slot of a tile already consumed) and touch no memory.
+    auto load = [&](int n) {
+        const bool real = n < ntl;
+        const int row0 = real ? (t0 + n) * BN : Nq;
+        issue_kv<C>(qb, gb, off, row0, Nq, qslot(n), gslot(n), wave);
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(stb + (real ? (size_t)(t0 + n) * 64 : 0)), (short)0,
+            real ? kStatsBytes : 0, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void *)sslot(n), 4, lane * 4, 0, 0, 0);
+#endif
     };
-    auto store_stats = [&](int n) {
-        if (wave == 0 && lane < 32) {
-            sslot(n)[lane] = nl;
-            sslot(n)[32 + lane] = nd;
-        }
-    };
+    constexpr int kAhead = (NS - 2) * (LPW + 1);  // loads of the tiles after the next one
 
-    if (t1 > t0) {
-        issue_kv<C>(qb, gb, off, t0 * BN, Nq, qslot(0), gslot(0), wave);
-        load_stats(t0);
-        __builtin_amdgcn_s_waitcnt(0);
-        store_stats(0);
-        __syncthreads();
-    }
-    for (int t = t0, n = 0; t < t1; ++t, ++n) {
-        if (t + 1 < t1) {
-            issue_kv<C>(qb, gb, off, (t + 1) * BN, Nq, qslot(n + 1), gslot(n + 1), wave);
-            load_stats(t + 1);
-        }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) load(j);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile 0, the K and V rows
+    ring_barrier();
+
+    for (int n = 0; n < ntl; ++n) {
+        load(n + NS - 1);
         const char *qt = qslot(n), *gt = gslot(n);
-        const float *st = sslot(n);
-        // S = Q K^T and dP = dO V^T: lane (g, key) holds rows 8(e/4) + 4g + e%4.
-        f32x16 s = {}, dp = {};
+        const float *st = (const float *)sslot(n);
+        const int ip0 = (t0 + n) * BN + delta;  // absolute position of the tile's row 0
+
+        // Fragment reads run one step ahead of their MFMAs; the scheduling barriers keep the
+        // compiler from hoisting all of them (which would need more registers than exist).
+        f32x16 s[2], dp[2];
+        {
+            s16x8 a = *(const s16x8 *)(qt + kofs[0]);
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            s = Op::mma(*(const s16x8 *)(qt + kofs[kk]), kf[kk], s);
-            dp = Op::mma(*(const s16x8 *)(gt + kofs[kk]), vf[kk], dp);
+            for (int kk = 0; kk < NKK; ++kk) {
+                const s16x8 an = *(const s16x8 *)(qt + kofs[(kk + 1) % NKK]);
+                s[0] = Op::mma(a, kf[0][kk], kk == 0 ? f32x16{} : s[0]);
+                s[1] = Op::mma(a, kf[1][kk], kk == 0 ? f32x16{} : s[1]);
+                a = an;
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        f32x4 lv[4], dv4[4];
+        const bool full = block_visible<MASK>(ip0, ip0 + BN - 1, kw, kw + 63, W, G);
+        int lo[2] = {INT_MIN, INT_MIN}, hi[2] = {INT_MAX, INT_MAX};
+        if (MASK != 0 && !full) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            lv[q] = *(const f32x4 *)(st + 8 * q + 4 * g);
-            dv4[q] = *(const f32x4 *)(st + 32 + 8 * q + 4 * g);
+            for (int h = 0; h < 2; ++h)
+                key_row_range<MASK>(kw + 32 * h + li, ip0 + 4 * g, W, G, lo[h], hi[h]);
         }
-        const int row0 = t * BN + (Nkv - Nq);  // absolute position of tile row 0
+        // dP = dO V^T; P = 2^(c S - L) is formed alongside, two elements of each half per
+        // step, so that one wave keeps its matrix and vector units busy together.
+        {
+            f32x4 lv[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = 8 * (e >> 2) + 4 * g + (e & 3);
-            float p = fast_exp2(__builtin_fmaf(s[e], c, -lv[e >> 2][e & 3]));
-            if (MASK != 0 && !key_visible<MASK>(row0 + r, key, W, G)) p = 0.f;
-            s[e] = p;
-            dp[e] = p * (dp[e] - dv4[e >> 2][e & 3]);
+            for (int q = 0; q < 4; ++q) lv[q] = *(const f32x4 *)(st + 8 * q + 4 * g);
+            s16x8 a = *(const s16x8 *)(gt + kofs[0]);
+            s16x8 v0 = *(const s16x8 *)(vw + kofs[0]);
+            s16x8 v1 = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[0]);
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int kn = (kk + 1) % NKK;
+                const s16x8 an = *(const s16x8 *)(gt + kofs[kn]);
+                const s16x8 v0n = *(const s16x8 *)(vw + kofs[kn]);
+                const s16x8 v1n = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[kn]);
+                dp[0] = Op::mma(a, v0, kk == 0 ? f32x16{} : dp[0]);
+                dp[1] = Op::mma(a, v1, kk == 0 ? f32x16{} : dp[1]);
+#pragma unroll
+                for (int e = 16 * kk / NKK; e < 16 * (kk + 1) / NKK; ++e) {
+                    const int r = 8 * (e >> 2) + (e & 3);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float p =
+                            fast_exp2(__builtin_fmaf(s[h][e], c, -lv[e >> 2][e & 3]));
+                        s[h][e] = (MASK == 0 || (r >= lo[h] && r <= hi[h])) ? p : 0.f;
+                    }
+                }
+                a = an;
+                v0 = v0n;
+                v1 = v1n;
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over two 16-row chunks.
+        // dV^T += dO^T P; dS = P (dP - D) is formed alongside.
+        {
+            f32x4 dv4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dv4[q] = *(const f32x4 *)(st + 32 + 8 * q + 4 * g);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const int o8 = 8 * kc;
+                s16x8 pf[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    pf[h] = Op::pack8(s[h][o8], s[h][o8 + 1], s[h][o8 + 2], s[h][o8 + 3],
+                                      s[h][o8 + 4], s[h][o8 + 5], s[h][o8 + 6], s[h][o8 + 7]);
+                const char *p0 = gt + kc * 16 * C::ROWB;
+                s16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][0]));
+                s16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][0]));
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int dn = (db + 1) % NDB;
+                    const s16x4 lon = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][dn]));
+                    const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
+                    const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    mma_agpr<T>(dvt[0][db], ta, pf[0]);
+                    mma_agpr<T>(dvt[1][db], ta, pf[1]);
+#pragma unroll
+                    for (int e = o8 + 8 * db / NDB; e < o8 + 8 * (db + 1) / NDB; ++e)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            dp[h][e] = s[h][e] * (dp[h][e] - dv4[e >> 2][e & 3]);
+                    tlo = lon;
+                    thi = hin;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        // dK^T += Q^T dS
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             const int o8 = 8 * kc;
-            const s16x8 pf = Op::pack8(s[o8], s[o8 + 1], s[o8 + 2], s[o8 + 3], s[o8 + 4],
-                                       s[o8 + 5], s[o8 + 6], s[o8 + 7]);
-            const s16x8 sf = Op::pack8(dp[o8], dp[o8 + 1], dp[o8 + 2], dp[o8 + 3], dp[o8 + 4],
-                                       dp[o8 + 5], dp[o8 + 6], dp[o8 + 7]);
+            s16x8 sf[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                sf[h] = Op::pack8(dp[h][o8], dp[h][o8 + 1], dp[h][o8 + 2], dp[h][o8 + 3],
+                                  dp[h][o8 + 4], dp[h][o8 + 5], dp[h][o8 + 6], dp[h][o8 + 7]);
+            const char *p0 = qt + kc * 16 * C::ROWB;
+            s16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][0]));
+            s16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][0]));
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int base = kc * 16 * C::ROWB;
-                const s16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(gt + base + tro[0][db]));
-                const s16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(gt + base + tro[1][db]));
-                dvt[db] = Op::mma(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7), pf,
-                                  dvt[db]);
-                const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(qt + base + tro[0][db]));
-                const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(qt + base + tro[1][db]));
-                dkt[db] = Op::mma(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sf,
-                                  dkt[db]);
+                const int dn = (db + 1) % NDB;
+                const s16x4 lon = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][dn]));
+                const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
+                const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
+                mma_agpr<T>(dkt[0][db], ta, sf[0]);
+                mma_agpr<T>(dkt[1][db], ta, sf[1]);
+                tlo = lon;
+                thi = hin;
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        if (t + 1 < t1) store_stats(n + 1);
-        __syncthreads();
+        // tile n + 1 resident (the NS - 2 tiles after it may still be in flight), then publish
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));
+        ring_barrier();
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still write this LDS at exit
+    // The last matrix results must be complete before vector reads of them (19 wait states
+    // for a 16-pass MFMA; the inline MFMAs are invisible to the compiler's hazard checks).
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_nop 7");
+    __asm__ volatile("s_nop 7");
+    __asm__ volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
 
     // dK^T / dV^T: lane (g, key) holds columns db*32 + 8(e/4) + 4g + e%4.
-    if (key < Nkv) {
-        uint16_t *krow = dK + kvbase + (size_t)key * D;
-        uint16_t *vrow = dV + kvbase + (size_t)key * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int h = 0; h < 2; ++h) {
+        const int key = kw + 32 * h + li;
+        if (key < Nkv) {
+            uint16_t *krow = dK + kvbase + (size_t)key * D;
+            uint16_t *vrow = dV + kvbase + (size_t)key * D;
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                *(s16x4 *)(krow + db * 32 + 8 * blk + 4 * g) =
-                    Op::pack4(dkt[db][4 * blk] * scale, dkt[db][4 * blk + 1] * scale,
-                              dkt[db][4 * blk + 2] * scale, dkt[db][4 * blk + 3] * scale);
-                *(s16x4 *)(vrow + db * 32 + 8 * blk + 4 * g) =
-                    Op::pack4(dvt[db][4 * blk], dvt[db][4 * blk + 1], dvt[db][4 * blk + 2],
-                              dvt[db][4 * blk + 3]);
-            }
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk) {
+                    *(s16x4 *)(krow + db * 32 + 8 * blk + 4 * g) = Op::pack4(
+                        dkt[h][db][4 * blk] * scale, dkt[h][db][4 * blk + 1] * scale,
+                        dkt[h][db][4 * blk + 2] * scale, dkt[h][db][4 * blk + 3] * scale);
+                    *(s16x4 *)(vrow + db * 32 + 8 * blk + 4 * g) =
+                        Op::pack4(dvt[h][db][4 * blk], dvt[h][db][4 * blk + 1],
+                                  dvt[h][db][4 * blk + 2], dvt[h][db][4 * blk + 3]);
+                }
+        }
     }
 }
 
@@ -267,10 +448,10 @@ template <typename T, int D, int MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ Drow, const float *__restrict__ Lrow, uint16_t *__restrict__ dQ,
-    int Nq, int Nkv, float c, float scale, int W, int G, int nqt)
+    const float *__restrict__ ST, uint16_t *__restrict__ dQ, int Nq, int Nkv, float c,
+    float scale, int W, int G, int nqt, int nt32)
 {
-    using C = CfgBD<D>;
+    using C = CfgSP<D, 2, 4>;
     using Op = Ops16<T>;
     constexpr int BM = 128, BN = 32, NKK = C::NKK, NDB = C::NDB;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
@@ -295,8 +476,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             qf[kk] = gf[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
     }
-    const float lrow = row < Nq ? Lrow[(size_t)bh * Nq + row] : INFINITY;
-    const float drow = row < Nq ? Drow[(size_t)bh * Nq + row] : 0.f;
+    const float lrow = row < Nq ? ST[stats_index(bh, nt32, row)] : INFINITY;
+    const float drow = row < Nq ? ST[stats_index(bh, nt32, row) + 32] : 0.f;
 
     const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);
     const int ntl = sch.total, nint = sch.interior;
@@ -384,36 +565,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 template <typename T, int D, int MASK>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s)
 {
-    using C = CfgBD<D>;
-    const long rows = (long)a.B * a.H * a.Nq;
-    float *drow = (float *)a.workspace;
-    float *lrow = drow + rows;
-    hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256),
-                       0, s, (const uint16_t *)a.o, (const uint16_t *)a.dout, a.lse, drow, lrow,
-                       rows);
+    const int nt32 = (a.Nq + 31) / 32;
+    const long padded = (long)a.B * a.H * nt32 * 32;
+    float *st = (float *)a.workspace;
+    hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((padded + 15) / 16)),
+                       dim3(256), 0, s, (const uint16_t *)a.o, (const uint16_t *)a.dout, a.lse,
+                       st, a.Nq, nt32, padded);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float c = a.scale * kLog2e;
-    const int nkt = (a.Nkv + 127) / 128;
-    const int lds_a = C::LDS_BYTES + 512;
+    using CA = CfgBD<D>;
+    const int nkt = (a.Nkv + 255) / 256;
+    const int lds_a = CA::LDS_BYTES + kBwdStages * kStatsBytes + 256 * CA::ROWB;
     auto ka = bwd_dkdv_kernel<T, D, MASK>;
     e = hipFuncSetAttribute((const void *)ka, hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ka, dim3((unsigned)((long)nkt * a.B * a.H)), dim3(256), lds_a, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       (const uint16_t *)a.dout, drow, lrow, (uint16_t *)a.dk, (uint16_t *)a.dv,
-                       a.Nq, a.Nkv, c, a.scale, a.window, a.n_global, nkt);
+                       (const uint16_t *)a.dout, st, (uint16_t *)a.dk, (uint16_t *)a.dv, a.Nq,
+                       a.Nkv, c, a.scale, a.window, a.n_global, nkt, nt32);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    using CB = CfgSP<D, 2, 4>;
     const int nqt = (a.Nq + 127) / 128;
     auto kb = bwd_dq_kernel<T, D, MASK>;
     e = hipFuncSetAttribute((const void *)kb, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            C::LDS_BYTES);
+                            CB::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kb, dim3((unsigned)((long)nqt * a.B * a.H)), dim3(256), C::LDS_BYTES, s,
+    hipLaunchKernelGGL(kb, dim3((unsigned)((long)nqt * a.B * a.H)), dim3(256), CB::LDS_BYTES, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       (const uint16_t *)a.dout, drow, lrow, (uint16_t *)a.dq, a.Nq, a.Nkv, c,
-                       a.scale, a.window, a.n_global, nqt);
+                       (const uint16_t *)a.dout, st, (uint16_t *)a.dq, a.Nq, a.Nkv, c, a.scale,
+                       a.window, a.n_global, nqt, nt32);
     return hipGetLastError();
 }
 

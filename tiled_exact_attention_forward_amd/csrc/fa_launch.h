@@ -78,12 +78,14 @@ struct BwdArgs {
     int B, H, Nq, Nkv, d;
     float scale;
     int mask, window, n_global, dtype;
-    void *workspace;  // 2 * B * H * Nq floats: D = rowsum(dO o O), then log2-domain LSE
+    void *workspace;  // backward_workspace_floats(B, H, Nq) floats of row statistics
 };
 
+// Row statistics of the backward: per 32-row tile of each (b, h), 32 log2-scaled LSE values
+// then 32 values of D = rowsum(dO o O).
 inline size_t backward_workspace_floats(int B, int H, int Nq)
 {
-    return 2 * (size_t)B * H * Nq;
+    return (size_t)B * H * (size_t)((Nq + 31) / 32) * 64;
 }
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
