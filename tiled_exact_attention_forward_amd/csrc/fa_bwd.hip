@@ -165,6 +165,135 @@ __device__ __forceinline__ bool block_visible(int i0, int i1, int k0, int k1, in
     return k1 <= i0 || k1 < G;
 }
 
+// One 32-row tile of the dK/dV kernel for this wave's 64 keys: qt, gt and st are the tile's
+// Q, dO and statistics in LDS, vw the wave's V rows. The pointers are restrict-qualified:
+// nothing else in the step touches that memory, which also tells the compiler that the
+// loads of later tiles into other slots, still in flight, cannot overlap these reads.
+template <typename T, typename C, int MASK>
+__device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const char *__restrict__ gt,
+                                          const char *__restrict__ vw,
+                                          const float *__restrict__ st,
+                                          const s16x8 (&kf)[2][C::NKK],
+                                          f32x16 (&dkt)[2][C::NDB], f32x16 (&dvt)[2][C::NDB],
+                                          const int (&kofs)[C::NKK], const int (&tro)[2][C::NDB],
+                                          float c, int ip0, int kw, int li, int g, int W, int G)
+{
+    using Op = Ops16<T>;
+    constexpr int BN = 32, NKK = C::NKK, NDB = C::NDB;
+    f32x16 s[2], dp[2];
+    {
+        // all Q fragments first, then both halves' MFMAs, which share each fragment
+        s16x8 a[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) a[kk] = *(const s16x8 *)(qt + kofs[kk]);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            s[0] = Op::mma(a[kk], kf[0][kk], kk == 0 ? f32x16{} : s[0]);
+            s[1] = Op::mma(a[kk], kf[1][kk], kk == 0 ? f32x16{} : s[1]);
+        }
+    }
+    const bool full = block_visible<MASK>(ip0, ip0 + BN - 1, kw, kw + 63, W, G);
+    int lo[2] = {INT_MIN, INT_MIN}, hi[2] = {INT_MAX, INT_MAX};
+    if (MASK != 0 && !full) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            key_row_range<MASK>(kw + 32 * h + li, ip0 + 4 * g, W, G, lo[h], hi[h]);
+    }
+    // dP = dO V^T; P = 2^(c S - L) is formed alongside, two elements of each half per
+    // step, so that one wave keeps its matrix and vector units busy together.
+    {
+        f32x4 lv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lv[q] = *(const f32x4 *)(st + 8 * q + 4 * g);
+        s16x8 a = *(const s16x8 *)(gt + kofs[0]);
+        s16x8 v0 = *(const s16x8 *)(vw + kofs[0]);
+        s16x8 v1 = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[0]);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int kn = (kk + 1) % NKK;
+            const s16x8 an = *(const s16x8 *)(gt + kofs[kn]);
+            const s16x8 v0n = *(const s16x8 *)(vw + kofs[kn]);
+            const s16x8 v1n = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[kn]);
+            dp[0] = Op::mma(a, v0, kk == 0 ? f32x16{} : dp[0]);
+            dp[1] = Op::mma(a, v1, kk == 0 ? f32x16{} : dp[1]);
+#pragma unroll
+            for (int e = 16 * kk / NKK; e < 16 * (kk + 1) / NKK; ++e) {
+                const int r = 8 * (e >> 2) + (e & 3);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float p =
+                        fast_exp2(__builtin_fmaf(s[h][e], c, -lv[e >> 2][e & 3]));
+                    s[h][e] = (MASK == 0 || (r >= lo[h] && r <= hi[h])) ? p : 0.f;
+                }
+            }
+            a = an;
+            v0 = v0n;
+            v1 = v1n;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // dV^T += dO^T P; dS = P (dP - D) is formed alongside.
+    {
+        f32x4 dv4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dv4[q] = *(const f32x4 *)(st + 32 + 8 * q + 4 * g);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int o8 = 8 * kc;
+            s16x8 pf[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                pf[h] = Op::pack8(s[h][o8], s[h][o8 + 1], s[h][o8 + 2], s[h][o8 + 3],
+                                  s[h][o8 + 4], s[h][o8 + 5], s[h][o8 + 6], s[h][o8 + 7]);
+            const char *p0 = gt + kc * 16 * C::ROWB;
+            s16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][0]));
+            s16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][0]));
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int dn = (db + 1) % NDB;
+                const s16x4 lon = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][dn]));
+                const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
+                const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
+                mma_agpr<T>(dvt[0][db], ta, pf[0]);
+                mma_agpr<T>(dvt[1][db], ta, pf[1]);
+#pragma unroll
+                for (int e = o8 + 8 * db / NDB; e < o8 + 8 * (db + 1) / NDB; ++e)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        dp[h][e] = s[h][e] * (dp[h][e] - dv4[e >> 2][e & 3]);
+                tlo = lon;
+                thi = hin;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    // dK^T += Q^T dS
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int o8 = 8 * kc;
+        s16x8 sf[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            sf[h] = Op::pack8(dp[h][o8], dp[h][o8 + 1], dp[h][o8 + 2], dp[h][o8 + 3],
+                              dp[h][o8 + 4], dp[h][o8 + 5], dp[h][o8 + 6], dp[h][o8 + 7]);
+        const char *p0 = qt + kc * 16 * C::ROWB;
+        s16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][0]));
+        s16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][0]));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int dn = (db + 1) % NDB;
+            const s16x4 lon = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][dn]));
+            const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
+            const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
+            mma_agpr<T>(dkt[0][db], ta, sf[0]);
+            mma_agpr<T>(dkt[1][db], ta, sf[1]);
+            tlo = lon;
+            thi = hin;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // dK and dV. A workgroup owns 256 keys, 64 per wave in two 32-key halves. K fragments stay in
 // registers and V rows in LDS (64 KB, loaded once; registers go to the dK/dV accumulators);
 // each Q or dO fragment read from LDS feeds both halves, which halves the LDS reads per
@@ -295,120 +424,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const float *st = (const float *)sslot(n);
         const int ip0 = (t0 + n) * BN + delta;  // absolute position of the tile's row 0
 
-        // Fragment reads run one step ahead of their MFMAs; the scheduling barriers keep the
-        // compiler from hoisting all of them (which would need more registers than exist).
-        f32x16 s[2], dp[2];
-        {
-            s16x8 a = *(const s16x8 *)(qt + kofs[0]);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const s16x8 an = *(const s16x8 *)(qt + kofs[(kk + 1) % NKK]);
-                s[0] = Op::mma(a, kf[0][kk], kk == 0 ? f32x16{} : s[0]);
-                s[1] = Op::mma(a, kf[1][kk], kk == 0 ? f32x16{} : s[1]);
-                a = an;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        const bool full = block_visible<MASK>(ip0, ip0 + BN - 1, kw, kw + 63, W, G);
-        int lo[2] = {INT_MIN, INT_MIN}, hi[2] = {INT_MAX, INT_MAX};
-        if (MASK != 0 && !full) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                key_row_range<MASK>(kw + 32 * h + li, ip0 + 4 * g, W, G, lo[h], hi[h]);
-        }
-        // dP = dO V^T; P = 2^(c S - L) is formed alongside, two elements of each half per
-        // step, so that one wave keeps its matrix and vector units busy together.
-        {
-            f32x4 lv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) lv[q] = *(const f32x4 *)(st + 8 * q + 4 * g);
-            s16x8 a = *(const s16x8 *)(gt + kofs[0]);
-            s16x8 v0 = *(const s16x8 *)(vw + kofs[0]);
-            s16x8 v1 = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[0]);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int kn = (kk + 1) % NKK;
-                const s16x8 an = *(const s16x8 *)(gt + kofs[kn]);
-                const s16x8 v0n = *(const s16x8 *)(vw + kofs[kn]);
-                const s16x8 v1n = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[kn]);
-                dp[0] = Op::mma(a, v0, kk == 0 ? f32x16{} : dp[0]);
-                dp[1] = Op::mma(a, v1, kk == 0 ? f32x16{} : dp[1]);
-#pragma unroll
-                for (int e = 16 * kk / NKK; e < 16 * (kk + 1) / NKK; ++e) {
-                    const int r = 8 * (e >> 2) + (e & 3);
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const float p =
-                            fast_exp2(__builtin_fmaf(s[h][e], c, -lv[e >> 2][e & 3]));
-                        s[h][e] = (MASK == 0 || (r >= lo[h] && r <= hi[h])) ? p : 0.f;
-                    }
-                }
-                a = an;
-                v0 = v0n;
-                v1 = v1n;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // dV^T += dO^T P; dS = P (dP - D) is formed alongside.
-        {
-            f32x4 dv4[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dv4[q] = *(const f32x4 *)(st + 32 + 8 * q + 4 * g);
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const int o8 = 8 * kc;
-                s16x8 pf[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    pf[h] = Op::pack8(s[h][o8], s[h][o8 + 1], s[h][o8 + 2], s[h][o8 + 3],
-                                      s[h][o8 + 4], s[h][o8 + 5], s[h][o8 + 6], s[h][o8 + 7]);
-                const char *p0 = gt + kc * 16 * C::ROWB;
-                s16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][0]));
-                s16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][0]));
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int dn = (db + 1) % NDB;
-                    const s16x4 lon = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][dn]));
-                    const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
-                    const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    mma_agpr<T>(dvt[0][db], ta, pf[0]);
-                    mma_agpr<T>(dvt[1][db], ta, pf[1]);
-#pragma unroll
-                    for (int e = o8 + 8 * db / NDB; e < o8 + 8 * (db + 1) / NDB; ++e)
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            dp[h][e] = s[h][e] * (dp[h][e] - dv4[e >> 2][e & 3]);
-                    tlo = lon;
-                    thi = hin;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-        // dK^T += Q^T dS
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            const int o8 = 8 * kc;
-            s16x8 sf[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                sf[h] = Op::pack8(dp[h][o8], dp[h][o8 + 1], dp[h][o8 + 2], dp[h][o8 + 3],
-                                  dp[h][o8 + 4], dp[h][o8 + 5], dp[h][o8 + 6], dp[h][o8 + 7]);
-            const char *p0 = qt + kc * 16 * C::ROWB;
-            s16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][0]));
-            s16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][0]));
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int dn = (db + 1) % NDB;
-                const s16x4 lon = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[0][dn]));
-                const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
-                const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
-                mma_agpr<T>(dkt[0][db], ta, sf[0]);
-                mma_agpr<T>(dkt[1][db], ta, sf[1]);
-                tlo = lon;
-                thi = hin;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        dkdv_step<T, C, MASK>(qt, gt, vw, st, kf, dkt, dvt, kofs, tro, c, ip0, kw, li, g, W, G);
         // tile n + 1 resident (the NS - 2 tiles after it may still be in flight), then publish
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));
         ring_barrier();
