@@ -429,7 +429,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));
         ring_barrier();
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still write this LDS at exit
+    // Every wave's loads (the empty ones past the last tile included) have landed before any
+    // wave reuses the ring for the output rows, and before the workgroup exits.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
     // The last matrix results must be complete before vector reads of them (19 wait states
     // for a 16-pass MFMA; the inline MFMAs are invisible to the compiler's hazard checks).
     __builtin_amdgcn_sched_barrier(0);
@@ -438,25 +441,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __asm__ volatile("s_nop 7");
     __builtin_amdgcn_sched_barrier(0);
 
-    // dK^T / dV^T: lane (g, key) holds columns db*32 + 8(e/4) + 4g + e%4.
+    // dK^T / dV^T: lane (g, key) holds columns db*32 + 8(e/4) + 4g + e%4. Rows go out
+    // through LDS (this wave's 64 rows, padded by 16 bytes against bank conflicts; the ring
+    // is free after the last barrier) so that each store writes whole 256-byte rows: stores
+    // of 16 bytes per row, all waves of the chip finishing together, left partly written
+    // lines for the L2 to evict and write back more than once.
+    constexpr int RP = C::ROWB + 16;
+    static_assert(4 * 64 * RP <= C::LDS_BYTES + NS * kStatsBytes + 256 * C::ROWB, "staging");
+    char *const stg = lds + wave * 64 * RP;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int key = kw + 32 * h + li;
-        if (key < Nkv) {
-            uint16_t *krow = dK + kvbase + (size_t)key * D;
-            uint16_t *vrow = dV + kvbase + (size_t)key * D;
+    for (int t = 0; t < 2; ++t) {  // dK, then dV
+        uint16_t *dst = (t == 0 ? dK : dV) + kvbase;
+        const float f = t == 0 ? scale : 1.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int blk = 0; blk < 4; ++blk) {
-                    *(s16x4 *)(krow + db * 32 + 8 * blk + 4 * g) = Op::pack4(
-                        dkt[h][db][4 * blk] * scale, dkt[h][db][4 * blk + 1] * scale,
-                        dkt[h][db][4 * blk + 2] * scale, dkt[h][db][4 * blk + 3] * scale);
-                    *(s16x4 *)(vrow + db * 32 + 8 * blk + 4 * g) =
-                        Op::pack4(dvt[h][db][4 * blk], dvt[h][db][4 * blk + 1],
-                                  dvt[h][db][4 * blk + 2], dvt[h][db][4 * blk + 3]);
+                    const f32x16 &acc = t == 0 ? dkt[h][db] : dvt[h][db];
+                    *(s16x4 *)(stg + (32 * h + li) * RP + 2 * (db * 32 + 8 * blk + 4 * g)) =
+                        Op::pack4(acc[4 * blk] * f, acc[4 * blk + 1] * f, acc[4 * blk + 2] * f,
+                                  acc[4 * blk + 3] * f);
                 }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
+        __asm__ volatile("" ::: "memory");
+        constexpr int PER_ROW = C::ROWB / 16;  // 16-byte pieces of a row
+#pragma unroll
+        for (int it = 0; it < 64 * PER_ROW / 64; ++it) {
+            const int i = it * 64 + lane, r = i / PER_ROW, cpos = i % PER_ROW;
+            const s16x8 val = *(const s16x8 *)(stg + r * RP + 16 * cpos);
+            if (kw + r < Nkv) *(s16x8 *)(dst + (size_t)(kw + r) * D + 8 * cpos) = val;
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next tensor's writes
+        __asm__ volatile("" ::: "memory");
     }
 }
 
