@@ -33,11 +33,14 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PAGES_BF16_TFLOPS = 1.25    # pages' Ascend 910 bf16 time for this workload, as TFLOP/s
-KERNEL_SOURCES = ["tiled_exact_attention_forward_amd/csrc/fa_device.h",
-                  "tiled_exact_attention_forward_amd/csrc/fa_fwd.hip",
-                  "tiled_exact_attention_forward_amd/csrc/fa_bwd.hip",
-                  "tiled_exact_attention_forward_amd/csrc/fa_decode.hip",
-                  "tiled_exact_attention_forward_amd/csrc/fa_merge.hip"]
+CSRC = "tiled_exact_attention_forward_amd/csrc/"
+# Sources each measured kernel is compiled from (its traffic entry is valid for these only).
+KERNEL_SOURCES = {
+    "fwd": [CSRC + "fa_device.h", CSRC + "fa_fwd.hip"],
+    "bwd": [CSRC + "fa_device.h", CSRC + "fa_bwd.hip"],
+    "decode": [CSRC + "fa_launch.h", CSRC + "fa_decode.hip"],
+    "merge": [CSRC + "fa_device.h", CSRC + "fa_merge.hip"],
+}
 
 
 # ----------------------------------------------------------------- accounting
@@ -94,25 +97,36 @@ def decode_bytes(w, seq_lens, elem):
     return 2 * keys * w["H"] * w["d"] * elem + 2 * w["S"] * w["H"] * w["d"] * elem + 4 * w["S"] * w["H"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(group=None):
+    """Hash of the sources of one kernel group (all groups when None)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    groups = [group] if group else sorted(KERNEL_SOURCES)
+    for gname in groups:
+        for p in KERNEL_SOURCES[gname]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(kernel_key):
-    """HBM traffic per launch measured with rocprofv3 counters, if taken on this source."""
+    """HBM traffic per launch measured with rocprofv3 counters, if taken on the current
+    sources of that kernel (each entry records the hash of its own sources)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
-        return None
     e = t.get("kernels", {}).get(kernel_key)
-    return None if e is None else e.get("bytes_per_launch")
+    if e is None or e.get("source_hash") != kernel_source_hash(e.get("sources")):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def backward_traffic(workload):
+    """Summed counter-measured HBM bytes of the three backward kernels, when measured."""
+    parts = [load_traffic(f"bwd_{k}_bf16_d128{m}_{workload}")
+             for k, m in (("rowdot", ""), ("dkdv", "_mask0"), ("dq", "_mask0"))]
+    return None if any(p is None for p in parts) else sum(parts)
 
 
 # ----------------------------------------------------------------- timing
@@ -438,6 +452,7 @@ def main():
                 frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), visible_pairs=r["pairs"],
                 cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
                 cold_tflops=round(r["cold_tflops"], 2),
+                traffic=backward_traffic(name),
                 note="fa_backward (3 kernels); 10*d FLOPs per visible pair")
             print(f"[bench] backward {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
