@@ -254,8 +254,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
 
     const char *kbh = (const char *)(K + kvbase);
     const char *vbh = (const char *)(V + kvbase);
-    auto kslot = [&](int t) { return lds + (t % NS) * C::TILEB; };
-    auto vslot = [&](int t) { return lds + C::VREG + (t % NS) * C::TILEB; };
+    auto kslot = [&](int t) { return lds + ((unsigned)t % NS) * C::TILEB; };
+    auto vslot = [&](int t) { return lds + C::VREG + ((unsigned)t % NS) * C::TILEB; };
     // Load u of this wave fills rows r of the K (or V) tile; lane l lands in physical chunk
     // l % CHUNKS of row r = first + l / CHUNKS, so it fetches the logical chunk the swizzle
     // stores there. Offsets are relative to the tile's first key.
@@ -332,8 +332,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
             ld = sch.next(ld);
         }
     };
-    // Two steps per iteration so that sa and sb swap roles without register copies. Every
-    // step in the loop has a tile t+1; the last step is peeled.
+    // Steps come in pairs so that sa and sb swap roles without register copies, and the main
+    // loop takes four at a time (the ring depth) so that each step's ring slots are known at
+    // compile time and the LDS reads carry them as immediate offsets. Every step in the
+    // loops has a tile t+1; the last step is peeled.
     auto step = [&](int t, f32x16 &cur, f32x16 &nxt) {
         load_ahead(t);
         sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, true>(
@@ -349,6 +351,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     };
     if (ntl > 0) {
         int t = 0;
+        for (; t + 4 < ntl; t += 4) {
+            step(t, sa, sb);
+            step(t + 1, sb, sa);
+            step(t + 2, sa, sb);
+            step(t + 3, sb, sa);
+        }
         for (; t + 2 < ntl; t += 2) {
             step(t, sa, sb);
             step(t + 1, sb, sa);
