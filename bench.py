@@ -257,13 +257,19 @@ def bench_multimodal(name, steps, warmup, torch, fa, workloads, cold_calls=20):
     def unified():
         fa.fa_forward(q, k, v, scale, fa.FA_MASK_PREFIX_LM, 0, w["n_img"], out=o, lse=lse)
 
+    def fused():
+        fa.fa_multimodal_forward(qi, ki, vi, qt, kt, vt, scale,
+                                 text_mode=fa.FA_MULTIMODAL_FUSED)
+
     ms, wall = time_calls(split, steps, warmup, torch)
+    ms_f, _ = time_calls(fused, steps, warmup, torch)
     ms_u, _ = time_calls(unified, steps, warmup, torch)
     cold = time_cold(split, cold_calls, torch) if cold_calls else (ms, ms, ms)
     pairs = multimodal_pairs(w)
     flops = 4 * w["d"] * pairs
-    return dict(workload=name, w=w, ms=ms, wall_s=wall, ms_unified=ms_u, flops=flops,
-                pairs=pairs, tflops=flops / (ms * 1e-3) / 1e12,
+    return dict(workload=name, w=w, ms=ms, wall_s=wall, ms_unified=ms_u, ms_fused=ms_f,
+                flops=flops, pairs=pairs, tflops=flops / (ms * 1e-3) / 1e12,
+                tflops_fused=flops / (ms_f * 1e-3) / 1e12,
                 tflops_unified=flops / (ms_u * 1e-3) / 1e12, cold_ms=cold)
 
 
@@ -435,14 +441,16 @@ def main():
         others["multimodal_bf16"] = dict(
             us=round(r["ms"] * 1e3, 2), tflops=round(r["tflops"], 2),
             frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), visible_pairs=r["pairs"],
+            fused_us=round(r["ms_fused"] * 1e3, 2), fused_tflops=round(r["tflops_fused"], 2),
             unified_us=round(r["ms_unified"] * 1e3, 2),
             unified_tflops=round(r["tflops_unified"], 2),
-            split_speedup=round(r["ms_unified"] / r["ms"], 3),
             cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
-            note="three calls (image full, text causal, text to image) + LSE merge; unified_*: "
-                 "one prefix-LM call over [image; text]")
-        print(f"[bench] multimodal_bf16: split {r['ms'] * 1e3:.1f} us, unified "
-              f"{r['ms_unified'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+            note="us/tflops: three calls (image full, text causal, text to image) + LSE merge; "
+                 "fused_*: image call + one causal text call over [image; text] keys read from "
+                 "both tensors; unified_*: one prefix-LM call over concatenated [image; text]")
+        print(f"[bench] multimodal_bf16: split {r['ms'] * 1e3:.1f} us, fused "
+              f"{r['ms_fused'] * 1e3:.1f} us, unified {r['ms_unified'] * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
         del r
         for name in ("dense_bf16", "causal_bf16"):
             r = bench_backward(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch,

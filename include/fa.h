@@ -167,31 +167,40 @@ int fa_merge_lse(const void *o_a, const float *lse_a, const void *o_b, const flo
  * fa_multimodal_forward -- attention of image and text tokens with the multimodal pattern
  * of the "ascend-transformer-boost" article (场景四): image tokens attend to all image
  * tokens and no text; text tokens attend to all image tokens and causally to text tokens.
- * As the article does, this runs three regular attention calls, none with an irregular
- * mask, and merges by log-sum-exp:
- *   1. image queries x image keys, no mask        -> o_img, lse_img
- *   2. text queries x text keys, causal           -> o_txt, lse_txt
- *   3. text queries x image keys, no mask         -> workspace
- *   4. fa_merge_lse of 2 and 3 into o_txt, lse_txt.
- * The result equals (up to rounding) one call over [image; text] with FA_MASK_PREFIX_LM
- * and n_global = n_img.
+ * The article runs this as regular attention calls rather than one call with an irregular
+ * mask; text_mode picks how the text part is computed:
+ *  FA_MULTIMODAL_SPLIT_MERGE  the article's three calls, merged by log-sum-exp:
+ *     1. image queries x image keys, no mask        -> o_img, lse_img
+ *     2. text queries x text keys, causal           -> o_txt, lse_txt
+ *     3. text queries x image keys, no mask         -> workspace
+ *     4. fa_merge_lse of 2 and 3 into o_txt, lse_txt.
+ *  FA_MULTIMODAL_FUSED  call 1, then calls 2 and 3 as ONE causal launch over n_img + n_txt
+ *     keys whose key tiles come first from the image K/V and then from the text K/V (with
+ *     bottom-right alignment every text row sees all image keys and the text keys up to
+ *     itself): no merge, no workspace. Needs n_img % 32 == 0 and FA_F16 or FA_BF16
+ *     (FA_ERR_UNSUPPORTED otherwise).
+ * Both equal (up to rounding) one call over [image; text] with FA_MASK_PREFIX_LM and
+ * n_global = n_img.
  *
  *  q_img, k_img, v_img  [B, H, n_img, d] dtype;  q_txt, k_txt, v_txt  [B, H, n_txt, d]
  *  o_img [B, H, n_img, d], lse_img [B, H, n_img]; o_txt [B, H, n_txt, d],
  *  lse_txt [B, H, n_txt]: written (lse float32).
- *  workspace  at least fa_multimodal_workspace_bytes(B, H, n_txt, d, dtype) bytes,
- *             16-byte aligned, no initialisation needed (the text-to-image partial result).
+ *  workspace  (split-merge only; may be NULL when fused) at least
+ *             fa_multimodal_workspace_bytes(B, H, n_txt, d, dtype) bytes, 16-byte aligned,
+ *             no initialisation needed (the text-to-image partial result).
  *  Supported: as fa_forward for each call (d in {64, 128}; FA_F32, FA_F16, FA_BF16).
- *  All argument checks of the four steps run before the first launch; the four kernels
- *  are enqueued in order on `stream`.
+ *  All argument checks run before the first launch; the kernels are enqueued in order on
+ *  `stream`.
  */
+typedef enum { FA_MULTIMODAL_SPLIT_MERGE = 0, FA_MULTIMODAL_FUSED = 1 } fa_multimodal_mode;
+
 size_t fa_multimodal_workspace_bytes(int B, int H, int n_txt, int d, int dtype);
 
 int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_img,
                           const void *q_txt, const void *k_txt, const void *v_txt, void *o_img,
                           float *lse_img, void *o_txt, float *lse_txt, int B, int H, int n_img,
-                          int n_txt, int d, float scale, int dtype, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          int n_txt, int d, float scale, int dtype, int text_mode,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Paged single-token decode ("ascend-transformer-boost" article, 场景二: KV cache split

@@ -188,12 +188,12 @@ def test_merge_rejects_before_launch(kw, status):
 
 
 def mm(qi=P, ki=P, vi=P, qt=P, kt=P, vt=P, oi=P, li=P, ot=P, lt=P, B=1, H=2, ni=9, nt=14, d=64,
-       scale=0.1, dtype=2, ws=P, wsb=None):
+       scale=0.1, dtype=2, mode=0, ws=P, wsb=None):
     lib = fa.load_library()
     if wsb is None:
         wsb = lib.fa_multimodal_workspace_bytes(B, H, nt, d, dtype)
     return lib.fa_multimodal_forward(qi, ki, vi, qt, kt, vt, oi, li, ot, lt, B, H, ni, nt, d,
-                                     scale, dtype, ws, wsb, None)
+                                     scale, dtype, mode, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -202,7 +202,9 @@ def mm(qi=P, ki=P, vi=P, qt=P, kt=P, vt=P, oi=P, li=P, ot=P, lt=P, B=1, H=2, ni=
     (dict(d=80), fa.FA_ERR_UNSUPPORTED), (dict(dtype=9), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=N), fa.FA_ERR_WORKSPACE), (dict(wsb=64), fa.FA_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x1001)), fa.FA_ERR_WORKSPACE),
-    (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE), (dict(mode=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(mode=1, ni=33), fa.FA_ERR_UNSUPPORTED), (dict(mode=1, ni=64, dtype=0),
+                                                   fa.FA_ERR_UNSUPPORTED),
 ])
 def test_multimodal_rejects_before_launch(kw, status):
     assert mm(**kw) == status

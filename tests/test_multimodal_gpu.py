@@ -62,11 +62,11 @@ def test_merge_lse(dtype, d, rows):
     assert torch.equal(a, o) and torch.equal(al, lse)
 
 
-def run_mm(inp):
+def run_mm(inp, mode=fa.FA_MULTIMODAL_SPLIT_MERGE):
     names = ("q_img", "k_img", "v_img", "q_txt", "k_txt", "v_txt")
     dev = to_dev(*(inp[n] for n in names))
     d = inp["q_img"].shape[-1]
-    out = fa.fa_multimodal_forward(*dev, workloads.default_scale(d))
+    out = fa.fa_multimodal_forward(*dev, workloads.default_scale(d), text_mode=mode)
     torch.cuda.synchronize()
     return out, dev
 
@@ -96,9 +96,34 @@ def test_multimodal_small(dtype, d, shape):
     check(ot, lt, f64(o1[:, :, ni:]), f64(l1[:, :, ni:]), dtype, "text vs one call")
 
 
+FUSED_SHAPES = [(1, 1, 64, 1), (2, 2, 32, 50), (1, 3, 576, 300), (1, 2, 128, 257),
+                (1, 2, 96, 33), (1, 1, 32, 1000)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_multimodal_fused_small(dtype, d, shape):
+    """Fused text call (keys read from the image and the text tensors in one launch) against
+    the oracle, and against the article's three-call split with its merge."""
+    B, H, ni, nt = shape
+    seed = zlib.crc32(repr(("mmf", dtype, d, shape)).encode()) % 100000
+    inp = workloads.gen_multimodal(B, H, ni, nt, d, dtype, seed)
+    (oi, li, ot, lt), _ = run_mm(inp, fa.FA_MULTIMODAL_FUSED)
+    scale = workloads.default_scale(d)
+    roi, rli, rot, rlt = oracle.multimodal(inp["q_img"], inp["k_img"], inp["v_img"],
+                                           inp["q_txt"], inp["k_txt"], inp["v_txt"], scale)
+    check(oi, li, roi, rli, dtype, f"fused image {dtype} d{d} {shape}")
+    check(ot, lt, rot, rlt, dtype, f"fused text {dtype} d{d} {shape}")
+    (si, sli, so, slt), _ = run_mm(inp, fa.FA_MULTIMODAL_SPLIT_MERGE)
+    assert torch.equal(oi, si) and torch.equal(li, sli)  # the image call is the same launch
+    check(ot, lt, f64(so), f64(slt), dtype, "fused text vs split")
+
+
 def test_multimodal_full_size():
     w, inp = workloads.gen_workload("multimodal_bf16")
     (oi, li, ot, lt), _ = run_mm(inp)
+    (fi, fli, fo, flt), _ = run_mm(inp, fa.FA_MULTIMODAL_FUSED)
     scale = workloads.default_scale(w["d"])
     for b, h in ((0, 0), (3, 31), (1, 12)):
         sl = {k: v[b:b + 1, h:h + 1] for k, v in inp.items()}
@@ -106,3 +131,5 @@ def test_multimodal_full_size():
                                                sl["q_txt"], sl["k_txt"], sl["v_txt"], scale)
         check(oi[b:b + 1, h:h + 1], li[b:b + 1, h:h + 1], roi, rli, "bf16", f"image ({b},{h})")
         check(ot[b:b + 1, h:h + 1], lt[b:b + 1, h:h + 1], rot, rlt, "bf16", f"text ({b},{h})")
+        check(fo[b:b + 1, h:h + 1], flt[b:b + 1, h:h + 1], rot, rlt, "bf16",
+              f"fused text ({b},{h})")

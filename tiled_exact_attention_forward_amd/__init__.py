@@ -28,12 +28,14 @@ __all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_
            "fa_multimodal_workspace_bytes", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
            "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
-           "FA_MASK_WINDOW_GLOBAL", "FA_MASK_BAND", "FA_MASK_PREFIX_LM", "EXPORTED_SYMBOLS"]
+           "FA_MASK_WINDOW_GLOBAL", "FA_MASK_BAND", "FA_MASK_PREFIX_LM", "FA_MULTIMODAL_SPLIT_MERGE",
+           "FA_MULTIMODAL_FUSED", "EXPORTED_SYMBOLS"]
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
+FA_MULTIMODAL_SPLIT_MERGE, FA_MULTIMODAL_FUSED = 0, 1
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_backward",
                     "fa_backward_workspace_bytes", "fa_decode_paged", "fa_prefill_paged",
                     "fa_merge_lse", "fa_multimodal_forward", "fa_multimodal_workspace_bytes",
@@ -91,7 +93,7 @@ def load_library():
     lib.fa_multimodal_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_multimodal_workspace_bytes.restype = sz
     lib.fa_multimodal_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
-                                          f, i, vp, sz, vp]
+                                          f, i, i, vp, sz, vp]
     lib.fa_multimodal_forward.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -345,10 +347,12 @@ def fa_multimodal_workspace_bytes(B, H, n_txt, d, dtype_code):
                                                             int(dtype_code)))
 
 
-def fa_multimodal_forward(q_img, k_img, v_img, q_txt, k_txt, v_txt, scale=None, workspace=None,
-                          stream=None):
-    """Image/text attention (image sees image; text sees image and earlier text) as three
-    attention calls and a log-sum-exp merge. Inputs [B,H,n,d] on the GPU. Returns
+def fa_multimodal_forward(q_img, k_img, v_img, q_txt, k_txt, v_txt, scale=None,
+                          text_mode=FA_MULTIMODAL_SPLIT_MERGE, workspace=None, stream=None):
+    """Image/text attention (image sees image; text sees image and earlier text). text_mode
+    FA_MULTIMODAL_SPLIT_MERGE: three attention calls and a log-sum-exp merge;
+    FA_MULTIMODAL_FUSED: the image call and one causal call over [image; text] keys read from
+    the two tensors (n_img % 32 == 0, fp16/bf16). Inputs [B,H,n,d] on the GPU. Returns
     (o_img, lse_img, o_txt, lse_txt)."""
     torch = _torch()
     B, H, n_img, d = q_img.shape
@@ -365,17 +369,17 @@ def fa_multimodal_forward(q_img, k_img, v_img, q_txt, k_txt, v_txt, scale=None, 
     lse_txt = torch.empty((B, H, n_txt), dtype=torch.float32, device=q_img.device)
     code = _dtype_code(q_img)
     need = fa_multimodal_workspace_bytes(B, H, n_txt, d, code)
-    if workspace is None:
+    if workspace is None and text_mode == FA_MULTIMODAL_SPLIT_MERGE:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q_img.device)
     for name, t in (("q_img", q_img), ("k_img", k_img), ("v_img", v_img), ("q_txt", q_txt),
                     ("k_txt", k_txt), ("v_txt", v_txt)):
         _check_dev(name, t, q_img.dtype)
     _check_dev("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load_library().fa_multimodal_forward(
         _ptr(q_img), _ptr(k_img), _ptr(v_img), _ptr(q_txt), _ptr(k_txt), _ptr(v_txt),
         _ptr(o_img), _ptr(lse_img), _ptr(o_txt), _ptr(lse_txt), B, H, n_img, n_txt, d,
-        float(scale), code, _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream))
+        float(scale), code, int(text_mode), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != FA_OK:
         raise FaError(rc, "fa_multimodal_forward")
     return o_img, lse_img, o_txt, lse_txt

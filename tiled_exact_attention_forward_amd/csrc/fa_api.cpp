@@ -120,8 +120,8 @@ size_t fa_multimodal_workspace_bytes(int B, int H, int n_txt, int d, int dtype)
 int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_img,
                           const void *q_txt, const void *k_txt, const void *v_txt, void *o_img,
                           float *lse_img, void *o_txt, float *lse_txt, int B, int H, int n_img,
-                          int n_txt, int d, float scale, int dtype, void *workspace,
-                          size_t workspace_bytes, void *stream)
+                          int n_txt, int d, float scale, int dtype, int text_mode,
+                          void *workspace, size_t workspace_bytes, void *stream)
 {
     teaf::FwdArgs img, txt, cross;
     int st = check_forward(q_img, k_img, v_img, o_img, lse_img, B, H, n_img, n_img, d, scale,
@@ -130,6 +130,21 @@ int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_im
     st = check_forward(q_txt, k_txt, v_txt, o_txt, lse_txt, B, H, n_txt, n_txt, d, scale,
                        FA_MASK_CAUSAL, 0, 0, dtype, &txt);
     if (st != FA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (text_mode == FA_MULTIMODAL_FUSED) {
+        // text rows against [image; text] keys, causal with bottom-right alignment: every
+        // image key, and text keys up to the row's own position
+        if (n_img % 32 != 0 || dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+        if ((long long)(n_img + (long long)n_txt) * d > (long long)INT_MAX) return FA_ERR_SHAPE;
+        teaf::FwdArgs fused = txt;
+        fused.k = k_img;
+        fused.v = v_img;
+        fused.Nkv = n_img + n_txt;
+        hipError_t e = teaf::launch_forward(img, s);
+        if (e == hipSuccess) e = teaf::launch_forward_causal_two_part(fused, k_txt, v_txt, n_img, s);
+        return hip_status(e);
+    }
+    if (text_mode != FA_MULTIMODAL_SPLIT_MERGE) return FA_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < fa_multimodal_workspace_bytes(B, H, n_txt, d, dtype) ||
         !aligned16(workspace))
         return FA_ERR_WORKSPACE;
@@ -140,7 +155,6 @@ int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_im
                        FA_MASK_NONE, 0, 0, dtype, &cross);
     if (st != FA_OK) return st;
     const teaf::MergeArgs mg{o_txt, lse_txt, ws, lse_x, o_txt, lse_txt, (long)rows, d, dtype};
-    hipStream_t s = (hipStream_t)stream;
     hipError_t e = teaf::launch_forward(img, s);
     if (e == hipSuccess) e = teaf::launch_forward(txt, s);
     if (e == hipSuccess) e = teaf::launch_forward(cross, s);

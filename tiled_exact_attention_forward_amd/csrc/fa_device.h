@@ -376,9 +376,18 @@ __device__ __forceinline__ void issue_kv(const char *kbh, const char *vbh,
 // j / kPageTokens]. Query chunks are [S, Qmax, H, D] (row i of sequence s at (s Qmax + i) H + h),
 // LSE [S, Qmax, H].
 constexpr int kPageTokens = 256;
-struct PagedKV {
+
+// Where a forward launch finds its keys and values.
+//  kKvDense:   K, V [B, H, Nkv, d] contiguous.
+//  kKvPaged:   a paged cache (fields table .. H); query chunks token-major, see above.
+//  kKvTwoPart: keys [0, n1) from K, V [B, H, n1, d] and keys [n1, Nkv) from k2, v2
+//              [B, H, Nkv - n1, d]; n1 is a multiple of the 32-key tile, so no tile spans both.
+constexpr int kKvDense = 0, kKvPaged = 1, kKvTwoPart = 2;
+struct KvLayout {
     const int32_t *table, *seq_lens, *q_lens;
     int max_pages, num_pages, Qmax, H;
+    const uint16_t *k2, *v2;
+    int n1;
 };
 
 // The K and V tiles of keys [kv0, kv0 + 32) of head h of a paged sequence (a tile never

@@ -133,16 +133,19 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
     }
 }
 
-// PAGED: the query rows are a chunk of the newest tokens of sequence bh / H (head bh % H) and
-// K/V come from the page pool described by pg; Nq and Nkv are then that sequence's chunk
-// and cache lengths, read from pg (the arguments are ignored).
-template <typename T, int D, int MASK, int NS, int NW, bool PAGED>
+// KVL (kKvDense, kKvPaged, kKvTwoPart) says where the keys are, see KvLayout. Paged: the
+// query rows are a chunk of the newest tokens of sequence bh / H (head bh % H) and K/V come
+// from the page pool described by pg; Nq and Nkv are then that sequence's chunk and cache
+// lengths, read from pg (the arguments are ignored). Two parts: key tiles below pg.n1 come
+// from K and V, the rest from pg.k2 and pg.v2.
+template <typename T, int D, int MASK, int NS, int NW, int KVL>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
     int Nkv, float c, int W, int G, int nqt, const uint8_t *__restrict__ layout, int H,
-    const PagedKV pg)
+    const KvLayout pg)
 {
+    constexpr bool PAGED = KVL == kKvPaged;
     using C = CfgSP<D, NS, NW>;
     using Op = Ops16<T>;
     constexpr int BM = C::BM, BN = C::BN, LPW = C::LPW;
@@ -158,6 +161,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     // start. Lengths in a paged cache are clamped to what the table and the chunk can hold.
     int rs = D;
     size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D, lbase = (size_t)bh * Nq;
+    if (KVL == kKvTwoPart) kvbase = (size_t)bh * pg.n1 * D;
     int lstride = 1, seq = 0, head = 0;
     if constexpr (PAGED) {
         seq = bh / pg.H;
@@ -270,11 +274,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     }
     const int32_t *seq_table = PAGED ? pg.table + (size_t)seq * pg.max_pages : nullptr;
     auto load_tile = [&](int tl, int slot) {
-        if constexpr (PAGED)
+        if constexpr (PAGED) {
             issue_kv_paged<C>(kbh, vbh, seq_table, pg.num_pages, pg.H, head, off, tl * BN, Nkv,
                               kslot(slot), vslot(slot), wave);
-        else
+        } else if constexpr (KVL == kKvTwoPart) {
+            const int kv0 = __builtin_amdgcn_readfirstlane(tl * BN);
+            if (kv0 < pg.n1) {
+                issue_kv<C>(kbh, vbh, off, kv0, pg.n1, kslot(slot), vslot(slot), wave);
+            } else {
+                const size_t b2 = (size_t)bh * (Nkv - pg.n1) * D;
+                issue_kv<C>((const char *)(pg.k2 + b2), (const char *)(pg.v2 + b2), off,
+                            kv0 - pg.n1, Nkv - pg.n1, kslot(slot), vslot(slot), wave);
+            }
+        } else {
             issue_kv<C>(kbh, vbh, off, tl * BN, Nkv, kslot(slot), vslot(slot), wave);
+        }
     };
     int kofs[C::NKK], vofs[C::NDB];
 #pragma unroll
@@ -536,7 +550,7 @@ hipError_t launch16(const FwdArgs &a, hipStream_t s)
     using C = CfgSP<D, kStages, kWaves>;
     const int nqt = (a.Nq + C::BM - 1) / C::BM;
     const long nblk = (long)nqt * a.B * a.H;
-    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves, false>;
+    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves, kKvDense>;
     // block sparse: wave counts and the key-block list (2 bytes a block) after the ring
     const int lds = MASK == kBlockSparse ? C::LDS_BYTES + 16 + 2 * kMaxKeyBlocks : C::LDS_BYTES;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -545,7 +559,7 @@ hipError_t launch16(const FwdArgs &a, hipStream_t s)
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), lds, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        (uint16_t *)a.o, a.lse, a.Nq, a.Nkv, a.scale * kLog2e, a.window,
-                       a.n_global, nqt, a.layout, a.H, PagedKV{});
+                       a.n_global, nqt, a.layout, a.H, KvLayout{});
     return hipGetLastError();
 }
 
@@ -557,11 +571,12 @@ hipError_t launch16_paged(const PrefillArgs &a, hipStream_t s)
     using C = CfgSP<D, kStages, kWaves>;
     const int nqt = (a.Qmax + C::BM - 1) / C::BM;
     const long nblk = (long)nqt * a.S * a.H;
-    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves, true>;
+    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves, kKvPaged>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    const PagedKV pg{a.page_table, a.seq_lens, a.q_lens, a.max_pages, a.num_pages, a.Qmax, a.H};
+    const KvLayout pg{a.page_table, a.seq_lens, a.q_lens, a.max_pages, a.num_pages, a.Qmax, a.H,
+                      nullptr, nullptr, 0};
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), C::LDS_BYTES, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k_pages,
                        (const uint16_t *)a.v_pages, (uint16_t *)a.o, a.lse, 0, 0,
@@ -630,6 +645,30 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t s)
     return a.d == 64 ? launch16_mask<__bf16, 64>(a, s) : launch16_mask<__bf16, 128>(a, s);
 }
 
+// Causal attention whose keys sit in two tensors (see KvLayout): [0, n1) in a.k/a.v,
+// [n1, Nkv) in k2/v2.
+template <typename T, int D>
+hipError_t launch16_two_part(const FwdArgs &a, const void *k2, const void *v2, int n1,
+                             hipStream_t s)
+{
+    using C = CfgSP<D, kStages, kWaves>;
+    const int nqt = (a.Nq + C::BM - 1) / C::BM;
+    const long nblk = (long)nqt * a.B * a.H;
+    auto kern = fwd16_kernel<T, D, 1, kStages, kWaves, kKvTwoPart>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    KvLayout pg{};
+    pg.k2 = (const uint16_t *)k2;
+    pg.v2 = (const uint16_t *)v2;
+    pg.n1 = n1;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(C::NT), C::LDS_BYTES, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (uint16_t *)a.o, a.lse, a.Nq, a.Nkv, a.scale * kLog2e, 0, 0, nqt, nullptr,
+                       a.H, pg);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_paged(const PrefillArgs &a, hipStream_t s)
 {
     (void)hipGetLastError();
@@ -638,6 +677,17 @@ hipError_t launch_prefill_paged(const PrefillArgs &a, hipStream_t s)
                          : launch16_paged_mask<_Float16, 128>(a, s);
     return a.d == 64 ? launch16_paged_mask<__bf16, 64>(a, s)
                      : launch16_paged_mask<__bf16, 128>(a, s);
+}
+
+hipError_t launch_forward_causal_two_part(const FwdArgs &a, const void *k2, const void *v2,
+                                         int n1, hipStream_t s)
+{
+    (void)hipGetLastError();
+    if (a.dtype == 1)
+        return a.d == 64 ? launch16_two_part<_Float16, 64>(a, k2, v2, n1, s)
+                         : launch16_two_part<_Float16, 128>(a, k2, v2, n1, s);
+    return a.d == 64 ? launch16_two_part<__bf16, 64>(a, k2, v2, n1, s)
+                     : launch16_two_part<__bf16, 128>(a, k2, v2, n1, s);
 }
 
 }  // namespace teaf

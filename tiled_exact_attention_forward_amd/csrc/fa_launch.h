@@ -93,5 +93,9 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
+// Causal forward (16-bit types) whose keys are [0, n1) from a.k/a.v ([B,H,n1,d]) and
+// [n1, a.Nkv) from k2/v2 ([B,H,a.Nkv-n1,d]); n1 a multiple of 32.
+hipError_t launch_forward_causal_two_part(const FwdArgs &a, const void *k2, const void *v2,
+                                         int n1, hipStream_t stream);
 
 }  // namespace teaf
