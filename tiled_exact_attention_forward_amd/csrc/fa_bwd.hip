@@ -19,8 +19,7 @@
 //  * bwd_dq_kernel: a workgroup owns 128 query rows (4 waves x 32) with Q and dO in
 //    registers and walks the visible 32-key tiles like the forward pass: S^T = K Q^T and
 //    dP^T = V dO^T with lanes indexed by row, then dQ^T += K^T dS^T.
-// Tiles stream from HBM to LDS with buffer_load ... lds (a 4-slot ring for dK/dV, two
-// stages for dQ). Scores, P, dS and all accumulators are fp32; P and dS are rounded to the
+// Tiles stream from HBM to LDS with buffer_load ... lds through 4-slot rings. Scores, P, dS and all accumulators are fp32; P and dS are rounded to the
 // input type for the products.
 #include "fa_device.h"
 
@@ -478,6 +477,56 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
 }
 
+// One 32-key tile of the dQ kernel: kt and vt are the tile's K and V in LDS
+// (restrict-qualified: the loads of later tiles into other ring slots cannot overlap them).
+// S^T = K Q^T and dP^T = V dO^T (lane (g, row) holds keys 8(e/4) + 4g + e%4), then
+// dQ^T += K^T dS^T with K^T read transposed.
+template <typename T, typename C, int MASK>
+__device__ __forceinline__ void dq_step(const char *__restrict__ kt, const char *__restrict__ vt,
+                                        const s16x8 (&qf)[C::NKK], const s16x8 (&gf)[C::NKK],
+                                        f32x16 (&dqt)[C::NDB], const int (&kofs)[C::NKK],
+                                        const int (&tro)[2][C::NDB], float c, float lrow,
+                                        float drow, bool masked, int kv0, int ip, int Nkv, int W,
+                                        int G, int g)
+{
+    using Op = Ops16<T>;
+    constexpr int NKK = C::NKK, NDB = C::NDB;
+    // the S and dP accumulation chains alternate, so no MFMA waits for its predecessor
+    f32x16 s, dp;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        s = Op::mma(*(const s16x8 *)(kt + kofs[kk]), qf[kk], kk == 0 ? f32x16{} : s);
+        dp = Op::mma(*(const s16x8 *)(vt + kofs[kk]), gf[kk], kk == 0 ? f32x16{} : dp);
+    }
+    if (masked) mask_tile<MASK>(s, kv0, ip, Nkv, W, G, g);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {  // hidden scores are -inf; P = 0 for any sign of c
+        const float p = s[e] == -INFINITY ? 0.f : fast_exp2(__builtin_fmaf(s[e], c, -lrow));
+        dp[e] = p * (dp[e] - drow);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const int o8 = 8 * kc;
+        const s16x8 sf = Op::pack8(dp[o8], dp[o8 + 1], dp[o8 + 2], dp[o8 + 3], dp[o8 + 4],
+                                   dp[o8 + 5], dp[o8 + 6], dp[o8 + 7]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int base = kc * 16 * C::ROWB;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(kt + base + tro[0][db]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(kt + base + tro[1][db]));
+            dqt[db] = Op::mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sf,
+                              dqt[db]);
+        }
+    }
+}
+
+// dQ. A workgroup owns 128 query rows (4 waves x 32) with Q and dO in registers and walks
+// the visible 32-key tiles with the forward's schedule. K/V tiles stream through the
+// forward's 4-slot ring; every step issues a load (empty past the last tile), so every wait
+// has the same count.
+constexpr int kDqStages = 4;
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -485,9 +534,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const float *__restrict__ ST, uint16_t *__restrict__ dQ, int Nq, int Nkv, float c,
     float scale, int W, int G, int nqt, int nt32)
 {
-    using C = CfgSP<D, 2, 4>;
+    using C = CfgSP<D, kDqStages, 4>;
     using Op = Ops16<T>;
-    constexpr int BM = 128, BN = 32, NKK = C::NKK, NDB = C::NDB;
+    constexpr int BM = 128, BN = 32, NKK = C::NKK, NDB = C::NDB, NS = kDqStages, LPW = C::LPW;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char *const lds = (char *)smem;
 
@@ -519,9 +568,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
 
-    unsigned off[C::LPW];
+    unsigned off[LPW];
 #pragma unroll
-    for (int u = 0; u < C::LPW; ++u) {
+    for (int u = 0; u < LPW; ++u) {
         const int i = wave + C::NW * u;
         const int r = (i % C::KL) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
         off[u] = r * C::ROWB + 16 * k_swz<D>(r, lane % C::CHUNKS);
@@ -537,52 +586,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
     const char *kb = (const char *)(K + kvbase);
     const char *vb = (const char *)(V + kvbase);
-    auto kslot = [&](int n) { return lds + (n & 1) * C::TILEB; };
-    auto vslot = [&](int n) { return lds + C::VREG + (n & 1) * C::TILEB; };
-    TileSchedule::Cursor cur = sch.begin(), nxt = sch.next(cur);
-    if (ntl > 0) {
-        issue_kv<C>(kb, vb, off, cur.t * BN, Nkv, kslot(0), vslot(0), wave);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
+    auto kslot = [&](int n) { return lds + ((unsigned)n % NS) * C::TILEB; };
+    auto vslot = [&](int n) { return lds + C::VREG + ((unsigned)n % NS) * C::TILEB; };
+    // Tile n of the stream goes to slot n % NS; past the last tile the load is empty
+    // (zero rows: it touches no memory and only writes zeros into a consumed slot).
+    TileSchedule::Cursor ld = sch.begin(), cur = sch.begin();
+    auto load = [&](int n) {
+        const int kv0 = n < ntl ? ld.t * BN : Nkv;
+        issue_kv<C>(kb, vb, off, kv0, Nkv, kslot(n), vslot(n), wave);
+        if (n < ntl) ld = sch.next(ld);
+    };
+    constexpr int kAhead = (NS - 2) * LPW;  // loads of the tiles after the next one
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) load(j);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile 0 (and the Q, dO rows)
+    ring_barrier();
     for (int n = 0; n < ntl; ++n) {
-        if (n + 1 < ntl) issue_kv<C>(kb, vb, off, nxt.t * BN, Nkv, kslot(n + 1), vslot(n + 1), wave);
-        const char *kt = kslot(n), *vt = vslot(n);
-        // S^T = K Q^T and dP^T = V dO^T: lane (g, row) holds keys 8(e/4) + 4g + e%4.
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            s = Op::mma(*(const s16x8 *)(kt + kofs[kk]), qf[kk], s);
-            dp = Op::mma(*(const s16x8 *)(vt + kofs[kk]), gf[kk], dp);
-        }
-        if (n >= nint) mask_tile<MASK>(s, cur.t * BN, ip, Nkv, W, G, g);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {  // hidden scores are -inf; P = 0 for any sign of c
-            const float p = s[e] == -INFINITY ? 0.f : fast_exp2(__builtin_fmaf(s[e], c, -lrow));
-            dp[e] = p * (dp[e] - drow);
-        }
-        // dQ^T += K^T dS^T over two 16-key chunks.
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            const int o8 = 8 * kc;
-            const s16x8 sf = Op::pack8(dp[o8], dp[o8 + 1], dp[o8 + 2], dp[o8 + 3], dp[o8 + 4],
-                                       dp[o8 + 5], dp[o8 + 6], dp[o8 + 7]);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int base = kc * 16 * C::ROWB;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(kt + base + tro[0][db]));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(kt + base + tro[1][db]));
-                dqt[db] = Op::mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sf,
-                                  dqt[db]);
-            }
-        }
-        cur = nxt;
-        nxt = sch.next(nxt);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        load(n + NS - 1);
+        dq_step<T, C, MASK>(kslot(n), vslot(n), qf, gf, dqt, kofs, tro, c, lrow, drow, n >= nint,
+                            cur.t * BN, ip, Nkv, W, G, g);
+        cur = sch.next(cur);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile n + 1 resident
+        ring_barrier();
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still write this LDS at exit
 
     if (row < Nq) {
         uint16_t *out = dQ + qbase + (size_t)row * D;
@@ -620,7 +647,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s)
                        a.Nkv, c, a.scale, a.window, a.n_global, nkt, nt32);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    using CB = CfgSP<D, 2, 4>;
+    using CB = CfgSP<D, kDqStages, 4>;
     const int nqt = (a.Nq + 127) / 128;
     auto kb = bwd_dq_kernel<T, D, MASK>;
     e = hipFuncSetAttribute((const void *)kb, hipFuncAttributeMaxDynamicSharedMemorySize,
