@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the tiled exact attention path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_bf16] [--warm-seconds S]
 
 One step is one call of the tiled attention forward (query-tile decomposition, Q load, K/V
 tile stream, QK^T, scale and mask, online softmax, PV and the epilogue) over the dense bf16
@@ -131,10 +131,22 @@ def backward_traffic(workload):
 
 # ----------------------------------------------------------------- timing
 
-def time_calls(fn, steps, warmup, torch):
+# Untimed warm-up lasts at least this long (wall clock) besides the W warm-up steps: the
+# GPU raises its clock over the first fraction of a second of load, and the first calls of
+# a kernel in a process run slower; the timed steps measure the steady state.
+MIN_WARM_S = 1.0
+
+
+def time_calls(fn, steps, warmup, torch, min_warm_s=None):
+    min_warm_s = MIN_WARM_S if min_warm_s is None else min_warm_s
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t_warm < min_warm_s:
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -356,6 +368,7 @@ def cpu_baseline(res, budget_s):
 
 
 def main():
+    global MIN_WARM_S
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -365,6 +378,9 @@ def main():
                     help="skip the other workloads and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--warm-seconds", type=float, default=None,
+                    help="untimed warm-up also lasts at least this many seconds per workload "
+                         f"(default {MIN_WARM_S}; 0 with --profile-workload, for profilers)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (for HBM counter scaling)")
     ap.add_argument("--profile-workload", default=None,
@@ -372,6 +388,9 @@ def main():
     ap.add_argument("--profile-backward", action="store_true",
                     help="with --profile-workload: time the backward pass instead")
     args = ap.parse_args()
+    if args.warm_seconds is None:
+        args.warm_seconds = 0.0 if args.profile_workload else MIN_WARM_S
+    MIN_WARM_S = args.warm_seconds
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the attention path has no multi-GPU sharding in this build)", file=sys.stderr)
@@ -499,6 +518,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_seconds": args.warm_seconds,
         "ms_per_step": round(head["ms"], 6),
         "higher_is_better": True,
         "scaling": "weak",
