@@ -75,6 +75,9 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
     const float nmu = (m == -INFINITY) ? 0.f : -m;
     __builtin_amdgcn_sched_barrier(0);
 
+    // The wave runs phase A at raised priority: of the two waves sharing a SIMD, the one
+    // issuing the score MFMAs and exponentials goes first (about 1 % faster, measured).
+    __builtin_amdgcn_s_setprio(1);
     // Phase A: S(t+1) = K(t+1) Q^T, P(t) = 2^(c S(t) - m).
     s16x4 vlo[NF], vhi[NF];
     auto vread = [&](int f) {
@@ -102,6 +105,7 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // Phase B: O^T += V^T P^T(t); l += row sums of P(t); mask and maximum of S(t+1).
     float ps[4];
 #pragma unroll
