@@ -55,6 +55,31 @@ def test_small_shapes(dtype, d, mask, shape):
     check(o, lse, ro, rl, dtype, f"{dtype} d{d} mask{mask} {shape}")
 
 
+# More 128-row query tiles than two workgroups per CU hold at once (512 on a 256-CU device),
+# so the tiles run in several rounds of workgroups, compared on every element: ragged Nq and
+# Nkv, key-tile counts of every residue mod the ring depth of 4, a single masked key tile,
+# and a negative scale.
+MANY_TILE_SHAPES = [
+    (1, 64, 1100, 333, 128, "bf16", 1),   # 576 query tiles, 11 key tiles, tail masked
+    (3, 40, 700, 70, 64, "f16", 1),       # 720 query tiles, 3 key tiles
+    (1, 130, 520, 31, 128, "f16", 1),     # 650 query tiles, one masked key tile
+    (4, 32, 1536, 64, 64, "bf16", 1),     # 1536 query tiles (three rounds), 2 key tiles
+    (1, 32, 2125, 1000, 128, "bf16", 1),  # 544 query tiles, 32 key tiles, tail masked
+    (2, 40, 900, 100, 128, "bf16", -1),   # 640 query tiles, 4 key tiles, negative scale
+]
+
+
+@pytest.mark.parametrize("shape", MANY_TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dense_many_query_tiles(shape):
+    B, H, Nq, Nkv, d, dtype, sign = shape
+    seed = zlib.crc32(repr(("many", shape)).encode()) % 100000
+    q, k, v = workloads.gen_prefill(B, H, Nq, Nkv, d, dtype, seed)
+    scale = sign * workloads.default_scale(d)
+    o, lse = run_fwd(q, k, v, scale, 0)
+    ro, rl = oracle.attention(q, k, v, scale, 0)
+    check(o, lse, ro, rl, dtype, f"{shape}")
+
+
 def test_tiny_f32_workload():
     w, inp = workloads.gen_workload("tiny_f32")
     scale = workloads.default_scale(w["d"])
