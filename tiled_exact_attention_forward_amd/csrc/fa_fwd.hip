@@ -89,6 +89,13 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
     s16x8 pf[2];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
+        // The first group's exponentials go ahead of the first score instruction, covering
+        // the latency of the K fragment reads that follow the step's barrier.
+        if (kk == 0) {
+#pragma unroll
+            for (int e = 0; e < EPK; ++e) sc[e] = fast_exp2(__builtin_fmaf(sc[e], c, nmu));
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (NEXT) {
             if (kk + KPF < NKK) kf[kk + KPF] = *(const s16x8 *)(kn + kofs[kk + KPF]);
             sn = Op::mma(kf[kk], qf[kk], kk == 0 ? f32x16{} : sn);
@@ -96,7 +103,7 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
         if (kk >= NKK - VPF) vread(kk - (NKK - VPF));
 #pragma unroll
         for (int e = kk * EPK; e < (kk + 1) * EPK; ++e)
-            sc[e] = fast_exp2(__builtin_fmaf(sc[e], c, nmu));
+            if (kk > 0) sc[e] = fast_exp2(__builtin_fmaf(sc[e], c, nmu));
         if (((kk + 1) * EPK) % 8 == 0) {
             const int o = (kk + 1) * EPK - 8;
             pf[o / 8] = Op::pack8(sc[o], sc[o + 1], sc[o + 2], sc[o + 3], sc[o + 4], sc[o + 5],
@@ -114,24 +121,40 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
         if (f + VPF < NF) vread(f + VPF);
         const s16x8 a = __builtin_shufflevector(vlo[f], vhi[f], 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = Op::mma(a, pf[kc], oacc[db]);
-        // vector work spread over the matrix instructions
+        // Vector work spread over the matrix instructions. The empty asm statements pin each
+        // partial result to its slot: otherwise the row sum is sunk past the end of the step,
+        // where it delays the next step's first K fragment reads (about 1 % slower, measured).
         if (NF == 8) {
-            if (f < 4) ps[f] = (sc[4 * f] + sc[4 * f + 1]) + (sc[4 * f + 2] + sc[4 * f + 3]);
-            if (f == 4) l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            if (f < 4) {
+                ps[f] = (sc[4 * f] + sc[4 * f + 1]) + (sc[4 * f + 2] + sc[4 * f + 3]);
+                __asm__ volatile("" : "+v"(ps[f]));
+            }
+            if (f == 4) {
+                l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                __asm__ volatile("" : "+v"(l));
+            }
             if (NEXT && f == 4 && mask_next) mask_tile<MASK>(sn, kvn, ip, Nkv, W, G, g);
-            if (NEXT && f == 6) mt = half_swap_max(max16(sn)) * c;
+            if (NEXT && f == 6) {
+                mt = half_swap_max(max16(sn)) * c;
+                __asm__ volatile("" : "+v"(mt));
+            }
         } else {
             if (f == 0) {
                 ps[0] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
                 ps[1] = (sc[4] + sc[5]) + (sc[6] + sc[7]);
+                __asm__ volatile("" : "+v"(ps[0]), "+v"(ps[1]));
             }
             if (f == 1) {
                 ps[2] = (sc[8] + sc[9]) + (sc[10] + sc[11]);
                 ps[3] = (sc[12] + sc[13]) + (sc[14] + sc[15]);
                 l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                __asm__ volatile("" : "+v"(l));
             }
             if (NEXT && f == 2 && mask_next) mask_tile<MASK>(sn, kvn, ip, Nkv, W, G, g);
-            if (NEXT && f == 3) mt = half_swap_max(max16(sn)) * c;
+            if (NEXT && f == 3) {
+                mt = half_swap_max(max16(sn)) * c;
+                __asm__ volatile("" : "+v"(mt));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
