@@ -165,8 +165,9 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
 // from the page pool described by pg; Nq and Nkv are then that sequence's chunk and cache
 // lengths, read from pg (the arguments are ignored). Two parts: key tiles below pg.n1 come
 // from K and V, the rest from pg.k2 and pg.v2.
+// Launch bound: NW waves per workgroup, at least two waves per SIMD (256 registers each).
 template <typename T, int D, int MASK, int NS, int NW, int KVL>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
     int Nkv, float c, int W, int G, int nqt, const uint8_t *__restrict__ layout, int H,
@@ -568,16 +569,26 @@ __global__ __launch_bounds__(256) void fwd32_kernel(const float *__restrict__ Q,
     }
 }
 
-// 4 waves (128 query rows) per workgroup, two workgroups per CU, a 4-slot K/V ring.
-constexpr int kStages = 4, kWaves = 4;
+// 4 waves (128 query rows) per workgroup, two workgroups per CU, a 4-slot K/V ring: the
+// fastest shape of a sweep over 2, 4 and 8 waves and 3 to 8 ring slots on MI355X. The sweep
+// (tile_sweep.py) rebuilds with FA_FWD_WAVES and FA_FWD_STAGES set; the block-sparse kernel
+// keeps 4 waves, since its query tile must match the 128-position layout block.
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 4
+#endif
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 4
+#endif
+constexpr int kStages = FA_FWD_STAGES, kWaves = FA_FWD_WAVES;
 
 template <typename T, int D, int MASK>
 hipError_t launch16(const FwdArgs &a, hipStream_t s)
 {
-    using C = CfgSP<D, kStages, kWaves>;
+    constexpr int NS = MASK == kBlockSparse ? 4 : kStages, NW = MASK == kBlockSparse ? 4 : kWaves;
+    using C = CfgSP<D, NS, NW>;
     const int nqt = (a.Nq + C::BM - 1) / C::BM;
     const long nblk = (long)nqt * a.B * a.H;
-    auto kern = fwd16_kernel<T, D, MASK, kStages, kWaves, kKvDense>;
+    auto kern = fwd16_kernel<T, D, MASK, NS, NW, kKvDense>;
     // block sparse: wave counts and the key-block list (2 bytes a block) after the ring
     const int lds = MASK == kBlockSparse ? C::LDS_BYTES + 16 + 2 * kMaxKeyBlocks : C::LDS_BYTES;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
