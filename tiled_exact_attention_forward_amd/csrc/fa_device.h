@@ -22,6 +22,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) const char lds_char;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -436,11 +437,11 @@ __device__ __forceinline__ void mask_tile(f32x16 &s, int kv0, int ip, int Nkv, i
 
 __device__ __forceinline__ float max16(const f32x16 &v)
 {
-    const float a = vmax(vmax(vmax(v[0], v[1]), vmax(v[2], v[3])),
-                         vmax(vmax(v[4], v[5]), vmax(v[6], v[7])));
-    const float b = vmax(vmax(vmax(v[8], v[9]), vmax(v[10], v[11])),
-                         vmax(vmax(v[12], v[13]), vmax(v[14], v[15])));
-    return vmax(a, b);
+    // a tree of three-input maxima: 5 + 2 + 1 instructions
+    const float r0 = vmax(vmax(v[0], v[1]), v[2]), r1 = vmax(vmax(v[3], v[4]), v[5]);
+    const float r2 = vmax(vmax(v[6], v[7]), v[8]), r3 = vmax(vmax(v[9], v[10]), v[11]);
+    const float r4 = vmax(vmax(v[12], v[13]), v[14]);
+    return vmax(vmax(vmax(r0, r1), r2), vmax(vmax(r3, r4), v[15]));
 }
 
 }  // namespace

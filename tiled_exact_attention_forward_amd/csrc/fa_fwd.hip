@@ -41,15 +41,19 @@ namespace teaf {
 namespace {
 
 // One pipeline step for tile t. sc: raw scores of tile t (masked if needed), mt its
-// scaled row maximum. NEXT: there is a tile t+1 (K in LDS at kn); mask_next: it needs the
-// element mask (wave-uniform). vc: V of tile t in LDS.
+// scaled row maximum. m: running scaled row maximum, nmu = -m (0 while m is -inf), both
+// changed only when the maximum moves. NEXT: there is a tile t+1 (K in LDS at kn);
+// mask_next: it needs the element mask (wave-uniform). vslot_ofs: where V of tile t sits in
+// the V ring (bytes from the ring's first slot); vptr: this lane's V^T read addresses in
+// the first slot.
 template <typename T, typename C, int MASK, bool NEXT>
-__device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char *__restrict__ vc,
-                                        const int (&kofs)[C::NKK], const int (&vofs)[C::NDB],
+__device__ __forceinline__ void sp_step(const char *__restrict__ kn, unsigned vslot_ofs,
+                                        const int (&kofs)[C::NKK],
+                                        const lds_char *const (&vptr)[C::NDB],
                                         const s16x8 (&qf)[C::NKK], f32x16 (&oacc)[C::NDB],
-                                        f32x16 &sc, f32x16 &sn, float &m, float &l, float &mt,
-                                        float c, bool mask_next, int kvn, int ip, int Nkv, int W,
-                                        int G, int g)
+                                        f32x16 &sc, f32x16 &sn, float &m, float &nmu, float &l,
+                                        float &mt, float c, bool mask_next, int kvn, int ip,
+                                        int Nkv, int W, int G, int g)
 {
     using Op = Ops16<T>;
     constexpr int NKK = C::NKK, NDB = C::NDB, KPF = C::KPF, VPF = C::VPF;
@@ -66,13 +70,13 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
         const float mn = fmaxf(m, mt);
         const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
         m = mn;
+        nmu = mn == -INFINITY ? 0.f : -mn;
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
-    const float nmu = (m == -INFINITY) ? 0.f : -m;
     __builtin_amdgcn_sched_barrier(0);
 
     // The wave runs phase A at raised priority: of the two waves sharing a SIMD, the one
@@ -80,9 +84,11 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
     __builtin_amdgcn_s_setprio(1);
     // Phase A: S(t+1) = K(t+1) Q^T, P(t) = 2^(c S(t) - m).
     s16x4 vlo[NF], vhi[NF];
+    // V^T reads: per-lane LDS addresses made once per workgroup; the slot (a constant in
+    // the unrolled loop) and the chunk enter as immediate offsets.
     auto vread = [&](int f) {
         const int kc = f / NDB, db = f % NDB;
-        const char *p0 = vc + vofs[db] + kc * 16 * C::ROWB;
+        const lds_char *p0 = vptr[db] + vslot_ofs + kc * 16 * C::ROWB;
         vlo[f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
         vhi[f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 8 * C::ROWB));
     };
@@ -114,6 +120,7 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char 
 
     __builtin_amdgcn_s_setprio(0);
     // Phase B: O^T += V^T P^T(t); l += row sums of P(t); mask and maximum of S(t+1).
+    // The row sums add the fp32 probabilities (before rounding for the product).
     float ps[4];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
         return __builtin_amdgcn_readfirstlane((int)blist[p / TPB] * TPB + p % TPB);
     };
 
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, nmu = 0.f, l = 0.f;
     f32x16 oacc[C::NDB];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
@@ -287,7 +294,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     const char *kbh = (const char *)(K + kvbase);
     const char *vbh = (const char *)(V + kvbase);
     auto kslot = [&](int t) { return lds + ((unsigned)t % NS) * C::TILEB; };
-    auto vslot = [&](int t) { return lds + C::VREG + ((unsigned)t % NS) * C::TILEB; };
+    auto vring_ofs = [&](int t) { return ((unsigned)t % NS) * C::TILEB; };
+    auto vslot = [&](int t) { return lds + C::VREG + vring_ofs(t); };
     // Load u of this wave fills rows r of the K (or V) tile; lane l lands in physical chunk
     // l % CHUNKS of row r = first + l / CHUNKS, so it fetches the logical chunk the swizzle
     // stores there. Offsets are relative to the tile's first key.
@@ -318,7 +326,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
             issue_kv<C>(kbh, vbh, off, tl * BN, Nkv, kslot(slot), vslot(slot), wave);
         }
     };
-    int kofs[C::NKK], vofs[C::NDB];
+    int kofs[C::NKK];
+    const lds_char *vptr[C::NDB];
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * k_swz<D>(li, 2 * kk + g);
     {
@@ -326,7 +335,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
         const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-            vofs[db] = trow * C::ROWB + 16 * v_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
+            vptr[db] = (const lds_char *)(lds + C::VREG) + trow * C::ROWB +
+                       16 * v_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
     }
 
     // Prologue: tiles 0 .. NS-2 in flight; wait for tiles 0 and 1.
@@ -381,15 +391,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     auto step = [&](int t, f32x16 &cur, f32x16 &nxt) {
         load_ahead(t);
         sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, true>(
-            kslot(t + 1), vslot(t), kofs, vofs, qf, oacc, cur, nxt, m, l, mt, c, t + 1 >= nint,
+            kslot(t + 1), vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, l, mt, c,
+            t + 1 >= nint,
             MASK == kBlockSparse ? tail_kv0 : nx.t * BN, ip, Nkv, W, G, g);
         nx = sch.next(nx);
         step_end(t);
     };
     auto last = [&](int t, f32x16 &cur, f32x16 &nxt) {
         sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, false>(
-            nullptr, vslot(t), kofs, vofs, qf, oacc, cur, nxt, m, l, mt, c, false, 0, ip, Nkv, W,
-            G, g);
+            nullptr, vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, l, mt, c, false, 0, ip,
+            Nkv, W, G, g);
     };
     if (ntl > 0) {
         int t = 0;
