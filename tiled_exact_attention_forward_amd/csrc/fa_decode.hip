@@ -220,8 +220,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 // grid (S, H); 256 threads = 4 groups of 64. Group q takes splits q, q + 4, ...; thread
 // (q, i) accumulates columns 2i and 2i+1 over them, issuing the loads of up to 32 splits at
 // once, then the groups are summed through LDS. Partial lse values are in log2 units.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineGroups = kCombineThreads / 64;
+// Combine: one wave per (sequence, head); lane i owns columns 2i and 2i+1. The partial
+// results of up to kCombineBatch splits are loaded together (one memory round trip per
+// batch), and the merge keeps a running maximum of the partial lse values, rescaling the
+// running sums when a later batch raises it, so no separate pass finds the maximum first.
+constexpr int kCombineThreads = 64;
 constexpr int kCombineBatch = 32;
 
 template <typename T>
@@ -230,63 +233,45 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const int32_t *__restrict__ seq_lens, uint16_t *__restrict__ O, float *__restrict__ LSE,
     int H, int max_splits, int split)
 {
-    __shared__ float red[kCombineThreads];
-    __shared__ float2 acc_s[kCombineGroups][64];
-    const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    const int q = tid >> 6, i = tid & 63;
-    const int ns = (seq_lens[s] + split - 1) / split;
+    const int s = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+    const int ns = min((seq_lens[s] + split - 1) / split, max_splits);
     const size_t slot0 = ((size_t)s * H + h) * max_splits;
 
-    // maximum of the partial lse values
-    float mx = -INFINITY;
-    for (int j = tid; j < ns; j += kCombineThreads) mx = fmaxf(mx, part_lse[slot0 + j]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int w = kCombineThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-    }
-    const float mu = red[0] == -INFINITY ? 0.f : red[0];
-    __syncthreads();
-
+    float mu = -INFINITY, wsum = 0.f;  // running maximum (log2 units) and sum of weights
     float2 acc = {0.f, 0.f};
-    float wsum = 0.f;
-    for (int j0 = q; j0 < ns; j0 += kCombineGroups * kCombineBatch) {
+    for (int j0 = 0; j0 < ns; j0 += kCombineBatch) {
         float2 o[kCombineBatch];
         float lw[kCombineBatch];
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
-            const int j = j0 + kCombineGroups * u;
+            const int j = j0 + u;
             o[u] = j < ns ? *(const float2 *)(part_o + (slot0 + j) * kD + 2 * i) : float2{0.f, 0.f};
             lw[u] = j < ns ? part_lse[slot0 + j] : -INFINITY;
         }
+        float bm = lw[0];
+#pragma unroll
+        for (int u = 1; u < kCombineBatch; ++u) bm = fmaxf(bm, lw[u]);
+        const float nm = fmaxf(mu, bm);
+        if (nm == -INFINITY) continue;  // no split so far has a visible key
+        const float r = __builtin_amdgcn_exp2f(mu - nm);  // 0 while mu is -inf
+        acc.x *= r;
+        acc.y *= r;
+        wsum *= r;
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
-            const float w = __builtin_amdgcn_exp2f(lw[u] - mu);
+            const float w = __builtin_amdgcn_exp2f(lw[u] - nm);
             acc.x = fmaf(w, o[u].x, acc.x);
             acc.y = fmaf(w, o[u].y, acc.y);
             wsum += w;
         }
+        mu = nm;
     }
-    acc_s[q][i] = acc;
-    red[tid] = wsum;
-    __syncthreads();
-    if (q == 0) {
-        float2 t = acc_s[0][i];
-        float wt = red[i];
-#pragma unroll
-        for (int g = 1; g < kCombineGroups; ++g) {
-            t.x += acc_s[g][i].x;
-            t.y += acc_s[g][i].y;
-            wt += red[64 * g + i];
-        }
-        const float inv = wt > 0.f ? 1.f / wt : 0.f;
-        uint16_t *op = O + ((size_t)s * H + h) * kD + 2 * i;
-        op[0] = from_float<T>(t.x * inv);
-        op[1] = from_float<T>(t.y * inv);
-        if (LSE != nullptr && i == 0)
-            LSE[(size_t)s * H + h] = wt > 0.f ? (mu + __builtin_amdgcn_logf(wt)) * kLn2 : -INFINITY;
-    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    uint16_t *op = O + ((size_t)s * H + h) * kD + 2 * i;
+    op[0] = from_float<T>(acc.x * inv);
+    op[1] = from_float<T>(acc.y * inv);
+    if (LSE != nullptr && i == 0)
+        LSE[(size_t)s * H + h] = wsum > 0.f ? (mu + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int HW, int SPLIT>
