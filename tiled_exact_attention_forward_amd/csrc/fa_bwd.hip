@@ -609,18 +609,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile n + 1 resident
         ring_barrier();
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still write this LDS at exit
-
-    if (row < Nq) {
-        uint16_t *out = dQ + qbase + (size_t)row * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-                *(s16x4 *)(out + db * 32 + 8 * blk + 4 * g) =
-                    Op::pack4(dqt[db][4 * blk] * scale, dqt[db][4 * blk + 1] * scale,
-                              dqt[db][4 * blk + 2] * scale, dqt[db][4 * blk + 3] * scale);
-    }
+    // dQ leaves as whole rows through the ring: every wave's loads (the empty ones past the
+    // last tile included) must have landed and every wave must be done reading it.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    static_assert(4 * 32 * (C::ROWB + 16) <= C::LDS_BYTES, "dQ staging must fit the ring");
+    store_rows_via_lds<T, D>(lds + wave * 32 * (C::ROWB + 16), dqt, scale, lane, dQ + qbase,
+                             q0 + wave * 32, Nq, D);
 }
 
 template <typename T, int D, int MASK>

@@ -248,6 +248,40 @@ struct Ops16<_Float16> {
     }
 };
 
+// Store a wave's 32 x D output tile (accumulator layout of the 32x32 MFMA: lane (g, i) holds
+// 8-byte pieces of row i) as whole rows. Stored straight from the accumulator, each
+// instruction would write 16 bytes of each of 32 rows; instead the tile is staged in LDS at
+// st (32 rows of pitch D*2 + 16 bytes: 16-byte aligned, and the row-wise read-back is free
+// of bank conflicts) and read back so that each store writes 64 / (D / 8) complete rows.
+// Rows r with row0 + r >= nvalid are not stored; row r goes to out + (row0 + r) * rs.
+// The wave reads back only what it wrote itself: LDS operations of one wave complete in
+// order, so no barrier separates the writes from the reads.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows_via_lds(char *st, const f32x16 (&acc)[D / 32],
+                                                   float mul, int lane, uint16_t *out,
+                                                   int row0, int nvalid, int rs)
+{
+    constexpr int OP = 2 * D + 16, CH = D / 8, RPI = 64 / CH;
+    const int g = lane >> 5, li = lane & 31;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const s16x4 v4 = Ops16<T>::pack4(acc[db][4 * blk] * mul, acc[db][4 * blk + 1] * mul,
+                                             acc[db][4 * blk + 2] * mul,
+                                             acc[db][4 * blk + 3] * mul);
+            *(s16x4 *)(st + li * OP + 2 * (db * 32 + 8 * blk + 4 * g)) = v4;
+        }
+    }
+    const int rr = lane / CH, cc = lane % CH;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+        const int r = it * RPI + rr;
+        const s16x8 v8 = *(const s16x8 *)(st + r * OP + 16 * cc);
+        if (row0 + r < nvalid) *(s16x8 *)(out + (size_t)(row0 + r) * rs + 8 * cc) = v8;
+    }
+}
+
 // ------------------------------------------------------------------ 16-bit kernel
 
 // LDS tiles are unpadded rows with an XOR swizzle of the 16-byte chunks (an involution:

@@ -425,34 +425,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     // Epilogue: both lane halves hold partial sums of the same row (same reference max).
     const float lt = half_swap_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    // A lane holds 8-byte pieces of one row, so stores straight from the accumulator write
-    // 16 bytes of each of 32 rows per instruction. Instead each wave stages its 32 rows in
-    // the idle K/V ring (row pitch ROWB + 16 bytes: 16-byte aligned, and the read-back below
-    // is free of bank conflicts) and stores whole rows, 64 / CHUNKS of them per instruction.
-    constexpr int OP = C::ROWB + 16;
-    if constexpr (NW * 32 * OP <= C::LDS_BYTES) {
+    // O leaves as whole rows through the idle K/V ring (32 rows per wave), when it fits.
+    if constexpr (NW * 32 * (C::ROWB + 16) <= C::LDS_BYTES) {
         __syncthreads();  // every wave has finished reading K and V from the ring
-        char *const st = lds + wave * 32 * OP;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const s16x4 v4 = Op::pack4(oacc[db][4 * blk + 0] * inv, oacc[db][4 * blk + 1] * inv,
-                                           oacc[db][4 * blk + 2] * inv, oacc[db][4 * blk + 3] * inv);
-                *(s16x4 *)(st + li * OP + 2 * (db * 32 + 8 * blk + 4 * g)) = v4;
-            }
-        }
-        // Each wave reads back only the rows it wrote: LDS operations of one wave complete
-        // in order, so no barrier is needed between the writes and these reads.
-        constexpr int RPI = 64 / C::CHUNKS;  // rows per store instruction
-        const int rr = lane / C::CHUNKS, cc = lane % C::CHUNKS;
-#pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
-            const int r = it * RPI + rr;
-            const s16x8 v8 = *(const s16x8 *)(st + r * OP + 16 * cc);
-            const int orow_i = q0 + wave * 32 + r;
-            if (orow_i < Nq) *(s16x8 *)(O + qbase + (size_t)orow_i * rs + 8 * cc) = v8;
-        }
+        store_rows_via_lds<T, D>(lds + wave * 32 * (C::ROWB + 16), oacc, inv, lane,
+                                 O + qbase, q0 + wave * 32, Nq, rs);
     } else if (row < Nq) {
         uint16_t *orow = O + qbase + (size_t)row * rs;
 #pragma unroll
