@@ -435,7 +435,11 @@ __device__ __forceinline__ void issue_kv_paged(const char *kpool, const char *vp
                                                int Nkv, char *kdst, char *vdst, int wave)
 {
     kv0 = __builtin_amdgcn_readfirstlane(kv0);
-    int pid = __builtin_amdgcn_readfirstlane(seq_table[kv0 / kPageTokens]);
+    // The page id is read through the constant address space with a uniform address, i.e.
+    // by a scalar load: its wait (lgkmcnt) leaves the K/V tiles in flight alone, whereas a
+    // vector load completes in order after them and waiting for it would drain the ring.
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    int pid = __builtin_amdgcn_readfirstlane(((const_i32 *)seq_table)[kv0 / kPageTokens]);
     pid = min(max(pid, 0), num_pages - 1);
     const size_t tok = (size_t)pid * kPageTokens + (size_t)(kv0 % kPageTokens);
     const size_t at = (tok * (size_t)H + (size_t)h) * C::ROWB;
