@@ -425,22 +425,26 @@ struct KvLayout {
     int n1;
 };
 
-// The K and V tiles of keys [kv0, kv0 + 32) of head h of a paged sequence (a tile never
-// crosses a page). Page ids are clamped into the pool, so a corrupt table cannot send a
-// load outside it.
-template <typename C>
-__device__ __forceinline__ void issue_kv_paged(const char *kpool, const char *vpool,
-                                               const int32_t *seq_table, int num_pages, int H,
-                                               int h, const unsigned (&off)[C::LPW], int kv0,
-                                               int Nkv, char *kdst, char *vdst, int wave)
+// Page id of entry pidx of a sequence's page-table row, clamped into the pool (a corrupt
+// table cannot send a load outside it). Read through the constant address space with a
+// uniform address, i.e. by a scalar load: its wait (lgkmcnt) leaves the K/V tiles in flight
+// alone, whereas a vector load completes in order after them and waiting for it would
+// drain the ring.
+__device__ __forceinline__ int page_id(const int32_t *seq_table, int num_pages, int pidx)
 {
-    kv0 = __builtin_amdgcn_readfirstlane(kv0);
-    // The page id is read through the constant address space with a uniform address, i.e.
-    // by a scalar load: its wait (lgkmcnt) leaves the K/V tiles in flight alone, whereas a
-    // vector load completes in order after them and waiting for it would drain the ring.
     typedef __attribute__((address_space(4))) const int32_t const_i32;
-    int pid = __builtin_amdgcn_readfirstlane(((const_i32 *)seq_table)[kv0 / kPageTokens]);
-    pid = min(max(pid, 0), num_pages - 1);
+    const int pid = __builtin_amdgcn_readfirstlane(((const_i32 *)seq_table)[pidx]);
+    return min(max(pid, 0), num_pages - 1);
+}
+
+// The K and V tiles of keys [kv0, kv0 + 32) of head h of a paged sequence, in page pid (a
+// tile never crosses a page).
+template <typename C>
+__device__ __forceinline__ void issue_kv_paged(const char *kpool, const char *vpool, int pid,
+                                               int H, int h, const unsigned (&off)[C::LPW],
+                                               int kv0, int Nkv, char *kdst, char *vdst,
+                                               int wave)
+{
     const size_t tok = (size_t)pid * kPageTokens + (size_t)(kv0 % kPageTokens);
     const size_t at = (tok * (size_t)H + (size_t)h) * C::ROWB;
     const int rows = min(Nkv - kv0, C::BN);

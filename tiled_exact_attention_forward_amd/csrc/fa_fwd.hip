@@ -309,10 +309,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
                  16 * (i < C::KL ? k_swz<D>(r, pc) : v_swz<D>(r, pc));
     }
     const int32_t *seq_table = PAGED ? pg.table + (size_t)seq * pg.max_pages : nullptr;
+    // Paged: a page holds kPageTokens / BN tiles, so the current page's id is kept and the
+    // next page's id is read when the walk enters a page; it is then at hand when the walk
+    // moves on, and only a jump (a gap in the visible tiles) waits for a lookup.
+    const int last_page = (Nkv - 1) / kPageTokens;
+    int pidx_cur = -2, pid_cur = 0, pid_next = 0;
     auto load_tile = [&](int tl, int slot) {
         if constexpr (PAGED) {
-            issue_kv_paged<C>(kbh, vbh, seq_table, pg.num_pages, pg.H, head, off, tl * BN, Nkv,
-                              kslot(slot), vslot(slot), wave);
+            const int kv0 = __builtin_amdgcn_readfirstlane(tl * BN);
+            const int pidx = kv0 / kPageTokens;
+            if (pidx != pidx_cur) {
+                pid_cur = pidx == pidx_cur + 1 ? pid_next : page_id(seq_table, pg.num_pages, pidx);
+                pidx_cur = pidx;
+                pid_next = page_id(seq_table, pg.num_pages, min(pidx + 1, last_page));
+            }
+            issue_kv_paged<C>(kbh, vbh, pid_cur, pg.H, head, off, kv0, Nkv, kslot(slot),
+                              vslot(slot), wave);
         } else if constexpr (KVL == kKvTwoPart) {
             const int kv0 = __builtin_amdgcn_readfirstlane(tl * BN);
             if (kv0 < pg.n1) {
