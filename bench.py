@@ -138,9 +138,8 @@ def load_clock(kernel_key):
 
 
 def backward_traffic(workload):
-    """Summed counter-measured HBM bytes of the three backward kernels, when measured."""
-    parts = [load_traffic(f"bwd_{k}_bf16_d128{m}_{workload}")
-             for k, m in (("rowdot", ""), ("dkdv", "_mask0"), ("dq", "_mask0"))]
+    """Summed counter-measured HBM bytes of the two backward kernels, when measured."""
+    parts = [load_traffic(f"bwd_{k}_bf16_d128_mask0_{workload}") for k in ("dq", "dkdv")]
     return None if any(p is None for p in parts) else sum(parts)
 
 
@@ -495,7 +494,7 @@ def main():
                 cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
                 cold_tflops=round(r["cold_tflops"], 2),
                 traffic=backward_traffic(name),
-                note="fa_backward (3 kernels); 10*d FLOPs per visible pair")
+                note="fa_backward (2 kernels); 10*d FLOPs per visible pair")
             print(f"[bench] backward {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
             del r

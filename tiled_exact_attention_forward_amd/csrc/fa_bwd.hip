@@ -7,20 +7,20 @@
 // forward pass, P = exp(S - LSE) is rebuilt tile by tile, and with D_i = dO_i . O_i
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),   dK = scale dS^T Q,   dQ = scale dS K.
 //
-// gfx950 mapping: three kernels, no atomics (results are deterministic).
-//  * bwd_rowdot_kernel: D_i = sum_c dO_ic O_ic and the log2-domain row statistic
-//    L_i = LSE_i log2 e (+inf for a row without a visible key, so its P is 0), stored per
-//    32-row tile so that one 256-byte load brings a tile's statistics.
+// gfx950 mapping: two kernels, no atomics (results are deterministic).
+//  * bwd_dq_kernel runs first: a workgroup owns 128 query rows (4 waves x 32) with Q and dO
+//    in registers. Its prologue also reads O and forms the row statistics the gradient needs,
+//    D_i = sum_c dO_ic O_ic and L_i = LSE_i log2 e (+inf for a row without a visible key, so
+//    its P is 0), and stores them per 32-row tile so that one 256-byte load brings a tile's
+//    statistics to the dK/dV kernel. It then walks the visible 32-key tiles like the forward
+//    pass: S^T = K Q^T and dP^T = V dO^T with lanes indexed by row, then dQ^T += K^T dS^T.
 //  * bwd_dkdv_kernel: a workgroup owns 256 keys (4 waves x 64) with their K and V rows in
 //    registers and walks the 32-row query tiles that can see them. It computes S = Q K^T and
 //    dP = dO V^T with lanes indexed by key, so that P and dS convert in place into the B
 //    operand of dV^T += dO^T P and dK^T += Q^T dS; Q^T and dO^T come from LDS through
 //    ds_read_b64_tr_b16.
-//  * bwd_dq_kernel: a workgroup owns 128 query rows (4 waves x 32) with Q and dO in
-//    registers and walks the visible 32-key tiles like the forward pass: S^T = K Q^T and
-//    dP^T = V dO^T with lanes indexed by row, then dQ^T += K^T dS^T.
-// Tiles stream from HBM to LDS with buffer_load ... lds through 4-slot rings. Scores, P, dS and all accumulators are fp32; P and dS are rounded to the
-// input type for the products.
+// Tiles stream from HBM to LDS with buffer_load ... lds through 4-slot rings. Scores, P, dS
+// and all accumulators are fp32; P and dS are rounded to the input type for the products.
 #include "fa_device.h"
 
 namespace teaf {
@@ -39,49 +39,6 @@ constexpr int kStatsBytes = 256;
 __host__ __device__ inline size_t stats_index(size_t bh, int nt32, int row)
 {
     return ((size_t)bh * nt32 + (size_t)(row >> 5)) * 64 + (size_t)(row & 31);
-}
-
-// D_i and L_i for every row (padding rows of the last tile included): 16 lanes per row, 8
-// elements each for d = 128 (4 for d = 64).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restrict__ O,
-                                                         const uint16_t *__restrict__ dO,
-                                                         const float *__restrict__ LSE,
-                                                         float *__restrict__ ST, int Nq,
-                                                         int nt32, long padded_rows)
-{
-    constexpr int PER = D / 16;
-    const long pr = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int part = threadIdx.x & 15;
-    const long per_bh = (long)nt32 * 32;
-    const long bh = pr / per_bh;
-    const int rr = (int)(pr % per_bh);
-    const bool valid = pr < padded_rows && rr < Nq;
-    float acc = 0.f;
-    if (valid) {
-        const size_t r = (size_t)bh * Nq + rr;
-        const uint16_t *o = O + r * D + part * PER;
-        const uint16_t *g = dO + r * D + part * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const T a = __builtin_bit_cast(T, o[e]);
-            const T b = __builtin_bit_cast(T, g[e]);
-            acc = __builtin_fmaf((float)a, (float)b, acc);
-        }
-    }
-    // sum over the 16 lanes of a row
-#pragma unroll
-    for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
-    if (pr < padded_rows && part == 0) {
-        const size_t at = stats_index(bh, nt32, rr);
-        float l = INFINITY;
-        if (valid) {
-            const float lse = LSE[(size_t)bh * Nq + rr];
-            l = lse == -INFINITY ? INFINITY : lse * kLog2e;
-        }
-        ST[at] = l;
-        ST[at + 32] = valid ? acc : 0.f;
-    }
 }
 
 // Byte offsets (relative to a tile) of the transposed 16-bit reads that hand each lane four
@@ -531,8 +488,9 @@ template <typename T, int D, int MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ ST, uint16_t *__restrict__ dQ, int Nq, int Nkv, float c,
-    float scale, int W, int G, int nqt, int nt32)
+    const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ ST,
+    uint16_t *__restrict__ dQ, int Nq, int Nkv, float c, float scale, int W, int G, int nqt,
+    int nt32)
 {
     using C = CfgSP<D, kDqStages, 4>;
     using Op = Ops16<T>;
@@ -549,18 +507,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int row = q0 + wave * 32 + li, ip = row + (Nkv - Nq);
     const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
 
-    s16x8 qf[NKK], gf[NKK];
+    s16x8 qf[NKK], gf[NKK], of[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         if (row < Nq) {
             qf[kk] = *(const s16x8 *)(Q + qbase + (size_t)row * D + 16 * kk + 8 * g);
             gf[kk] = *(const s16x8 *)(dO + qbase + (size_t)row * D + 16 * kk + 8 * g);
+            of[kk] = *(const s16x8 *)(O + qbase + (size_t)row * D + 16 * kk + 8 * g);
         } else {
-            qf[kk] = gf[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            qf[kk] = gf[kk] = of[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
     }
-    const float lrow = row < Nq ? ST[stats_index(bh, nt32, row)] : INFINITY;
-    const float drow = row < Nq ? ST[stats_index(bh, nt32, row) + 32] : 0.f;
+    // Row statistics: lanes i and i + 32 hold complementary halves of row i's columns.
+    auto tof = [](short x) -> float {
+        if constexpr (__is_same(T, __bf16))
+            return __uint_as_float((unsigned)(unsigned short)x << 16);
+        else
+            return (float)__builtin_bit_cast(_Float16, x);
+    };
+    float dpart = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf(tof(gf[kk][e]), tof(of[kk][e]), dpart);
+    const float drow = half_swap_sum(dpart);  // 0 for rows past Nq (zero fragments)
+    float lrow = INFINITY;
+    if (row < Nq) {
+        const float lse = LSE[(size_t)bh * Nq + row];
+        lrow = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    }
+    // Stored for the dK/dV kernel, which runs next, for every row of the 32-row tiles (rows
+    // past Nq hold L = +inf, so their P is 0, and D = 0).
+    if (g == 0 && row < nt32 * 32) {
+        ST[stats_index(bh, nt32, row)] = lrow;
+        ST[stats_index(bh, nt32, row) + 32] = drow;
+    }
 
     const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);
     const int ntl = sch.total, nint = sch.interior;
@@ -622,14 +603,21 @@ template <typename T, int D, int MASK>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s)
 {
     const int nt32 = (a.Nq + 31) / 32;
-    const long padded = (long)a.B * a.H * nt32 * 32;
     float *st = (float *)a.workspace;
-    hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((padded + 15) / 16)),
-                       dim3(256), 0, s, (const uint16_t *)a.o, (const uint16_t *)a.dout, a.lse,
-                       st, a.Nq, nt32, padded);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const float c = a.scale * kLog2e;
+    // dQ first: it also writes the row statistics the dK/dV kernel reads.
+    using CB = CfgSP<D, kDqStages, 4>;
+    const int nqt = (a.Nq + 127) / 128;
+    auto kb = bwd_dq_kernel<T, D, MASK>;
+    hipError_t e = hipFuncSetAttribute((const void *)kb,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, CB::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kb, dim3((unsigned)((long)nqt * a.B * a.H)), dim3(256), CB::LDS_BYTES, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (const uint16_t *)a.dout, (const uint16_t *)a.o, a.lse, st,
+                       (uint16_t *)a.dq, a.Nq, a.Nkv, c, a.scale, a.window, a.n_global, nqt, nt32);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     using CA = CfgBD<D>;
     const int nkt = (a.Nkv + 255) / 256;
     const int lds_a = CA::LDS_BYTES + kBwdStages * kStatsBytes + 256 * CA::ROWB;
@@ -640,18 +628,6 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s)
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        (const uint16_t *)a.dout, st, (uint16_t *)a.dk, (uint16_t *)a.dv, a.Nq,
                        a.Nkv, c, a.scale, a.window, a.n_global, nkt, nt32);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    using CB = CfgSP<D, kDqStages, 4>;
-    const int nqt = (a.Nq + 127) / 128;
-    auto kb = bwd_dq_kernel<T, D, MASK>;
-    e = hipFuncSetAttribute((const void *)kb, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            CB::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kb, dim3((unsigned)((long)nqt * a.B * a.H)), dim3(256), CB::LDS_BYTES, s,
-                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       (const uint16_t *)a.dout, st, (uint16_t *)a.dq, a.Nq, a.Nkv, c, a.scale,
-                       a.window, a.n_global, nqt, nt32);
     return hipGetLastError();
 }
 
