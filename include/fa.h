@@ -138,8 +138,9 @@ int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o
  *                 (per-row D and log2-scaled LSE, grouped by 32-row tile); contents need no
  *                 initialisation; 16-byte aligned.
  *  Supported: d in {64, 128}; masks FA_MASK_NONE .. FA_MASK_PREFIX_LM; sizes as fa_forward.
- *  Three kernels run on `stream` (row statistics, then dK/dV, then dQ); no atomics, so the
- *  results are bitwise reproducible. All tensor pointers need 16-byte alignment.
+ *  Two kernels run on `stream`: dQ (which also forms the row statistics into the
+ *  workspace), then dK/dV; no atomics, so the results are bitwise reproducible. All tensor
+ *  pointers need 16-byte alignment.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int Nq);
 
