@@ -124,6 +124,30 @@ struct TileSchedule {
     {
         return c.t + 1 < c.end ? Cursor{c.k, c.t + 1, c.end} : seek(c.k + 1);
     }
+    // The cursor at schedule position p (past the end: the end cursor, as seek gives).
+    __device__ __forceinline__ Cursor at(int p) const
+    {
+        Cursor c{kRanges, 0, 0};
+        int base = 0;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < kRanges; ++q) {
+            const int n = e[q] - b[q];
+            if (!found && p < base + n) {
+                c = Cursor{q, b[q] + p - base, e[q]};
+                found = true;
+            }
+            base += n;
+        }
+        return c;
+    }
+    // Tile at position p < interior: the interior ranges are ranges 0 and 1 (either may be
+    // empty), so no walk over the ranges.
+    __device__ __forceinline__ int interior_tile(int p) const
+    {
+        const int n0 = e[0] - b[0];
+        return p < n0 ? b[0] + p : b[1] + (p - n0);
+    }
 };
 
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }

@@ -414,26 +414,30 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
             nullptr, vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, l, mt, c, false, 0, ip,
             Nkv, W, G, g);
     };
-    // Steady state (most steps): the step loads tile t + NS - 1, the next tile needs no
-    // element mask, and the wait is for one tile in flight: no branches on any of these.
+    // Steady state (most steps): the step loads tile t + NS - 1, an interior tile (so its
+    // index is found without walking the ranges), the next tile needs no element mask, and
+    // the wait is for one tile in flight: no branches on any of these. The cursors are not
+    // advanced here; the general loops below start from cursors set by position.
     auto steady = [&](int t, f32x16 &cur, f32x16 &nxt) {
-        const int tl = MASK == kBlockSparse ? bs_tile(t + NS - 1) : ld.t;
-        load_tile(tl, t + NS - 1);
-        ld = sch.next(ld);
+        const int p = t + NS - 1;
+        load_tile(MASK == kBlockSparse ? bs_tile(p) : sch.interior_tile(p), p);
         sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, true>(
             kslot(t + 1), vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, l, mt, c, false,
             0, ip, Nkv, W, G, g);
-        nx = sch.next(nx);
         wait_tiles<LPW, NS - 3>(NS - 3);
         ring_barrier();
     };
     if (ntl > 0) {
         int t = 0;
-        for (; t + 3 + NS - 1 < ntl && t + 4 < nint; t += 4) {
+        for (; t + 3 + NS - 1 < nint; t += 4) {
             steady(t, sa, sb);
             steady(t + 1, sb, sa);
             steady(t + 2, sa, sb);
             steady(t + 3, sb, sa);
+        }
+        if (t > 0) {
+            ld = sch.at(t + NS - 1);
+            nx = sch.at(t + 1);
         }
         for (; t + 4 < ntl; t += 4) {
             step(t, sa, sb);
