@@ -582,7 +582,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     for (int j = 0; j < NS - 1; ++j) load(j);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile 0 (and the Q, dO rows)
     ring_barrier();
-    for (int n = 0; n < ntl; ++n) {
+    // Steady state (like the forward's): tiles n .. n + 3 unmasked and their look-ahead loads
+    // interior, so the tile index comes from the schedule position, the mask is compiled
+    // out, and the loop is unrolled by the ring depth (slot offsets are constants).
+    static_assert(NS == 4, "the steady loop is unrolled by the ring depth");
+    auto steady = [&](int n) {
+        const int p = n + NS - 1;
+        issue_kv<C>(kb, vb, off, sch.interior_tile(p) * BN, Nkv, kslot(p), vslot(p), wave);
+        dq_step<T, C, MASK>(kslot(n), vslot(n), qf, gf, dqt, kofs, tro, c, lrow, drow, false, 0,
+                            ip, Nkv, W, G, g);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile n + 1 resident
+        ring_barrier();
+    };
+    int n = 0;
+    for (; n + 3 + NS - 1 < nint; n += 4) {
+        steady(n);
+        steady(n + 1);
+        steady(n + 2);
+        steady(n + 3);
+    }
+    if (n > 0) {
+        ld = sch.at(n + NS - 1);
+        cur = sch.at(n);
+    }
+    for (; n < ntl; ++n) {
         load(n + NS - 1);
         dq_step<T, C, MASK>(kslot(n), vslot(n), qf, gf, dqt, kofs, tro, c, lrow, drow, n >= nint,
                             cur.t * BN, ip, Nkv, W, G, g);
