@@ -374,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile 0, the K and V rows
     ring_barrier();
 
-    for (int n = 0; n < ntl; ++n) {
+    auto step = [&](int n) {
         load(n + NS - 1);
         const char *qt = qslot(n), *gt = gslot(n);
         const float *st = (const float *)sslot(n);
@@ -384,7 +384,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         // tile n + 1 resident (the NS - 2 tiles after it may still be in flight), then publish
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));
         ring_barrier();
+    };
+    // unrolled by the ring depth, so the slot offsets are constants
+    static_assert(NS == 4, "the main loop is unrolled by the ring depth");
+    int n = 0;
+    for (; n + 3 < ntl; n += 4) {
+        step(n);
+        step(n + 1);
+        step(n + 2);
+        step(n + 3);
     }
+    for (; n < ntl; ++n) step(n);
     // Every wave's loads (the empty ones past the last tile included) have landed before any
     // wave reuses the ring for the output rows, and before the workgroup exits.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
