@@ -347,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int ntl = rhi > rlo ? (rhi + BN - 1) / BN - t0 : 0;
     const char *qb = (const char *)(Q + qbase);
     const char *gb = (const char *)(dO + qbase);
-    const float *stb = ST + (size_t)bh * nt32 * 64;
+    [[maybe_unused]] const float *stb = ST + (size_t)bh * nt32 * 64;  // device code only
     auto qslot = [&](int n) { return lds + (n % NS) * C::TILEB; };
     auto gslot = [&](int n) { return lds + C::VREG + (n % NS) * C::TILEB; };
     auto sslot = [&](int n) { return lds + C::LDS_BYTES + (n % NS) * kStatsBytes; };
@@ -503,7 +503,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     int nt32)
 {
     using C = CfgSP<D, kDqStages, 4>;
-    using Op = Ops16<T>;
     constexpr int BM = 128, BN = 32, NKK = C::NKK, NDB = C::NDB, NS = kDqStages, LPW = C::LPW;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char *const lds = (char *)smem;

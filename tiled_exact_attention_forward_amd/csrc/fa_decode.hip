@@ -35,7 +35,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kD = 128;        // head dimension
 constexpr int kPage = 256;     // tokens per page
-constexpr int kBatch = 8;      // tokens per thread kept in flight
 constexpr int kThreads = 256;
 
 template <typename T>
