@@ -199,8 +199,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     if (KVL == kKvTwoPart) kvbase = (size_t)bh * pg.n1 * D;
     int lstride = 1, seq = 0, head = 0;
     if constexpr (PAGED) {
-        seq = bh / pg.H;
-        head = bh % pg.H;
+        // (sequence, head) pairs in head-major order: the consecutive pairs an XCD receives
+        // are a few heads of every sequence, so sequences of different lengths spread
+        // evenly over the XCDs (a sequence per XCD left one XCD with the longest history);
+        // the query tiles of a pair stay together on one XCD.
+        const int nseq = (int)gridDim.x / (nqt * pg.H);
+        seq = bh % nseq;
+        head = bh / nseq;
         Nkv = min(__builtin_amdgcn_readfirstlane(pg.seq_lens[seq]), pg.max_pages * kPageTokens);
         Nq = min(min(__builtin_amdgcn_readfirstlane(pg.q_lens[seq]), pg.Qmax), Nkv);
         if (q0 >= Nq) return;  // the whole workgroup: this chunk is shorter
