@@ -199,13 +199,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     if (KVL == kKvTwoPart) kvbase = (size_t)bh * pg.n1 * D;
     int lstride = 1, seq = 0, head = 0;
     if constexpr (PAGED) {
-        // (sequence, head) pairs in head-major order: the consecutive pairs an XCD receives
-        // are a few heads of every sequence, so sequences of different lengths spread
-        // evenly over the XCDs (a sequence per XCD left one XCD with the longest history);
-        // the query tiles of a pair stay together on one XCD.
+        // (sequence, head) pairs are spread so that every XCD receives H/8 heads of every
+        // sequence (a sequence per XCD left the XCD with the longest history last), and
+        // within an XCD's share the pairs go sequence by sequence with adjacent heads, so
+        // the pairs running side by side read neighbouring heads of the same pages (the
+        // same head of different sequences sits at the same offset in pages 2 MB apart and
+        // competes for the same L2 sets). The query tiles of a pair stay on one XCD.
         const int nseq = (int)gridDim.x / (nqt * pg.H);
-        seq = bh % nseq;
-        head = bh / nseq;
+        if (pg.H % kXcds == 0) {
+            const int hx = pg.H / kXcds, per = nseq * hx;  // heads per sequence per XCD
+            const int x = bh / per, k = bh % per;
+            seq = k / hx;
+            head = hx * ((x + seq) % kXcds) + k % hx;
+        } else {
+            seq = bh % nseq;
+            head = (bh / nseq + seq * max(1, pg.H / nseq)) % pg.H;
+        }
         Nkv = min(__builtin_amdgcn_readfirstlane(pg.seq_lens[seq]), pg.max_pages * kPageTokens);
         Nq = min(min(__builtin_amdgcn_readfirstlane(pg.q_lens[seq]), pg.Qmax), Nkv);
         if (q0 >= Nq) return;  // the whole workgroup: this chunk is shorter
