@@ -31,7 +31,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
-DATASHEET_GHZ = 2.4         # the clock that peak assumes
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PAGES_BF16_TFLOPS = 1.25    # pages' Ascend 910 bf16 time for this workload, as TFLOP/s
 CSRC = "tiled_exact_attention_forward_amd/csrc/"
@@ -121,20 +120,6 @@ def load_traffic(kernel_key):
     if e is None or e.get("source_hash") != kernel_source_hash(e.get("sources")):
         return None
     return e.get("bytes_per_launch")
-
-
-def load_clock(kernel_key):
-    """Shader clock (GHz) measured with rocprofv3 counters while that kernel ran, if taken
-    on its current sources."""
-    path = os.path.join(ROOT, "profiles", "clock.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        t = json.load(f)
-    e = t.get("kernels", {}).get(kernel_key)
-    if e is None or e.get("source_hash") != kernel_source_hash(e.get("sources")):
-        return None
-    return e.get("ghz")
 
 
 def backward_traffic(workload):
@@ -524,8 +509,9 @@ def main():
 
     w = head["w"]
     achieved = head["flops"] / (head["ms"] * 1e-3) / 1e12
-    kernel_key = f"fwd16_bf16_d{w['d']}_mask{w['mask']}_{args.workload}"
-    clock = load_clock(kernel_key)
+    kernel_key = f"fwd16_{w['dtype']}_d{w['d']}_mask{w['mask']}_{args.workload}"
+    mask_name = {0: "none", 1: "causal", 2: "window+global", 3: "band", 4: "prefix LM",
+                 5: "block sparse"}[w["mask"]]
     line = {
         "metric": "attention fwd TFLOP/s & % bf16 MFMA peak; paged-decode HBM GB/s",
         "value": round(head["tflops"], 3),
@@ -550,16 +536,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic(kernel_key),
-                     "kernel": "fwd16_kernel<bf16, 128, mask none>",
+                     "kernel": f"fwd16_kernel<{w['dtype']}, d={w['d']}, mask {mask_name}>",
                      "flops_per_launch": head["flops"],
                      "algorithmic_bytes_per_launch": head["bytes"],
-                     # the datasheet peak assumes 2.4 GHz; the same peak at the clock the
-                     # counters measured while this kernel ran
-                     "clock_ghz_measured": clock,
-                     "peak_at_measured_clock": None if clock is None else
-                     round(PEAK_BF16_TFLOPS * clock / DATASHEET_GHZ, 1),
-                     "frac_at_measured_clock": None if clock is None else
-                     round(achieved / (PEAK_BF16_TFLOPS * clock / DATASHEET_GHZ), 4)},
+                     # the same kernel with L2 and MALL flushed before each call (median)
+                     "achieved_cold": round(head["cold_tflops"], 3),
+                     "frac_cold": round(head["cold_tflops"] / PEAK_BF16_TFLOPS, 4)},
         "cpu_baseline": None if base is None else {
             k: (round(v, 6) if isinstance(v, float) else v) for k, v in base.items()},
         "workloads": others,

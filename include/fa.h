@@ -23,7 +23,9 @@
  *    reported as FA_ERR_HIP. Faults inside a kernel surface at the caller's next
  *    synchronisation, as for any HIP work.
  *  - Contents of device buffers (page tables, sequence lengths) cannot be checked on the
- *    host; out-of-range values there are undefined behaviour.
+ *    host. The paged entry points clamp page ids into the pool and lengths into their
+ *    documented ranges, so a corrupt table gives wrong values but no access outside the
+ *    buffers.
  */
 #ifndef TEAF_FA_H
 #define TEAF_FA_H
@@ -222,6 +224,9 @@ int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_im
  *              the per-split partial results (split-KV); contents need no initialisation.
  *  Supported: page_size == 256, d == 128, dtype FA_F16 or FA_BF16, H a multiple of 8.
  *  The kernels never read page slots at or past seq_lens[s], nor unused table entries.
+ *  Page ids outside [0, num_pages) are clamped into the pool (wrong values, never a read
+ *  outside it); a length past max_pages_per_seq*page_size counts as that maximum, and a
+ *  length below 1 gives o = 0 and lse = -inf for that sequence.
  *  Two kernels run on `stream`: the split pass writes partial (O, LSE) per split of
  *  the keys; the combine pass merges them by log-sum-exp and writes o and lse.
  */

@@ -1,20 +1,31 @@
-"""Tile-shape sweep of the 16-bit forward kernel (MI355X).
+"""Forward-kernel sweeps on one MI355X: tile shapes, and problem shapes for the per-round fit.
 
-The kernel's tile shape is fixed at compile time: W waves of 32 query rows per workgroup
+Tile sweep. The kernel's tile shape is fixed at compile time: W waves of 32 query rows per workgroup
 (query tile BM = 32 W) and an S-slot LDS ring of 32-key K/V tiles (32 S keys of K and V on
 chip per workgroup). The pages tune the query and key block sizes of their kernel by
 measurement (ops-transformer article on gitcode.csdn.net, section 三.1, block-size table);
 this script repeats that for gfx950: it builds the library once per (W, S) and times each
 build on the same inputs.
 
-    python -m tiled_exact_attention_forward_amd.tile_sweep --build   # hipcc, no GPU needed
-    python -m tiled_exact_attention_forward_amd.tile_sweep --run     # on the GPU
+    python sweep.py tiles --build    # hipcc, no GPU needed; builds go to _build/sweep/
+    python sweep.py tiles --run      # on the GPU
 
 Workloads: causal bf16 B4 H32 N4096 d128 (inputs 0.5 N(0,1)) and dense bf16 B4 H32 N1024
 d128. Each build's output is compared with the default build's (the shapes change only the
 order of the online-softmax updates). Timing: at least one second of calls before each
 measurement (the clock rises under load), builds measured in rotated order over several
 rounds, median reported.
+
+Shape sweep. The forward launches one workgroup per 128-row query tile; with two workgroups
+per CU a 256-CU MI355X runs 512 at once, so B * H * N / 128 tiles take B * H * N / 65536
+rounds, and each workgroup walks N / 32 key tiles of 32 keys (steps). Timing dense bf16
+attention (H 32, d 128, N(0,1) inputs) over shapes with 1 to 8 rounds and 32 to 128 steps and
+fitting  time = a + b * rounds + c * rounds * steps  separates the cost of a round of
+workgroups (Q loads and first tiles, output stores) from the cost of the steps themselves.
+Every measurement follows at least a second of calls; the median of 5 batches of 20
+back-to-back calls is reported.
+
+    python sweep.py shapes           # on the GPU, the in-tree library
 """
 import argparse
 import concurrent.futures as cf
@@ -25,9 +36,11 @@ import subprocess
 import sys
 import time
 
-from . import build as lib_build
+import numpy as np
 
-OUT = os.path.join(lib_build.PKG, "_sweep")
+from tiled_exact_attention_forward_amd import build as lib_build
+
+OUT = os.path.join(lib_build.BUILD, "sweep")
 # (waves, ring slots): LDS per workgroup is 16 KB per slot; 160 KB per CU.
 VARIANTS = [(2, 3), (4, 3), (4, 4), (4, 5), (8, 4), (8, 6), (8, 8)]
 
@@ -131,14 +144,70 @@ def run_all(rounds):
                   f"{flops / us / 1e6:.0f} | {d:.1e} |", flush=True)
 
 
+SHAPES = [(2, 1024), (4, 1024), (8, 1024), (16, 1024), (2, 2048), (4, 2048), (2, 4096),
+          (4, 4096)]
+
+
+def run_shapes():
+    import torch
+
+    import tiled_exact_attention_forward_amd as fa
+    fa.load_library()
+    H, D, concurrent = 32, 128, 512
+    g = torch.Generator(device="cpu").manual_seed(1)
+    rows = []
+    print("| B | N | rounds | steps per workgroup | us per call | TFLOP/s |")
+    print("|---|---|---|---|---|---|")
+    for B, N in SHAPES:
+        q, k, v = [torch.randn((B, H, N, D), generator=g).to(torch.bfloat16).cuda()
+                   for _ in range(3)]
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+
+        def call():
+            fa.fa_forward(q, k, v, D ** -0.5, fa.FA_MASK_NONE, out=o, lse=lse)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 20 * 1e3)
+        us = statistics.median(ts)
+        rounds, steps = B * H * N / 128 / concurrent, N // 32
+        rows.append((B, N, rounds, steps, us))
+        print(f"| {B} | {N} | {rounds:g} | {steps} | {us:.1f} | "
+              f"{4.0 * B * H * N * N * D / us / 1e6:.0f} |", flush=True)
+    A = np.array([[1.0, r, r * s] for _, _, r, s, _ in rows])
+    y = np.array([u for *_, u in rows])
+    c, *_ = np.linalg.lstsq(A, y, rcond=None)
+    step_flops = 4.0 * concurrent * 128 * 32 * D
+    print(f"fit: {c[0]:.2f} us + {c[1]:.2f} us per round + {c[2]:.4f} us per step and round "
+          f"(the steps at {step_flops / c[2] / 1e6:.0f} TFLOP/s)")
+    for (B, N, r, s, u), p in zip(rows, A @ c):
+        print(f"  B {B} N {N}: {u:.1f} us measured, {p:.1f} us fitted")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--build", action="store_true", help="build every variant (no GPU needed)")
-    ap.add_argument("--run", action="store_true", help="time every built variant on the GPU")
+    ap.add_argument("what", choices=["tiles", "shapes"])
+    ap.add_argument("--build", action="store_true", help="tiles: build every variant (no GPU)")
+    ap.add_argument("--run", action="store_true", help="tiles: time every built variant")
     ap.add_argument("--rounds", type=int, default=5)
     a = ap.parse_args()
+    if a.what == "shapes":
+        run_shapes()
+        return 0
     if not (a.build or a.run):
-        ap.error("give --build and/or --run")
+        ap.error("tiles: give --build and/or --run")
     if a.build:
         build_all()
     if a.run:

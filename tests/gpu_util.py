@@ -1,4 +1,4 @@
-"""Helpers for the GPU parity tests: device transfer, tolerances and sampled rows.
+"""Helpers for the GPU parity tests: device transfer and tolerances.
 
 Tolerances (stated once, used by every GPU parity test):
   * fp16 / bf16 outputs: max |O_gpu - O_ref| <= 1e-2 over every compared element and
@@ -44,8 +44,10 @@ def errors(o_gpu, lse_gpu, o_ref, lse_ref):
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lg), fin), "LSE finiteness differs"
     diff = np.abs(og - o_ref)
+    worst = np.unravel_index(int(np.argmax(diff)), diff.shape) if diff.size else ()
     return dict(
         o_max_abs=float(diff.max()) if diff.size else 0.0,
+        o_worst_at=tuple(int(x) for x in worst),
         o_ref_max=float(np.abs(o_ref).max()) if o_ref.size else 0.0,
         o_rel_l2=float(np.linalg.norm(og - o_ref) / max(np.linalg.norm(o_ref), 1e-300)),
         lse_max_abs=float(np.abs(lg[fin] - lse_ref[fin]).max()) if fin.any() else 0.0,
@@ -66,22 +68,3 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
         assert e["lse_max_abs"] <= LSE_ABS, f"{label}: {e}"
         assert e["o_rel_l2"] <= REL_L2[dtype], f"{label}: {e}"
     return e
-
-
-def sample_rows(B, H, Nq, tile_edges=(0, 1, 2, 31, 32, 63, 64, 127, 128, 129), extra=(),
-                per_head=16, seed=0):
-    """Flat row ids ((b*H+h)*Nq + i): fixed edge rows in every (b,h) plus random rows."""
-    rng = np.random.default_rng(seed)
-    fixed = sorted({i for i in list(tile_edges) + list(extra) + [Nq - 1, Nq - 2] if 0 <= i < Nq})
-    rows = []
-    for bh in range(B * H):
-        pick = set(fixed) | set(rng.integers(0, Nq, per_head).tolist())
-        rows.extend(bh * Nq + i for i in sorted(pick))
-    return np.array(rows, dtype=np.int64)
-
-
-def gather_rows(o, lse, rows):
-    d = o.shape[-1]
-    of = o.reshape(-1, d)[torch.as_tensor(rows, device=o.device)]
-    lf = lse.reshape(-1)[torch.as_tensor(rows, device=lse.device)]
-    return of, lf

@@ -1,9 +1,9 @@
 """Block-sparse forward (fa_forward_block_sparse) against the fp64 oracle on the GPU.
 
 Small shapes compare every element over random layouts (including query blocks with no
-visible key block, and ragged query and key tails); the full-size workload compares sampled
-rows that include the first and last rows of several query blocks. An all-ones layout must
-reproduce the unmasked forward pass bit for bit (same kernel, same tile order).
+visible key block, and ragged query and key tails); the full-size workload compares every
+element. An all-ones layout must reproduce the unmasked forward pass bit for bit (same
+kernel, same tile order).
 """
 import zlib
 
@@ -14,7 +14,7 @@ import torch
 import oracle
 import tiled_exact_attention_forward_amd as fa
 import workloads
-from gpu_util import check, f64, gather_rows, require_gpu, sample_rows, to_dev
+from gpu_util import check, f64, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -91,15 +91,12 @@ def test_never_reads_past_the_keys(dtype):
     check(o, lse, ro, rl, dtype, "nan canary block sparse")
 
 
-def test_full_size_sampled_rows():
+@pytest.mark.timeout(600)
+def test_full_size_every_element():
     w, inp = workloads.gen_workload("blocksparse_bf16")
     scale = workloads.default_scale(w["d"])
     o, lse = run_bs(inp["q"], inp["k"], inp["v"], inp["layout"], scale)
-    extra = (0, 127, 128, 255, 8191, 8192, 16255, 16256, 16383)
-    rows = sample_rows(w["B"], w["H"], w["Nq"], extra=extra, per_head=24, seed=w["seed"])
     ro, rl = oracle.attention_block_sparse(inp["q"], inp["k"], inp["v"], scale,
-                                           inp["layout"].numpy(), w["block"], rows=rows)
-    og, lg = gather_rows(o, lse, rows)
-    e = check(og, lg, ro, rl, w["dtype"], "blocksparse_bf16")
-    print("blocksparse_bf16", len(rows), "rows", e)
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+                                           inp["layout"].numpy(), w["block"])
+    e = check(o, lse, ro, rl, w["dtype"], "blocksparse_bf16")
+    print("blocksparse_bf16", e)

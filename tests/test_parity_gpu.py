@@ -2,19 +2,17 @@
 
 Small shapes compare every element and span several tiles plus ragged tails; the full-size
 workloads run in the same launch configuration the benchmark times and compare every
-element (dense, decode) or sampled rows that include every tile and mask edge (causal,
-window). Tolerances are stated in gpu_util.
+element as well. Tolerances are stated in gpu_util.
 """
 import zlib
 
-import numpy as np
 import pytest
 import torch
 
 import oracle
 import tiled_exact_attention_forward_amd as fa
 import workloads
-from gpu_util import check, f64, gather_rows, require_gpu, sample_rows, to_dev
+from gpu_util import check, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -99,26 +97,19 @@ def test_dense_full_size_every_element(name):
     print(name, e)
 
 
-@pytest.mark.parametrize("name,extra", [
-    ("causal_bf16", (255, 256, 257, 1023, 1024, 2047, 2048, 4094)),
-    ("window_bf16", (62, 63, 64, 65, 2046, 2047, 2048, 2049, 2110, 2111, 2112, 2113, 4095,
-                     4096, 16383, 16384, 32766)),
-    ("band_bf16", (0, 1, 2047, 2048, 2049, 4095, 4096, 16384, 30718, 30719, 30720, 32766,
-                   32767)),
-    ("prefix_bf16", (0, 1, 127, 128, 1022, 1023, 1024, 1025, 2047, 4095)),
-])
-def test_masked_full_size_sampled_rows(name, extra):
+# Every output element of the long masked workloads, in the launch configuration the
+# benchmark times. The oracle covers them in about a minute on 16 host threads (causal 550
+# GFLOP, window 1.1 TFLOP, band 2.1 TFLOP, prefix 0.6 TFLOP at 4 d FLOPs per visible pair).
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["causal_bf16", "window_bf16", "band_bf16", "prefix_bf16"])
+def test_masked_full_size_every_element(name):
     w, inp = workloads.gen_workload(name)
     scale = workloads.default_scale(w["d"])
     o, lse = run_fwd(inp["q"], inp["k"], inp["v"], scale, w["mask"], w["window"], w["n_global"])
-    rows = sample_rows(w["B"], w["H"], w["Nq"], extra=extra, per_head=24, seed=w["seed"])
     ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], scale, w["mask"], w["window"],
-                              w["n_global"], rows=rows)
-    og, lg = gather_rows(o, lse, rows)
-    e = check(og, lg, ro, rl, w["dtype"], name)
-    print(name, len(rows), "rows", e)
-    # every row, including those not sampled: finite, and LSE at least the largest score
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+                              w["n_global"])
+    e = check(o, lse, ro, rl, w["dtype"], name)
+    print(name, e)
 
 
 def test_decode_full_size_every_element():

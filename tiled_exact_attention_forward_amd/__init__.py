@@ -150,6 +150,12 @@ def _check_dev(name, t, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_shape(name, t, shape):
+    """Host-side shape check (before any pointer reaches the library)."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def fa_forward(q, k, v, scale=None, mask_mode=FA_MASK_NONE, window=0, n_global=0, out=None,
                lse=None, stream=None):
     """O, LSE = attention(q, k, v) with q [B,H,Nq,d], k/v [B,H,Nkv,d] (f32/f16/bf16).
@@ -162,6 +168,8 @@ def fa_forward(q, k, v, scale=None, mask_mode=FA_MASK_NONE, window=0, n_global=0
     Nkv = k.shape[2]
     if tuple(k.shape) != (B, H, Nkv, d) or tuple(v.shape) != (B, H, Nkv, d):
         raise ValueError("k and v must be [B,H,Nkv,d] matching q")
+    _check_shape("out", out, q.shape)
+    _check_shape("lse", lse, (B, H, Nq))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -192,6 +200,8 @@ def fa_forward_block_sparse(q, k, v, layout, block=128, scale=None, out=None, ls
     want = (H, -(-Nq // block), -(-Nkv // block))
     if tuple(layout.shape) != want or not layout.is_contiguous():
         raise ValueError(f"layout must be a contiguous {want} tensor")
+    _check_shape("out", out, q.shape)
+    _check_shape("lse", lse, (B, H, Nq))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -227,6 +237,9 @@ def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, windo
         raise ValueError("o and dout must have q's shape")
     if tuple(lse.shape) != (B, H, Nq):
         raise ValueError("lse must be [B,H,Nq]")
+    _check_shape("dq", dq, q.shape)
+    _check_shape("dk", dk, k.shape)
+    _check_shape("dv", dv, v.shape)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -255,11 +268,27 @@ def fa_decode_paged_workspace_bytes(num_seqs, H, d, max_pages_per_seq, page_size
         int(num_seqs), int(H), int(d), int(max_pages_per_seq), int(page_size)))
 
 
+def _check_decode_shapes(q, k_pages, v_pages, page_table, seq_lens, out, lse):
+    S, H, d = q.shape
+    if k_pages.dim() != 4:
+        raise ValueError("k_pages must be [num_pages, page_size, H, d]")
+    P, page_size = k_pages.shape[0], k_pages.shape[1]
+    _check_shape("k_pages", k_pages, (P, page_size, H, d))
+    _check_shape("v_pages", v_pages, (P, page_size, H, d))
+    if page_table.dim() != 2 or page_table.shape[0] != S:
+        raise ValueError(f"page_table must be [{S}, max_pages_per_seq], got "
+                         f"{tuple(page_table.shape)}")
+    _check_shape("seq_lens", seq_lens, (S,))
+    _check_shape("out", out, (S, H, d))
+    _check_shape("lse", lse, (S, H))
+
+
 def fa_decode_paged(q, k_pages, v_pages, page_table, seq_lens, scale=None, out=None, lse=None,
                     workspace=None, stream=None):
     """Single-token decode: q [S,H,d]; pages [P,page_size,H,d]; page_table [S,max_pages]
     int32; seq_lens [S] int32 (all on the GPU). Returns (out [S,H,d], lse [S,H] float32)."""
     torch = _torch()
+    _check_decode_shapes(q, k_pages, v_pages, page_table, seq_lens, out, lse)
     S, H, d = q.shape
     P, page_size = k_pages.shape[0], k_pages.shape[1]
     max_pages = page_table.shape[1]
@@ -299,6 +328,13 @@ def fa_prefill_paged(q, k_pages, v_pages, page_table, seq_lens, q_lens, scale=No
     P, page_size = k_pages.shape[0], k_pages.shape[1]
     if tuple(k_pages.shape) != (P, page_size, H, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
         raise ValueError("k_pages and v_pages must be [num_pages, page_size, H, d]")
+    if page_table.dim() != 2 or page_table.shape[0] != S:
+        raise ValueError(f"page_table must be [{S}, max_pages_per_seq], got "
+                         f"{tuple(page_table.shape)}")
+    _check_shape("seq_lens", seq_lens, (S,))
+    _check_shape("q_lens", q_lens, (S,))
+    _check_shape("out", out, (S, Qmax, H, d))
+    _check_shape("lse", lse, (S, Qmax, H))
     max_pages = page_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -328,6 +364,8 @@ def fa_merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse=None, stream=None):
     if tuple(o_b.shape) != tuple(o_a.shape) or tuple(lse_a.shape) != tuple(o_a.shape[:-1]) \
             or tuple(lse_b.shape) != tuple(lse_a.shape):
         raise ValueError("o_a, o_b [..., d] and lse_a, lse_b [...] must match")
+    _check_shape("out", out, o_a.shape)
+    _check_shape("lse", lse, lse_a.shape)
     out = torch.empty_like(o_a) if out is None else out
     lse = torch.empty_like(lse_a) if lse is None else lse
     for name, t in (("o_a", o_a), ("o_b", o_b), ("out", out)):

@@ -77,19 +77,20 @@ __device__ __forceinline__ s16x8 stream_load(const uint16_t *p)
 
 // Split pass. grid (H / HW, max_splits, S), 256 threads; a workgroup owns SPLIT
 // consecutive tokens (inside one page) of one sequence for HW heads. A page stores
-// [token][head][d], so the HW heads of one token are HW * 256 bytes contiguous (the whole
-// 8 KB row when HW = H = 32): thread t reads 16-byte chunk t % 16 of head (t / 16) % HW'
-// and its 16 apart companions, and each wave-wide load covers 1 KB contiguous.
-//   HW = 32: 2 heads per thread, all 256 threads on one token;
-//   HW = 16: 1 head per thread, all 256 threads on one token;
-//   HW = 8 : 1 head per thread, two token lanes (tokens tl, tl + 2, ...).
-// Loads run one batch of tokens ahead of the math (two register buffers).
+// [token][head][d], so the HW heads of one token are HW * 256 bytes contiguous: thread t
+// reads 16-byte chunk t % 16 of head (t / 16) % HW, and each wave-wide load covers 1 KB
+// contiguous.
+//   HW = 16: one head per thread, all 256 threads on one token;
+//   HW = 8 : one head per thread, two token lanes (tokens tl, tl + 2, ...).
+// Loads run one batch of tokens ahead of the math (two register buffers). The page id is
+// clamped into the pool, so a corrupt table entry gives wrong values but never a read
+// outside the pool (as in the chunked prefill).
 template <typename T, int HW, int SPLIT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t *__restrict__ Qp, const uint16_t *__restrict__ Kp,
     const uint16_t *__restrict__ Vp, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, float *__restrict__ part_o,
-    float *__restrict__ part_lse, int H, int max_pages, int max_splits, float c)
+    float *__restrict__ part_lse, int H, int max_pages, int num_pages, int max_splits, float c)
 {
     constexpr int PAIRS = HW * 16;                       // (head, chunk) pairs per token
     constexpr int HPT = PAIRS > kThreads ? PAIRS / kThreads : 1;   // heads per thread
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int hr = (tid >> 4) % (HW < 16 ? HW : 16);
     const int tl = TL > 1 ? tid / PAIRS : 0;
     const int ntok = min(SPLIT, L - t0);
-    const int page = page_table[(size_t)s * max_pages + t0 / kPage];
+    const int page = min(max(page_table[(size_t)s * max_pages + t0 / kPage], 0), num_pages - 1);
     const int slot0 = t0 % kPage;
     const size_t tstride = (size_t)H * kD;  // elements between consecutive tokens
     size_t base[HPT];
@@ -216,10 +217,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
 }
 
-// grid (S, H); 256 threads = 4 groups of 64. Group q takes splits q, q + 4, ...; thread
-// (q, i) accumulates columns 2i and 2i+1 over them, issuing the loads of up to 32 splits at
-// once, then the groups are summed through LDS. Partial lse values are in log2 units.
-// Combine: one wave per (sequence, head); lane i owns columns 2i and 2i+1. The partial
+// Combine: grid (S, H), one wave per (sequence, head); lane i owns columns 2i and 2i+1.
+// Partial lse values are in log2 units. The partial
 // results of up to kCombineBatch splits are loaded together (one memory round trip per
 // batch), and the merge keeps a running maximum of the partial lse values, rescaling the
 // running sums when a later batch raises it, so no separate pass finds the maximum first.
@@ -281,7 +280,7 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t st, int max_splits, flo
                        dim3((unsigned)(a.H / HW), (unsigned)max_splits, (unsigned)a.S),
                        dim3(kThreads), 0, st, (const uint16_t *)a.q, (const uint16_t *)a.k_pages,
                        (const uint16_t *)a.v_pages, a.page_table, a.seq_lens, part_o, part_lse,
-                       a.H, a.max_pages, max_splits, a.scale * kLog2e);
+                       a.H, a.max_pages, a.num_pages, max_splits, a.scale * kLog2e);
     return hipGetLastError();
 }
 
