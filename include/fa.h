@@ -12,10 +12,11 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers (HIP device memory) owned by the caller. The
- *    library allocates nothing and is thread-safe. Its only mutable state is the HIP error
- *    code of the last failed launch, kept per calling thread (see fa_last_hip_error);
- *    raising a kernel's dynamic LDS limit (an idempotent runtime attribute) happens on
- *    every launch.
+ *    library allocates nothing and is thread-safe. Its mutable state is the HIP error code
+ *    of the last failed launch, kept per calling thread (see fa_last_hip_error), and the
+ *    per-GPU address of the static scratch array of fa_decode_paged_noalloc (looked up
+ *    once per GPU, under a lock); raising a kernel's dynamic LDS limit (an idempotent
+ *    runtime attribute) happens on every launch.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). All work is
  *    enqueued on it; calls return before the work completes.
  *  - Return value: FA_OK (0) or a negative fa_status. Argument checks run on the host BEFORE
@@ -43,7 +44,8 @@ typedef enum {
     FA_ERR_SHAPE = -2,       /* a size is out of range (B, H, N < 1, window < 1, ...) */
     FA_ERR_UNSUPPORTED = -3, /* valid but not built: head dim, dtype, mask, page size */
     FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query function says */
-    FA_ERR_HIP = -5          /* the HIP runtime refused a launch */
+    FA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
+    FA_ERR_SCRATCH = -6      /* fa_decode_paged_noalloc: more than its static scratch */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -238,6 +240,31 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     int page_size, int num_seqs, int H, int d, int max_pages_per_seq,
                     int num_pages, float scale, int dtype, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * fa_decode_paged_noalloc -- fa_decode_paged without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It calls no allocating routine: the split partials go to a
+ * file-scope static device array of 16 MiB inside the library, one per GPU, held until the
+ * process ends (its address is looked up once per GPU, on the first call there).
+ *
+ *  Arguments as fa_decode_paged, without workspace and workspace_bytes; same kernels,
+ *  same results bit for bit.
+ *  Limit: the partials take num_seqs * H * ceil(max_pages_per_seq * 256 / split) * (d + 1)
+ *  * 4 bytes, split being the token run per workgroup the launch picks (256, 128 or 64:
+ *  the longest that still gives at least 512 workgroups). Every call with
+ *  num_seqs * H * max_pages_per_seq <= 8128 fits; larger ones fit when the longer splits
+ *  are picked (up to 32512 at split 256). A call that does not fit returns FA_ERR_SCRATCH
+ *  before anything is launched.
+ *  Concurrency: every call on one GPU uses that GPU's one array, so calls that can overlap
+ *  on a GPU (other streams, other threads) race and must be serialised by the caller.
+ *  Nothing in the array needs clearing between calls.
+ */
+int fa_decode_paged_noalloc(const void *q, const void *k_pages, const void *v_pages,
+                            const int32_t *page_table, const int32_t *seq_lens, void *o,
+                            float *lse, int page_size, int num_seqs, int H, int d,
+                            int max_pages_per_seq, int num_pages, float scale, int dtype,
+                            void *stream);
 
 /*
  * fa_prefill_paged -- multi-token (chunked) prefill against the paged KV cache of

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert fa.fa_status_string(0) == "ok"
-    for s in (-1, -2, -3, -4, -5):
+    for s in (-1, -2, -3, -4, -5, -6):
         assert fa.fa_status_string(s) and fa.fa_status_string(s) != "unknown status"
     assert fa.fa_status_string(42) == "unknown status"
     assert fa.fa_version() >= 10000
@@ -89,6 +89,27 @@ def dec(q=P, kp=P, vp=P, pt=P, sl=P, o=P, lse=N, page=256, S=8, H=32, d=128, max
 ])
 def test_decode_rejects_before_launch(kw, status):
     assert dec(**kw) == status
+
+
+def dec_noalloc(q=P, kp=P, vp=P, pt=P, sl=P, o=P, lse=N, page=256, S=8, H=32, d=128, maxp=32,
+                npages=300, scale=0.088, dtype=1):
+    return fa.load_library().fa_decode_paged_noalloc(q, kp, vp, pt, sl, o, lse, page, S, H, d,
+                                                     maxp, npages, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=N), fa.FA_ERR_NULL), (dict(pt=N), fa.FA_ERR_NULL), (dict(o=N), fa.FA_ERR_NULL),
+    (dict(S=0), fa.FA_ERR_SHAPE), (dict(maxp=0), fa.FA_ERR_SHAPE),
+    (dict(page=128), fa.FA_ERR_UNSUPPORTED), (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(H=12), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+    # partials beyond the 16 MiB static array, even at the longest split (256 tokens), which
+    # these sizes pick: 64 x 64 x 64 pages take 135 MB, 32 x 32 x 64 pages 33.8 MB
+    (dict(S=64, H=64, maxp=64), fa.FA_ERR_SCRATCH),
+    (dict(S=32, H=32, maxp=64), fa.FA_ERR_SCRATCH),
+])
+def test_decode_noalloc_rejects_before_launch(kw, status):
+    assert dec_noalloc(**kw) == status
 
 
 def bs(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nkv=8, d=64, scale=0.125, layout=P,

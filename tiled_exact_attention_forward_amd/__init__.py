@@ -8,6 +8,7 @@ C ABI declared in include/fa.h. The functions carry the C names:
     fa_backward(q, k, v, o, lse, dout, ...)  gradients dQ, dK, dV
     fa_backward_workspace_bytes(...)
     fa_decode_paged(q, k_pages, ...)  single-token decode against a paged K/V cache
+    fa_decode_paged_noalloc(...)      the same without a workspace (library's static scratch)
     fa_prefill_paged(q, k_pages, ...) multi-token chunk per sequence against a paged cache
     fa_merge_lse(o_a, lse_a, o_b, lse_b, ...)  merge results over disjoint key sets
     fa_multimodal_forward(...)        image/text attention as three calls plus a merge
@@ -24,7 +25,7 @@ import math
 import os
 
 __all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_bytes",
-           "fa_decode_paged", "fa_prefill_paged", "fa_merge_lse", "fa_multimodal_forward",
+           "fa_decode_paged", "fa_decode_paged_noalloc", "fa_prefill_paged", "fa_merge_lse", "fa_multimodal_forward",
            "fa_multimodal_workspace_bytes", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
            "FA_F32", "FA_F16", "FA_BF16", "FA_MASK_NONE", "FA_MASK_CAUSAL",
@@ -33,11 +34,13 @@ __all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
+FA_ERR_SCRATCH = -6
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
 FA_MULTIMODAL_SPLIT_MERGE, FA_MULTIMODAL_FUSED = 0, 1
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_backward",
-                    "fa_backward_workspace_bytes", "fa_decode_paged", "fa_prefill_paged",
+                    "fa_backward_workspace_bytes", "fa_decode_paged", "fa_decode_paged_noalloc",
+                    "fa_prefill_paged",
                     "fa_merge_lse", "fa_multimodal_forward", "fa_multimodal_workspace_bytes",
                     "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_last_hip_error",
                     "fa_version")
@@ -85,6 +88,9 @@ def load_library():
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
                                     vp]
     lib.fa_decode_paged.restype = i
+    lib.fa_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
+                                            vp]
+    lib.fa_decode_paged_noalloc.restype = i
     lib.fa_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i,
                                      i, i, i, vp]
     lib.fa_prefill_paged.restype = i
@@ -281,6 +287,35 @@ def _check_decode_shapes(q, k_pages, v_pages, page_table, seq_lens, out, lse):
     _check_shape("seq_lens", seq_lens, (S,))
     _check_shape("out", out, (S, H, d))
     _check_shape("lse", lse, (S, H))
+
+
+def fa_decode_paged_noalloc(q, k_pages, v_pages, page_table, seq_lens, scale=None, out=None,
+                            lse=None, stream=None):
+    """fa_decode_paged with the split partials in the library's static scratch (no
+    workspace). `out` and `lse` should be given by callers that must not allocate; calls
+    on one GPU must not overlap. Returns (out, lse)."""
+    torch = _torch()
+    _check_decode_shapes(q, k_pages, v_pages, page_table, seq_lens, out, lse)
+    S, H, d = q.shape
+    P, page_size = k_pages.shape[0], k_pages.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("out", out)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("page_table", page_table, torch.int32)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    _check_dev("lse", lse, torch.float32)
+    rc = load_library().fa_decode_paged_noalloc(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table), _ptr(seq_lens), _ptr(out),
+        _ptr(lse), page_size, S, H, d, page_table.shape[1], P, float(scale), _dtype_code(q),
+        _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_decode_paged_noalloc")
+    return out, lse
 
 
 def fa_decode_paged(q, k_pages, v_pages, page_table, seq_lens, scale=None, out=None, lse=None,

@@ -38,6 +38,8 @@ const char *fa_status_string(int status)
     case FA_ERR_UNSUPPORTED: return "valid arguments that this build does not support";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "the HIP runtime rejected a launch";
+    case FA_ERR_SCRATCH:
+        return "the call needs more scratch than the library's static array holds";
     default: return "unknown status";
     }
 }
@@ -265,11 +267,16 @@ size_t fa_decode_paged_workspace_bytes(int num_seqs, int H, int d, int max_pages
     return (size_t)num_seqs * H * splits * ((size_t)d + 1) * sizeof(float);
 }
 
-int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
-                    const int32_t *page_table, const int32_t *seq_lens, void *o, float *lse,
-                    int page_size, int num_seqs, int H, int d, int max_pages_per_seq,
-                    int num_pages, float scale, int dtype, void *workspace,
-                    size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode entry points (everything but the scratch memory); on
+// success fills *a with a null workspace.
+int check_decode(const void *q, const void *k_pages, const void *v_pages,
+                 const int32_t *page_table, const int32_t *seq_lens, void *o, float *lse,
+                 int page_size, int num_seqs, int H, int d, int max_pages_per_seq, int num_pages,
+                 float scale, int dtype, teaf::DecodeArgs *a)
 {
     if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !o) return FA_ERR_NULL;
     if (num_seqs < 1 || H < 1 || max_pages_per_seq < 1 || num_pages < 1 || page_size < 1)
@@ -279,15 +286,50 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
     if (H % teaf::kDecodeHeads != 0) return FA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || H / teaf::kDecodeHeads > 65535) return FA_ERR_SHAPE;
     if ((long long)num_pages * page_size * H * d > (long long)1 << 40) return FA_ERR_SHAPE;
+    if ((long long)max_pages_per_seq * page_size > (1ll << 30)) return FA_ERR_SHAPE;
     if (!(scale == scale)) return FA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
         return FA_ERR_UNSUPPORTED;
+    *a = teaf::DecodeArgs{q, k_pages, v_pages, page_table, seq_lens, o, lse, page_size,
+                          num_seqs, H, d, max_pages_per_seq, num_pages, scale, dtype, nullptr};
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *page_table, const int32_t *seq_lens, void *o, float *lse,
+                    int page_size, int num_seqs, int H, int d, int max_pages_per_seq,
+                    int num_pages, float scale, int dtype, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    teaf::DecodeArgs a;
+    const int rc = check_decode(q, k_pages, v_pages, page_table, seq_lens, o, lse, page_size,
+                                num_seqs, H, d, max_pages_per_seq, num_pages, scale, dtype, &a);
+    if (rc != FA_OK) return rc;
     const size_t need =
         fa_decode_paged_workspace_bytes(num_seqs, H, d, max_pages_per_seq, page_size);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_WORKSPACE;
-    teaf::DecodeArgs a{q, k_pages, v_pages, page_table, seq_lens, o, lse, page_size,
-                       num_seqs, H, d, max_pages_per_seq, num_pages, scale, dtype, workspace};
+    a.workspace = workspace;
+    return hip_status(teaf::launch_decode(a, (hipStream_t)stream));
+}
+
+int fa_decode_paged_noalloc(const void *q, const void *k_pages, const void *v_pages,
+                            const int32_t *page_table, const int32_t *seq_lens, void *o,
+                            float *lse, int page_size, int num_seqs, int H, int d,
+                            int max_pages_per_seq, int num_pages, float scale, int dtype,
+                            void *stream)
+{
+    teaf::DecodeArgs a;
+    const int rc = check_decode(q, k_pages, v_pages, page_table, seq_lens, o, lse, page_size,
+                                num_seqs, H, d, max_pages_per_seq, num_pages, scale, dtype, &a);
+    if (rc != FA_OK) return rc;
+    if (teaf::decode_partials_bytes(a) > teaf::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+    const hipError_t e = teaf::decode_static_scratch((hipStream_t)stream, &a.workspace);
+    if (e != hipSuccess) return hip_status(e);
     return hip_status(teaf::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -22,6 +22,8 @@
 // cannot leak into the result.
 #include <math.h>
 
+#include <mutex>
+
 #include "fa_launch.h"
 
 namespace teaf {
@@ -284,45 +286,95 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t st, int max_splits, flo
     return hipGetLastError();
 }
 
+int splits_for(const DecodeArgs &a, int split)
+{
+    return (int)(((long)a.max_pages * kPage + split - 1) / split);
+}
+
 template <typename T, int HW>
 hipError_t launch_width(const DecodeArgs &a, hipStream_t st, int split, float *part_o,
                         float *part_lse)
 {
-    const int max_splits = (int)(((long)a.max_pages * kPage + split - 1) / split);
+    const int max_splits = splits_for(a, split);
     if (split == 256) return launch_split<T, HW, 256>(a, st, max_splits, part_o, part_lse);
     if (split == 128) return launch_split<T, HW, 128>(a, st, max_splits, part_o, part_lse);
     return launch_split<T, HW, 64>(a, st, max_splits, part_o, part_lse);
 }
 
-// Largest split (fewer, longer streams and fewer partials; measured fastest on the 8 x
-// 4096..8192-token workload) that still gives at least kMinSplitGroups workgroups when
-// every sequence is as long as the page table allows.
 constexpr long kMinSplitGroups = 512;
+
+// Split length the launch uses: the largest (fewer, longer streams and fewer partials;
+// measured fastest on the 8 x 4096..8192-token workload) that still gives at least
+// kMinSplitGroups workgroups when every sequence is as long as the page table allows.
+int pick_split(const DecodeArgs &a)
+{
+    const int hw = a.H % 16 == 0 ? 16 : 8;
+    for (int cand = 256; cand > 64; cand /= 2)
+        if ((long)a.S * (a.H / hw) * (((long)a.max_pages * kPage) / cand) >= kMinSplitGroups)
+            return cand;
+    return 64;
+}
 
 template <typename T>
 hipError_t launch(const DecodeArgs &a, hipStream_t st)
 {
     const int hw = a.H % 16 == 0 ? 16 : 8;
-    int split = 64;
-    for (int cand = 256; cand > 64; cand /= 2)
-        if ((long)a.S * (a.H / hw) * (((long)a.max_pages * kPage) / cand) >= kMinSplitGroups) {
-            split = cand;
-            break;
-        }
-    const int ws_splits = decode_workspace_splits(a.max_pages, a.page_size);
+    const int split = pick_split(a);
+    const int max_splits = splits_for(a, split);
+    // partial O [S, H, max_splits, d] then partial lse [S, H, max_splits], both fp32
     float *part_o = (float *)a.workspace;
-    float *part_lse = part_o + (size_t)a.S * a.H * ws_splits * kD;
+    float *part_lse = part_o + (size_t)a.S * a.H * max_splits * kD;
     const hipError_t e = hw == 16 ? launch_width<T, 16>(a, st, split, part_o, part_lse)
                                   : launch_width<T, 8>(a, st, split, part_o, part_lse);
     if (e != hipSuccess) return e;
-    const int max_splits = (int)(((long)a.max_pages * kPage + split - 1) / split);
     hipLaunchKernelGGL(decode_combine_kernel<T>, dim3((unsigned)a.S, (unsigned)a.H),
                        dim3(kCombineThreads), 0, st, part_o, part_lse, a.seq_lens,
                        (uint16_t *)a.o, a.lse, a.H, max_splits, split);
     return hipGetLastError();
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
 }  // namespace
+
+// Scratch of the allocation-free decode entry point: the split partials live in this
+// file-scope device array instead of a caller's workspace. Each GPU holds its own copy until
+// the process ends; every call on a GPU reuses it (nothing needs clearing: the split pass
+// writes every partial the combine pass reads).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+size_t decode_partials_bytes(const DecodeArgs &a)
+{
+    return (size_t)a.S * a.H * splits_for(a, pick_split(a)) * (kD + 1) * sizeof(float);
+}
+
+// Device address of `scratch` on the device `st` runs on (found once per device, with that
+// device current; in host code the array's name is not a device address).
+hipError_t decode_static_scratch(hipStream_t st, void **ptr)
+{
+    int dev = 0, cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (st != nullptr && (e = hipStreamGetDevice(st, &dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st)
 {

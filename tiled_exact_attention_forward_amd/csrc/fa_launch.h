@@ -40,6 +40,9 @@ constexpr int kDecodeMinSplit = 64;
 // Heads of one workgroup of the split pass: 16 when H is a multiple of 16, else 8.
 constexpr int kDecodeHeads = 8;
 
+// Static scratch of the allocation-free decode (file-scope device array, one per GPU).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+
 inline int decode_workspace_splits(int max_pages, int page_size)
 {
     long tokens = (long)max_pages * page_size;
@@ -91,6 +94,11 @@ inline size_t backward_workspace_floats(int B, int H, int Nq)
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// Bytes of split partials launch_decode places in a.workspace for these arguments (never
+// more than the workspace size fa_decode_paged_workspace_bytes reports).
+size_t decode_partials_bytes(const DecodeArgs &a);
+// Device address of the decode's static scratch on the device `stream` runs on.
+hipError_t decode_static_scratch(hipStream_t stream, void **ptr);
 hipError_t launch_prefill_paged(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 // Causal forward (16-bit types) whose keys are [0, n1) from a.k/a.v ([B,H,n1,d]) and
