@@ -252,3 +252,26 @@ def test_checker_rejects_planted_mistakes(name, tmp_path):
     check(o, lse, go, gl, "bf16" if not cfg.get("decode") else "f16", "good oracle")
     with pytest.raises(AssertionError):
         check(o, lse, ro, rl, "bf16" if not cfg.get("decode") else "f16", f"mutant {name}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("mask", [(0, 0, 0), (1, 0, 0), (2, 70, 0), (3, 20, 0)])
+@pytest.mark.parametrize("slope", [0.5, 3.0, 40.0])
+def test_rising_scores_rescale(dtype, mask, slope):
+    """Scores that grow from key tile to key tile, so that a later tile's probabilities
+    against the reference taken from an earlier tile overflow every bound (fp16 P tops out
+    at 65504) unless the running maximum is raised: q . k_j = slope * j / 32 (natural units
+    after the scale), plus noise. Compared with the oracle over several query tiles, with
+    rows whose first visible key lies past their first key tile (band and window masks)."""
+    N, d = 300, 128
+    g = torch.Generator("cpu").manual_seed(int(slope * 10) + 7 * mask[0])
+    q = torch.zeros((1, 2, N, d))
+    k = torch.randn((1, 2, N, d), generator=g) * 0.05
+    v = torch.randn((1, 2, N, d), generator=g) * 0.25  # |O| < 1, as the 1e-2 bound assumes
+    q[..., 0] = 1.0
+    k[..., 0] += slope * torch.arange(N, dtype=torch.float32) / 32 * 8.0  # scale 1/8
+    t = workloads.DTYPES[dtype]
+    q, k, v = q.to(t), k.to(t), v.to(t)
+    o, lse = fwd(q, k, v, 0.125, *mask)
+    ro, rl = oracle.attention(q, k, v, 0.125, *mask)
+    check(o, lse, ro, rl, dtype, f"rising {dtype} {mask} slope {slope}")

@@ -325,12 +325,6 @@ __device__ __forceinline__ int v_swz(int row, int chunk)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The running maximum is only moved (and O, l rescaled) when a row's new maximum exceeds
-// the one in use by more than this many powers of two; until then probabilities are taken
-// relative to the stale maximum and stay below 2^8, which fp32 sums and 16-bit P hold
-// exactly as well. The result is the same softmax: numerator and denominator share the
-// reference value, and the final division removes it.
-constexpr float kRescaleSlack = 8.0f;
 
 // Each wave owns 32 query rows and walks 32-key tiles, software-pipelined: while the
 // matrix cores form the scores of tile t+1, the vector unit turns the scores of tile t into

@@ -40,66 +40,84 @@
 namespace teaf {
 namespace {
 
-// One pipeline step for tile t. sc: raw scores of tile t (masked if needed), mt its
-// scaled row maximum. m: running scaled row maximum, nmu = -m (0 while m is -inf), both
-// changed only when the maximum moves. NEXT: there is a tile t+1 (K in LDS at kn);
-// mask_next: it needs the element mask (wave-uniform). vslot_ofs: where V of tile t sits in
-// the V ring (bytes from the ring's first slot); vptr: this lane's V^T read addresses in
-// the first slot.
+// Online softmax without a per-tile row maximum. The probabilities of tile t are formed as
+// 2^(c s - m) against the reference m in use, and the tile's row sums (formed anyway for l)
+// are checked before the probabilities are used: while every partial sum of 16 probabilities
+// stays at most the bound, every probability is below it, so fp32 sums of up to 2^31 keys,
+// P in the input type and the fp32 accumulator all stay finite and keep their relative
+// precision, and the result is the same softmax (numerator and denominator share the
+// reference, the final division removes it). The bound is 2^64 for bf16 (fp32's exponent
+// range) and 2^15 for fp16, whose largest finite value is 65504. A sum above the bound, an
+// infinity or a NaN, or any visible key for a row that had none (its reference is still
+// -inf; there the bound is 0), sends the wave to the rare exact path: the tile's scores are
+// formed again, the reference becomes the true running maximum and the accumulator and sum
+// are rescaled. This takes no maximum over the scores of ordinary tiles: the first tile of a
+// query tile sets the reference.
+template <typename T>
+constexpr float sum_bound()
+{
+    return __is_same(T, _Float16) ? 32768.f : 18446744073709551616.f;
+}
+
+// One pipeline step for tile t. sc: raw scores of tile t (masked if needed). m: scaled
+// reference maximum, nmu = -m (0 while m is -inf), bnd: the row-sum bound (0 while m is
+// -inf); all three change only on the rare path. NEXT: there is a tile t+1 (K in LDS at kn);
+// mask_next: it needs the element mask (wave-uniform), kvn its first key. kc: K of tile t
+// (for the rare path), mask_cur and kvc: its mask and first key. vslot_ofs: where V of tile t
+// sits in the V ring (bytes from the ring's first slot); vptr: this lane's V^T read addresses
+// in the first slot.
 template <typename T, typename C, int MASK, bool NEXT>
-__device__ __forceinline__ void sp_step(const char *__restrict__ kn, unsigned vslot_ofs,
-                                        const int (&kofs)[C::NKK],
+__device__ __forceinline__ void sp_step(const char *__restrict__ kn, const char *__restrict__ kc,
+                                        unsigned vslot_ofs, const int (&kofs)[C::NKK],
                                         const lds_char *const (&vptr)[C::NDB],
                                         const s16x8 (&qf)[C::NKK], f32x16 (&oacc)[C::NDB],
-                                        f32x16 &sc, f32x16 &sn, float &m, float &nmu, float &l,
-                                        float &mt, float c, bool mask_next, int kvn, int ip,
-                                        int Nkv, int W, int G, int g)
+                                        f32x16 &sc, f32x16 &sn, float &m, float &nmu, float &bnd,
+                                        float &l, float c, bool mask_cur, int kvc,
+                                        bool mask_next, int kvn, int ip, int Nkv, int W, int G,
+                                        int g)
 {
     using Op = Ops16<T>;
     constexpr int NKK = C::NKK, NDB = C::NDB, KPF = C::KPF, VPF = C::VPF;
     constexpr int EPK = 16 / NKK;   // probabilities formed per score instruction
     constexpr int NF = 2 * NDB;     // P V matrix instructions
 
-    // K fragment reads for the first matrix instructions go out before the rescale test.
     s16x8 kf[NKK];
     if (NEXT) {
 #pragma unroll
         for (int f = 0; f < KPF; ++f) kf[f] = *(const s16x8 *)(kn + kofs[f]);
-    }
-    if (!__all(mt <= m + kRescaleSlack)) {
-        const float mn = fmaxf(m, mt);
-        const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
-        m = mn;
-        nmu = mn == -INFINITY ? 0.f : -mn;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
     __builtin_amdgcn_sched_barrier(0);
 
     // The wave runs phase A at raised priority: of the two waves sharing a SIMD, the one
     // issuing the score MFMAs and exponentials goes first (about 1 % faster, measured).
     __builtin_amdgcn_s_setprio(1);
-    // Phase A: S(t+1) = K(t+1) Q^T, P(t) = 2^(c S(t) - m).
+    // Phase A: S(t+1) = K(t+1) Q^T; P(t) = 2^(c S(t) - m) and its row sums.
     s16x4 vlo[NF], vhi[NF];
     // V^T reads: per-lane LDS addresses made once per workgroup; the slot (a constant in
     // the unrolled loop) and the chunk enter as immediate offsets.
     auto vread = [&](int f) {
-        const int kc = f / NDB, db = f % NDB;
-        const lds_char *p0 = vptr[db] + vslot_ofs + kc * 16 * C::ROWB;
+        const int kcn = f / NDB, db = f % NDB;
+        const lds_char *p0 = vptr[db] + vslot_ofs + kcn * 16 * C::ROWB;
         vlo[f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
         vhi[f] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 8 * C::ROWB));
     };
     s16x8 pf[2];
+    float ps[4];
+    auto prob = [&](int e) { sc[e] = fast_exp2(__builtin_fmaf(sc[e], c, nmu)); };
+    auto pack = [&](int o) {
+        pf[o / 8] = Op::pack8(sc[o], sc[o + 1], sc[o + 2], sc[o + 3], sc[o + 4], sc[o + 5],
+                              sc[o + 6], sc[o + 7]);
+    };
+    auto psum = [&](int q) {
+        ps[q] = (sc[4 * q] + sc[4 * q + 1]) + (sc[4 * q + 2] + sc[4 * q + 3]);
+    };
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         // The first group's exponentials go ahead of the first score instruction, covering
         // the latency of the K fragment reads that follow the step's barrier.
         if (kk == 0) {
 #pragma unroll
-            for (int e = 0; e < EPK; ++e) sc[e] = fast_exp2(__builtin_fmaf(sc[e], c, nmu));
+            for (int e = 0; e < EPK; ++e) prob(e);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (NEXT) {
@@ -109,60 +127,52 @@ __device__ __forceinline__ void sp_step(const char *__restrict__ kn, unsigned vs
         if (kk >= NKK - VPF) vread(kk - (NKK - VPF));
 #pragma unroll
         for (int e = kk * EPK; e < (kk + 1) * EPK; ++e)
-            if (kk > 0) sc[e] = fast_exp2(__builtin_fmaf(sc[e], c, nmu));
-        if (((kk + 1) * EPK) % 8 == 0) {
-            const int o = (kk + 1) * EPK - 8;
-            pf[o / 8] = Op::pack8(sc[o], sc[o + 1], sc[o + 2], sc[o + 3], sc[o + 4], sc[o + 5],
-                                  sc[o + 6], sc[o + 7]);
-        }
+            if (kk > 0) prob(e);
+        const int done = (kk + 1) * EPK;  // probabilities formed so far
+        if (done % 4 == 0) psum(done / 4 - 1);
+        if (done % 8 == 0) pack(done - 8);
         __builtin_amdgcn_sched_barrier(0);
     }
+    float pt = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if (!__all(pt <= bnd)) {
+        // Rare path: the tile's scores again (K(t) is still in its slot), its true maximum as
+        // the new reference, the accumulator and sum rescaled, the tile's probabilities anew.
+        f32x16 s;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            s = Op::mma(*(const s16x8 *)(kc + kofs[kk]), qf[kk], kk == 0 ? f32x16{} : s);
+        if (mask_cur) mask_tile<MASK>(s, kvc, ip, Nkv, W, G, g);
+        const float mt = half_swap_max(max16(s)) * c;
+        const float mn = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+        m = mn;
+        nmu = mn == -INFINITY ? 0.f : -mn;
+        bnd = mn == -INFINITY ? 0.f : sum_bound<T>();
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        sc = s;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) prob(e);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) psum(q);
+        pack(0);
+        pack(8);
+        pt = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+    l += pt;
 
     __builtin_amdgcn_s_setprio(0);
-    // Phase B: O^T += V^T P^T(t); l += row sums of P(t); mask and maximum of S(t+1).
-    // The row sums add the fp32 probabilities (before rounding for the product).
-    float ps[4];
+    // Phase B: O^T += V^T P^T(t); the element mask of S(t+1) when it needs one.
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-        const int kc = f / NDB, db = f % NDB;
+        const int kcn = f / NDB, db = f % NDB;
         if (f + VPF < NF) vread(f + VPF);
         const s16x8 a = __builtin_shufflevector(vlo[f], vhi[f], 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = Op::mma(a, pf[kc], oacc[db]);
-        // Vector work spread over the matrix instructions. The empty asm statements pin each
-        // partial result to its slot: otherwise the row sum is sunk past the end of the step,
-        // where it delays the next step's first K fragment reads (about 1 % slower, measured).
-        if (NF == 8) {
-            if (f < 4) {
-                ps[f] = (sc[4 * f] + sc[4 * f + 1]) + (sc[4 * f + 2] + sc[4 * f + 3]);
-                __asm__ volatile("" : "+v"(ps[f]));
-            }
-            if (f == 4) {
-                l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                __asm__ volatile("" : "+v"(l));
-            }
-            if (NEXT && f == 4 && mask_next) mask_tile<MASK>(sn, kvn, ip, Nkv, W, G, g);
-            if (NEXT && f == 6) {
-                mt = half_swap_max(max16(sn)) * c;
-                __asm__ volatile("" : "+v"(mt));
-            }
-        } else {
-            if (f == 0) {
-                ps[0] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
-                ps[1] = (sc[4] + sc[5]) + (sc[6] + sc[7]);
-                __asm__ volatile("" : "+v"(ps[0]), "+v"(ps[1]));
-            }
-            if (f == 1) {
-                ps[2] = (sc[8] + sc[9]) + (sc[10] + sc[11]);
-                ps[3] = (sc[12] + sc[13]) + (sc[14] + sc[15]);
-                l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                __asm__ volatile("" : "+v"(l));
-            }
-            if (NEXT && f == 2 && mask_next) mask_tile<MASK>(sn, kvn, ip, Nkv, W, G, g);
-            if (NEXT && f == 3) {
-                mt = half_swap_max(max16(sn)) * c;
-                __asm__ volatile("" : "+v"(mt));
-            }
-        }
+        oacc[db] = Op::mma(a, pf[kcn], oacc[db]);
+        if (NEXT && f == NF / 2 && mask_next) mask_tile<MASK>(sn, kvn, ip, Nkv, W, G, g);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -383,18 +393,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
         for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = (qf[kk] ^ qsign) & keep;
     }
 
+    // The first tile's scores and their row maximum, which becomes the reference m.
     f32x16 sa, sb;
-    float mt = -INFINITY;
+    float bnd = 0.f;
+    int kv_cur = 0;  // first key of the tile the next step finishes (for its rare path)
     TileSchedule::Cursor nx = sch.begin();
     if (ntl > 0) {
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk)
             sa = Op::mma(*(const s16x8 *)(kslot(0) + kofs[kk]), qf[kk],
                          kk == 0 ? f32x16{} : sa);
-        if (nint == 0)
-            mask_tile<MASK == kBlockSparse ? 0 : MASK>(
-                sa, MASK == kBlockSparse ? tail_kv0 : nx.t * BN, ip, Nkv, W, G, g);
-        mt = half_swap_max(max16(sa)) * c;
+        kv_cur = MASK == kBlockSparse ? tail_kv0 : nx.t * BN;
+        if (nint == 0) mask_tile<MASK == kBlockSparse ? 0 : MASK>(sa, kv_cur, ip, Nkv, W, G, g);
+        const float mt = half_swap_max(max16(sa)) * c;
+        m = mt;
+        nmu = mt == -INFINITY ? 0.f : -mt;
+        bnd = mt == -INFINITY ? 0.f : sum_bound<T>();
         nx = sch.next(nx);
     }
 
@@ -416,17 +430,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     // loops has a tile t+1; the last step is peeled.
     auto step = [&](int t, f32x16 &cur, f32x16 &nxt) {
         load_ahead(t);
+        const int kvn = MASK == kBlockSparse ? tail_kv0 : nx.t * BN;
         sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, true>(
-            kslot(t + 1), vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, l, mt, c,
-            t + 1 >= nint,
-            MASK == kBlockSparse ? tail_kv0 : nx.t * BN, ip, Nkv, W, G, g);
+            kslot(t + 1), kslot(t), vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, bnd,
+            l, c, t >= nint, kv_cur, t + 1 >= nint, kvn, ip, Nkv, W, G, g);
+        kv_cur = kvn;
         nx = sch.next(nx);
         step_end(t);
     };
     auto last = [&](int t, f32x16 &cur, f32x16 &nxt) {
         sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, false>(
-            nullptr, vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, l, mt, c, false, 0, ip,
-            Nkv, W, G, g);
+            nullptr, kslot(t), vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, bnd, l, c,
+            t >= nint, kv_cur, false, 0, ip, Nkv, W, G, g);
     };
     // Steady state (most steps): the step loads tile t + NS - 1, an interior tile (so its
     // index is found without walking the ranges), the next tile needs no element mask, and
@@ -436,8 +451,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
         const int p = t + NS - 1;
         load_tile(MASK == kBlockSparse ? bs_tile(p) : sch.interior_tile(p), p);
         sp_step<T, C, MASK == kBlockSparse ? 0 : MASK, true>(
-            kslot(t + 1), vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, l, mt, c, false,
-            0, ip, Nkv, W, G, g);
+            kslot(t + 1), kslot(t), vring_ofs(t), kofs, vptr, qf, oacc, cur, nxt, m, nmu, bnd,
+            l, c, false, 0, false, 0, ip, Nkv, W, G, g);
         wait_tiles<LPW, NS - 3>(NS - 3);
         ring_barrier();
     };
