@@ -200,8 +200,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, li = lane & 31;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / nqt;
-    const int q0 = (nqt - 1 - L % nqt) * BM;  // most-loaded query tiles first
+    int bh = L / nqt;
+    int q0 = (nqt - 1 - L % nqt) * BM;  // most-loaded query tiles first
     // Row strides (elements) of Q and O, and where this workgroup's rows and LSE entries
     // start. Lengths in a paged cache are clamped to what the table and the chunk can hold.
     int rs = D;
@@ -214,13 +214,36 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
         // within an XCD's share the pairs go sequence by sequence with adjacent heads, so
         // the pairs running side by side read neighbouring heads of the same pages (the
         // same head of different sequences sits at the same offset in pages 2 MB apart and
-        // competes for the same L2 sets). The query tiles of a pair stay on one XCD.
+        // competes for the same L2 sets). The query tiles of a pair stay on one XCD and are
+        // dispatched together, so they read each K/V tile while it is in that XCD's L2.
         const int nseq = (int)gridDim.x / (nqt * pg.H);
         if (pg.H % kXcds == 0) {
             const int hx = pg.H / kXcds, per = nseq * hx;  // heads per sequence per XCD
             const int x = bh / per, k = bh % per;
             seq = k / hx;
+            // Up to 64 sequences go in order of decreasing work (chunk length times history,
+            // ties by index), so the workgroups an XCD runs side by side have similar
+            // lengths and finish together, and the query tiles of a pair start together.
+            if (nseq <= 64) {
+                const int sl = lane < nseq ? pg.seq_lens[lane] : 0;
+                const int ql = lane < nseq ? pg.q_lens[lane] : 0;
+                const long long wk = (long long)ql * (2LL * sl - ql);
+                int rank = 0;
+                for (int s2 = 0; s2 < nseq; ++s2) {
+                    const long long w2 = __shfl(wk, s2);
+                    rank += (w2 > wk || (w2 == wk && s2 < lane)) ? 1 : 0;
+                }
+                const unsigned long long hit = __ballot(lane < nseq && rank == seq);
+                seq = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+            }
             head = hx * ((x + seq) % kXcds) + k % hx;
+            // Within a pair the query tiles that hold rows come first (most loaded first),
+            // the empty ones past the chunk's end last: an empty tile exits at once, and
+            // ahead of its pair it let the next pair's tiles start before this pair's.
+            const int qlen = min(min(__builtin_amdgcn_readfirstlane(pg.q_lens[seq]), pg.Qmax),
+                                 __builtin_amdgcn_readfirstlane(pg.seq_lens[seq]));
+            const int nt = (qlen + BM - 1) / BM, i = L % nqt;
+            q0 = i < nt ? (nt - 1 - i) * BM : nqt * BM;
         } else {
             seq = bh % nseq;
             head = (bh / nseq + seq * max(1, pg.H / nseq)) % pg.H;
