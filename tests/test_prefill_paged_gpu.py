@@ -109,6 +109,28 @@ def test_prefill_paged_heads_multiple_of_8(H, mask):
     compare(out, lse, ro, rl, inp["q_lens"], "bf16", f"H{H} mask{mask}")
 
 
+@pytest.mark.parametrize("nseq", [63, 64, 65, 70])
+def test_prefill_paged_many_sequences(nseq):
+    """Up to 64 sequences are placed in order of decreasing work, more keep their index order:
+    both sides of that limit, every row of every chunk (lengths drawn per sequence, some
+    chunks empty, ties in work)."""
+    g = np.random.default_rng(nseq)
+    lens = g.integers(1, 700, nseq).tolist()
+    qls = [int(min(x, q)) for x, q in zip(lens, g.integers(0, 200, nseq))]
+    lens[1], qls[1] = lens[0], qls[0]  # a tie in work
+    qls[2] = 0                         # an empty chunk
+    inp = workloads.gen_prefill_paged(nseq, 200, 8, 128, "bf16", 1000 + nseq, max_len=700,
+                                      lens=lens, qlens=qls)
+    # Short sequences give rows that see 1-3 keys, whose outputs are single draws of V. V/4
+    # (exact in bf16) keeps |O| < 2: above 2 one bf16 step (2^-6) is wider than the 1e-2 bound.
+    inp["v_pages"] = inp["v_pages"] * 0.25
+    scale = workloads.default_scale(128)
+    out, lse = run_prefill(inp, scale, (1, 0, 0))
+    ro, rl = oracle.prefill_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
+                                  inp["seq_lens"], inp["q_lens"], scale, 1, 0, 0)
+    compare(out, lse, ro, rl, inp["q_lens"], "bf16", f"{nseq} sequences")
+
+
 @pytest.mark.timeout(600)
 def test_prefill_paged_full_size():
     """Every row of every (sequence, head) pair of the chunked-prefill workload; rows past
