@@ -402,7 +402,9 @@ __device__ __forceinline__ void issue_kv_at(const char *kt, const char *vt,
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u) {
         const int i = wave + C::NW * u;
-        if (i < C::KL)
+        // wave < NW: when NW divides KL, load u is a K load exactly when u < KL / NW, known
+        // at compile time
+        if (C::KL % C::NW == 0 ? u < C::KL / C::NW : i < C::KL)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(kdst + i * 1024), 16, off[u],
                                                      0, 0, 0);
         else
@@ -443,29 +445,16 @@ struct KvLayout {
     int n1;
 };
 
-// Page id of entry pidx of a sequence's page-table row, clamped into the pool (a corrupt
-// table cannot send a load outside it). Read through the constant address space with a
-// uniform address, i.e. by a scalar load: its wait (lgkmcnt) leaves the K/V tiles in flight
-// alone, whereas a vector load completes in order after them and waiting for it would
-// drain the ring.
-__device__ __forceinline__ int page_id(const int32_t *seq_table, int num_pages, int pidx)
-{
-    typedef __attribute__((address_space(4))) const int32_t const_i32;
-    const int pid = __builtin_amdgcn_readfirstlane(((const_i32 *)seq_table)[pidx]);
-    return min(max(pid, 0), num_pages - 1);
-}
-
-// The K and V tiles of keys [kv0, kv0 + 32) of head h of a paged sequence, in page pid (a
-// tile never crosses a page).
+// The K and V tiles of keys [kv0, kv0 + 32) of a paged sequence; page_at: byte offset of the
+// head's first row in the tile's page (a tile never crosses a page).
 template <typename C>
-__device__ __forceinline__ void issue_kv_paged(const char *kpool, const char *vpool, int pid,
-                                               int H, int h, const unsigned (&off)[C::LPW],
-                                               int kv0, int Nkv, char *kdst, char *vdst,
-                                               int wave)
+__device__ __forceinline__ void issue_kv_paged(const char *kpool, const char *vpool,
+                                               size_t page_at, int H,
+                                               const unsigned (&off)[C::LPW], unsigned kv0,
+                                               int Nkv, char *kdst, char *vdst, int wave)
 {
-    const size_t tok = (size_t)pid * kPageTokens + (size_t)(kv0 % kPageTokens);
-    const size_t at = (tok * (size_t)H + (size_t)h) * C::ROWB;
-    const int rows = min(Nkv - kv0, C::BN);
+    const size_t at = page_at + (kv0 % kPageTokens) * (unsigned)(H * C::ROWB);
+    const int rows = min(Nkv - (int)kv0, C::BN);
     const int rest = rows * H * C::ROWB;
     issue_kv_at<C>(kpool + at, vpool + at, off, rest, kdst, vdst, wave);
 }

@@ -356,21 +356,31 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
                  16 * (i < C::KL ? k_swz<D>(r, pc) : v_swz<D>(r, pc));
     }
     const int32_t *seq_table = PAGED ? pg.table + (size_t)seq * pg.max_pages : nullptr;
-    // Paged: a page holds kPageTokens / BN tiles, so the current page's id is kept and the
-    // next page's id is read when the walk enters a page; it is then at hand when the walk
-    // moves on, and only a jump (a gap in the visible tiles) waits for a lookup.
+    // Paged: the ids of 64 consecutive pages of the sequence (from page pbase) sit one per
+    // lane, so entering a page takes a register read, not a memory round trip; after 64
+    // pages (16,384 keys) the walk loads the next 64 and waits for them there, which drains
+    // the tiles in flight once. The page's offset in the pool is formed once per page.
     const int last_page = (Nkv - 1) / kPageTokens;
-    int pidx_cur = -2, pid_cur = 0, pid_next = 0;
+    unsigned pidx_cur = ~0u, pbase = 0;
+    int ptab = 0;
+    size_t page_at = 0;
+    if constexpr (PAGED) ptab = lane <= last_page ? seq_table[lane] : 0;
     auto load_tile = [&](int tl, int slot) {
         if constexpr (PAGED) {
-            const int kv0 = __builtin_amdgcn_readfirstlane(tl * BN);
-            const int pidx = kv0 / kPageTokens;
+            const unsigned kv0 = __builtin_amdgcn_readfirstlane(tl * BN);
+            const unsigned pidx = kv0 / kPageTokens;
             if (pidx != pidx_cur) {
-                pid_cur = pidx == pidx_cur + 1 ? pid_next : page_id(seq_table, pg.num_pages, pidx);
+                if (pidx - pbase >= 64u) {
+                    pbase = pidx & ~63u;
+                    ptab = (int)(pbase + lane) <= last_page ? seq_table[pbase + lane] : 0;
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                }
+                const int pid = min(max(__builtin_amdgcn_readlane(ptab, pidx - pbase), 0),
+                                    pg.num_pages - 1);
                 pidx_cur = pidx;
-                pid_next = page_id(seq_table, pg.num_pages, min(pidx + 1, last_page));
+                page_at = ((size_t)pid * kPageTokens * pg.H + head) * C::ROWB;
             }
-            issue_kv_paged<C>(kbh, vbh, pid_cur, pg.H, head, off, kv0, Nkv, kslot(slot),
+            issue_kv_paged<C>(kbh, vbh, page_at, pg.H, off, kv0, Nkv, kslot(slot),
                               vslot(slot), wave);
         } else if constexpr (KVL == kKvTwoPart) {
             const int kv0 = __builtin_amdgcn_readfirstlane(tl * BN);
