@@ -5,7 +5,8 @@ Each sequence's chunk (its newest q_lens[s] tokens) attends to its seq_lens[s] c
 with bottom-right masks. Small cases compare every row of every chunk across ragged page
 tails, empty chunks, one-token chunks and whole-sequence chunks, with head counts that are
 and are not multiples of 8 (the two work placements); the full-size chunked prefill
-workload compares every row of every (sequence, head) pair. Unused page slots and spare
+workload compares every row of every (sequence, head) pair. Histories past 64 pages
+(16,384 keys) take the kernel's reload of the page ids. Unused page slots and spare
 pages hold NaN, and Q rows past each chunk hold NaN, so reading any of them shows. Rows past
 a chunk must be left as they were. Tolerances are those of the forward (gpu_util).
 """
@@ -129,6 +130,21 @@ def test_prefill_paged_many_sequences(nseq):
     ro, rl = oracle.prefill_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
                                   inp["seq_lens"], inp["q_lens"], scale, 1, 0, 0)
     compare(out, lse, ro, rl, inp["q_lens"], "bf16", f"{nseq} sequences")
+
+
+@pytest.mark.parametrize("mask", [(1, 0, 0), (2, 1000, 64), (0, 0, 0)])
+def test_prefill_paged_long_history(mask):
+    """Histories past 64 pages (16,384 keys), where the kernel loads the next 64 page ids on
+    the way; the window mask jumps from the global tokens in page 0 to pages past 64."""
+    lens, qls = [20000, 17000, 300], [64, 200, 300]
+    inp = workloads.gen_prefill_paged(3, 300, 8, 128, "bf16", 77, max_len=20000, lens=lens,
+                                      qlens=qls)
+    inp["v_pages"] = inp["v_pages"] * 0.25  # the whole-sequence chunk's first rows: |O| < 2
+    scale = workloads.default_scale(128)
+    out, lse = run_prefill(inp, scale, mask)
+    ro, rl = oracle.prefill_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
+                                  inp["seq_lens"], inp["q_lens"], scale, *mask)
+    compare(out, lse, ro, rl, inp["q_lens"], "bf16", f"long history mask {mask}")
 
 
 @pytest.mark.timeout(600)
