@@ -72,6 +72,23 @@ __device__ __forceinline__ void mma_agpr(f32x16 &acc, s16x8 a, s16x8 b)
         __asm__("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// 24 wait states after the last inline MFMA into acc[h][*] and before anything reads them:
+// the accumulators are the statement's operands, which orders it after their writers and
+// before their readers.
+template <int NDB>
+__device__ __forceinline__ void settle_agpr(f32x16 (&acc)[2][NDB])
+{
+    static_assert(NDB == 2 || NDB == 4, "d 64 or 128");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if constexpr (NDB == 4)
+            __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                             : "+a"(acc[h][0]), "+a"(acc[h][1]), "+a"(acc[h][2]), "+a"(acc[h][3]));
+        else
+            __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[h][0]), "+a"(acc[h][1]));
+    }
+}
+
 // Rows that may see keys [k0, k1] (a superset; the element mask decides).
 template <int MASK>
 __device__ __forceinline__ void rows_seeing(int k0, int k1, int Nq, int Nkv, int W, int G, int &lo,
@@ -401,11 +418,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __syncthreads();
     // The last matrix results must be complete before vector reads of them (19 wait states
     // for a 16-pass MFMA; the inline MFMAs are invisible to the compiler's hazard checks).
-    __builtin_amdgcn_sched_barrier(0);
-    __asm__ volatile("s_nop 7");
-    __asm__ volatile("s_nop 7");
-    __asm__ volatile("s_nop 7");
-    __builtin_amdgcn_sched_barrier(0);
+    // The padding takes the accumulators as operands, so every MFMA that writes one comes
+    // before it and every read of one after it, wherever the compiler places the reads.
+    settle_agpr<NDB>(dkt);
+    settle_agpr<NDB>(dvt);
 
     // dK^T / dV^T: lane (g, key) holds columns db*32 + 8(e/4) + 4g + e%4. Rows go out
     // through LDS (this wave's 64 rows, padded by 16 bytes against bank conflicts; the ring
