@@ -41,8 +41,20 @@ __host__ __device__ inline size_t stats_index(size_t bh, int nt32, int row)
     return ((size_t)bh * nt32 + (size_t)(row >> 5)) * 64 + (size_t)(row & 31);
 }
 
+// Swizzle of the backward's LDS tiles, which are read both row-wise (16 consecutive rows at
+// one 16-byte chunk per 16 lanes, ds_read_b128) and transposed (4 consecutive rows x 4
+// consecutive chunks per 32 lanes, ds_read_b64_tr_b16). XOR with the row's two 2-bit fields
+// swapped spreads both patterns over all 64 banks; the forward's K swizzle (XOR with the row's
+// low bits) spreads only the first and leaves the second 4-way conflicted (2-way at d 64).
+template <int D>
+__device__ __forceinline__ int b_swz(int row, int chunk)
+{
+    return D == 128 ? chunk ^ (((row & 3) << 2) | ((row >> 2) & 3))
+                    : chunk ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
 // Byte offsets (relative to a tile) of the transposed 16-bit reads that hand each lane four
-// consecutive rows of one column, for tiles stored with the K swizzle: half h covers rows
+// consecutive rows of one column, for tiles stored with b_swz: half h covers rows
 // 8h .. 8h+7 of each 16-row chunk (the swizzle depends on the row within 16, so the two
 // halves need their own offsets; whole 16-row chunks add 16 rows).
 template <int D>
@@ -52,7 +64,7 @@ __device__ __forceinline__ int tr_ofs(int lane, int h, int db)
     const int g = lane >> 5;
     const int trow = 8 * h + 4 * g + ((lane & 15) >> 2);
     const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    return trow * ROWB + 16 * k_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
+    return trow * ROWB + 16 * b_swz<D>(trow, 4 * db + tchunk) + 8 * (lane & 1);
 }
 
 // acc += a * b on the matrix cores with acc held in accumulation registers (AGPRs). The dK/dV
@@ -313,8 +325,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
                             ? *(const s16x8 *)(K + kvbase + (size_t)key * D + 16 * kk + 8 * g)
                             : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    // V rows of this wave's 64 keys go to LDS (after the ring and the statistics) with the K
-    // swizzle, each wave loading its own rows, zero past Nkv.
+    // V rows of this wave's 64 keys go to LDS (after the ring and the statistics) with the
+    // same swizzle as the Q and dO tiles (they share the read offsets), each wave loading its
+    // own rows, zero past Nkv.
     char *const vl = lds + C::LDS_BYTES + NS * kStatsBytes;
 #if defined(__HIP_DEVICE_COMPILE__)
     {
@@ -326,7 +339,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int u = 0; u < VLOADS; ++u) {
             const int r = u * C::ROWS_PER_LOAD + lane / C::CHUNKS;
-            const unsigned vo = r * C::ROWB + 16 * k_swz<D>(r, lane % C::CHUNKS);
+            const unsigned vo = r * C::ROWB + 16 * b_swz<D>(r, lane % C::CHUNKS);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 vr, (lds_void *)(vl + (wave * 64 + u * C::ROWS_PER_LOAD) * C::ROWB), 16, vo, 0,
                 0, 0);
@@ -339,18 +352,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dkt[h][db] = dvt[h][db] = f32x16{};
 
-    // Q and dO tiles go to LDS like the forward's K tiles (K swizzle for both: read
-    // row-wise for S and dP, transposed for dK and dV).
+    // Q and dO tiles go to LDS like the forward's K tiles, swizzled by b_swz (read row-wise
+    // for S and dP, transposed for dK and dV).
     unsigned off[LPW];
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
         const int i = wave + C::NW * u;
         const int r = (i % C::KL) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
-        off[u] = r * C::ROWB + 16 * k_swz<D>(r, lane % C::CHUNKS);
+        off[u] = r * C::ROWB + 16 * b_swz<D>(r, lane % C::CHUNKS);
     }
     int kofs[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * k_swz<D>(li, 2 * kk + g);
+    for (int kk = 0; kk < NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * b_swz<D>(li, 2 * kk + g);
     int tro[2][NDB];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -579,11 +592,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     for (int u = 0; u < LPW; ++u) {
         const int i = wave + C::NW * u;
         const int r = (i % C::KL) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
-        off[u] = r * C::ROWB + 16 * k_swz<D>(r, lane % C::CHUNKS);
+        off[u] = r * C::ROWB + 16 * b_swz<D>(r, lane % C::CHUNKS);
     }
     int kofs[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * k_swz<D>(li, 2 * kk + g);
+    for (int kk = 0; kk < NKK; ++kk) kofs[kk] = li * C::ROWB + 16 * b_swz<D>(li, 2 * kk + g);
     int tro[2][NDB];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
