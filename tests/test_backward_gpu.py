@@ -109,6 +109,31 @@ def test_backward_negative_scale_and_large_inputs():
                         band_mask(200, 300, *mask))
 
 
+def test_backward_zero_and_subnormal_scale():
+    """scale 0, or a scale whose product with log2 e is subnormal (either sign), makes P uniform
+    over each row's visible keys; hidden scores must still give P = 0."""
+    q, k, v = workloads.gen_prefill(1, 2, 100, 150, 128, "bf16", 93)
+    do = workloads.gen_dout((1, 2, 100, 128), "bf16", 94)
+    u = U["bf16"]
+    for scale in (0.0, 1e-39, -1e-39):
+        for mask in ((0, 0, 0), (1, 0, 0), (2, 20, 3), (3, 10, 0)):
+            got = run_bwd(q, k, v, do, scale, *mask)
+            ref = oracle.attention_backward(q, k, v, do, scale, *mask)
+            label = f"scale {scale} mask {mask}"
+            if scale == 0.0:
+                check_grads(got, ref, "bf16", label, (q, k, v, do), scale,
+                            band_mask(100, 150, *mask))
+                continue
+            # dQ and dK are ~1e-39 (scale times O(1)), subnormal in the output type: only
+            # finite and tiny; dV carries P and is compared as usual
+            for g in got[:2]:
+                g = f64(g)
+                assert np.isfinite(g).all() and np.abs(g).max() < 1e-30, label
+            g, r = f64(got[2]), np.asarray(ref[2], np.float64).reshape(got[2].shape)
+            assert np.abs(g - r).max() <= 8 * u * np.abs(r).max(), label
+            assert np.linalg.norm(g - r) <= 4 * u * np.linalg.norm(r), label
+
+
 def test_backward_deterministic():
     q, k, v = workloads.gen_prefill(2, 4, 640, 640, 128, "bf16", 93)
     do = workloads.gen_dout((2, 4, 640, 128), "bf16", 94)

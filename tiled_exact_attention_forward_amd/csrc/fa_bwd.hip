@@ -496,8 +496,8 @@ __device__ __forceinline__ void dq_step(const char *__restrict__ kt, const char 
     }
     if (masked) mask_tile<MASK>(s, kv0, ip, Nkv, W, G, g);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {  // hidden scores are -inf; P = 0 for any sign of c
-        const float p = s[e] == -INFINITY ? 0.f : fast_exp2(__builtin_fmaf(s[e], c, -lrow));
+    for (int e = 0; e < 16; ++e) {  // hidden scores are -inf, c > 0: P = 2^-inf = 0
+        const float p = fast_exp2(__builtin_fmaf(s[e], c, -lrow));
         dp[e] = p * (dp[e] - drow);
     }
 #pragma unroll
@@ -555,6 +555,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         } else {
             qf[kk] = gf[kk] = of[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
+    }
+    // As in the forward, a negative scale moves into Q (sign bits flipped, exact; Q enters
+    // only the scores here) and c is kept at least the smallest normal float, so a hidden
+    // score (-inf) times c stays -inf and its P is 0 with no test.
+    {
+        const short qsign = c < 0.f ? (short)0x8000 : (short)0;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qf[kk] = qf[kk] ^ qsign;
+        c = fmaxf(fabsf(c), 1.17549435e-38f);
     }
     // Row statistics: lanes i and i + 32 hold complementary halves of row i's columns.
     auto tof = [](short x) -> float {
