@@ -28,14 +28,15 @@ namespace {
 
 // Q/dO tiles of 32 rows stream through a 4-slot ring (like the forward's K/V ring; the
 // "K" half of the ring holds Q, the "V" half dO). Each slot also holds the tile's row
-// statistics: 32 L values then 32 D values (256 bytes).
+// statistics: 32 L values then 32 values of -D (256 bytes).
 constexpr int kBwdStages = 4;
 template <int D>
 using CfgBD = CfgSP<D, kBwdStages, 4>;
 constexpr int kStatsBytes = 256;
 
-// Row statistics are stored per 32-row tile of each (b, h): [L_0..L_31, D_0..D_31], so one
-// 256-byte load brings a tile's statistics. Rows past Nq hold L = +inf (P = 0) and D = 0.
+// Row statistics are stored per 32-row tile of each (b, h): [L_0..L_31, -D_0..-D_31], so one
+// 256-byte load brings a tile's statistics (-D as the dK/dV kernel starts its dP accumulation
+// from it). Rows past Nq hold L = +inf (P = 0) and D = 0.
 __host__ __device__ inline size_t stats_index(size_t bh, int nt32, int row)
 {
     return ((size_t)bh * nt32 + (size_t)(row >> 5)) * 64 + (size_t)(row & 31);
@@ -187,9 +188,17 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
     // dP = dO V^T; P = 2^(c S - L) is formed alongside, two elements of each half per
     // step, so that one wave keeps its matrix and vector units busy together.
     {
-        f32x4 lv[4];
+        f32x4 lv[4], nd4[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) lv[q] = *(const f32x4 *)(st + 8 * q + 4 * g);
+        // -D of the rows this lane's accumulator elements belong to: the dP chains start
+        // from it, so they end at dP - D
+#pragma unroll
+        for (int q = 0; q < 4; ++q) nd4[q] = *(const f32x4 *)(st + 32 + 8 * q + 4 * g);
+        const f32x16 nd = __builtin_shufflevector(
+            __builtin_shufflevector(nd4[0], nd4[1], 0, 1, 2, 3, 4, 5, 6, 7),
+            __builtin_shufflevector(nd4[2], nd4[3], 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3, 4, 5,
+            6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
         s16x8 a = *(const s16x8 *)(gt + kofs[0]);
         s16x8 v0 = *(const s16x8 *)(vw + kofs[0]);
         s16x8 v1 = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[0]);
@@ -199,8 +208,8 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
             const s16x8 an = *(const s16x8 *)(gt + kofs[kn]);
             const s16x8 v0n = *(const s16x8 *)(vw + kofs[kn]);
             const s16x8 v1n = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[kn]);
-            dp[0] = Op::mma(a, v0, kk == 0 ? f32x16{} : dp[0]);
-            dp[1] = Op::mma(a, v1, kk == 0 ? f32x16{} : dp[1]);
+            dp[0] = Op::mma(a, v0, kk == 0 ? nd : dp[0]);
+            dp[1] = Op::mma(a, v1, kk == 0 ? nd : dp[1]);
 #pragma unroll
             for (int e = 16 * kk / NKK; e < 16 * (kk + 1) / NKK; ++e) {
                 const int r = 8 * (e >> 2) + (e & 3);
@@ -219,9 +228,6 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
     }
     // dV^T += dO^T P; dS = P (dP - D) is formed alongside.
     {
-        f32x4 dv4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dv4[q] = *(const f32x4 *)(st + 32 + 8 * q + 4 * g);
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             const int o8 = 8 * kc;
@@ -245,7 +251,7 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
                 for (int e = o8 + 8 * db / NDB; e < o8 + 8 * (db + 1) / NDB; ++e)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        dp[h][e] = s[h][e] * (dp[h][e] - dv4[e >> 2][e & 3]);
+                        dp[h][e] = s[h][e] * dp[h][e];
                 tlo = lon;
                 thi = hin;
                 __builtin_amdgcn_sched_barrier(0);
@@ -587,7 +593,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     // past Nq hold L = +inf, so their P is 0, and D = 0).
     if (g == 0 && row < nt32 * 32) {
         ST[stats_index(bh, nt32, row)] = lrow;
-        ST[stats_index(bh, nt32, row) + 32] = drow;
+        ST[stats_index(bh, nt32, row) + 32] = -drow;
     }
 
     const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);

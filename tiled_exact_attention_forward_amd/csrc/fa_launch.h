@@ -85,7 +85,7 @@ struct BwdArgs {
 };
 
 // Row statistics of the backward: per 32-row tile of each (b, h), 32 log2-scaled LSE values
-// then 32 values of D = rowsum(dO o O).
+// then 32 values of -D, D = rowsum(dO o O).
 inline size_t backward_workspace_floats(int B, int H, int Nq)
 {
     return (size_t)B * H * (size_t)((Nq + 31) / 32) * 64;
