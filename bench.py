@@ -80,6 +80,35 @@ def block_sparse_pairs(layout, Nq, Nkv, block):
     return int((lay * rows[None, :, None] * keys[None, None, :]).sum())
 
 
+def tile_elements(Nq, Nkv, mode, W=0, G=0, bm=128, bn=32, layout=None, block=128):
+    """(query tile, key tile) pairs of bm x bn tiles holding at least one visible pair, and the
+    elements of those tiles (partial tiles at the edges count their real rows and keys), for
+    one (b, h); summed over heads for a block layout [H, nqb, nkb]. The tile-granular work
+    behind the exact pair count."""
+    i0 = np.arange(0, Nq, bm, dtype=np.int64)
+    k0 = np.arange(0, Nkv, bn, dtype=np.int64)
+    rows = np.minimum(bm, Nq - i0)
+    cols = np.minimum(bn, Nkv - k0)
+    if mode == 5:
+        lay = np.asarray(layout, dtype=np.int64) != 0           # [H, nqb, nkb], bm == block
+        vis = lay[:, :, np.minimum(k0 // block, lay.shape[2] - 1)]  # [H, nqt, nkt]
+        return int(vis.sum()), int((vis * rows[None, :, None] * cols[None, None, :]).sum())
+    p0 = (i0 + (Nkv - Nq))[:, None]                 # position of each tile's first row
+    p1 = (i0 + rows - 1 + (Nkv - Nq))[:, None]      # and of its last row
+    a, b = k0[None, :], (k0 + cols - 1)[None, :]     # first and last key of each key tile
+    if mode == 0:
+        vis = np.ones((len(i0), len(k0)), dtype=bool)
+    elif mode == 1:
+        vis = a <= p1
+    elif mode == 2:
+        vis = ((a < G) & (a <= p1)) | (np.maximum(p0, a) <= np.minimum(p1, b + W - 1))
+    elif mode == 3:
+        vis = (a <= p1 + W) & (b >= p0 - W)
+    else:
+        vis = (a <= p1) | (a < G)
+    return int(vis.sum()), int((vis * rows[:, None] * cols[None, :]).sum())
+
+
 def prefill_flops(w, layout=None):
     if w["mask"] == 5:
         pairs = block_sparse_pairs(layout, w["Nq"], w["Nkv"], w["block"]) * w["B"]
@@ -198,8 +227,19 @@ def bench_prefill(name, steps, warmup, torch, fa, workloads, cold_calls=20):
     ms, wall = time_calls(step, steps, warmup, torch)
     cold = time_cold(step, cold_calls, torch) if cold_calls else (ms, ms, ms)
     flops, pairs = prefill_flops(w, inp.get("layout"))
+    tiles, elems = tile_elements(w["Nq"], w["Nkv"], w["mask"], w["window"], w["n_global"],
+                                 layout=inp.get("layout"))
+    if w["mask"] != 5:
+        tiles, elems = tiles * w["B"] * w["H"], elems * w["B"] * w["H"]
+    else:
+        tiles, elems = tiles * w["B"], elems * w["B"]
     elem = q.element_size()
     return dict(workload=name, w=w, ms=ms, wall_s=wall, flops=flops, pairs=pairs,
+                tile_count=dict(tiles=tiles, elements=elems,
+                                tflops=round(4 * w["d"] * elems / (ms * 1e-3) / 1e12, 2),
+                                note="4*d FLOPs per element of every 128x32 (query x key) tile "
+                                     "holding a visible pair; the headline counts visible "
+                                     "pairs only"),
                 tflops=flops / (ms * 1e-3) / 1e12, bytes=prefill_bytes(w, elem), inputs=inp,
                 cold_ms=cold, cold_tflops=flops / (cold[0] * 1e-3) / 1e12)
 
@@ -438,7 +478,8 @@ def main():
                                 frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
                                 visible_pairs=r["pairs"],
                                 cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
-                                cold_tflops=round(r["cold_tflops"], 2))
+                                cold_tflops=round(r["cold_tflops"], 2),
+                                tile_count=r["tile_count"])
             print(f"[bench] {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
             del r
