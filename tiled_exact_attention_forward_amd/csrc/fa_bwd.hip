@@ -313,9 +313,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, li = lane & 31;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / nkt;
-    const int k0 = (L % nkt) * KPB;
+    // Causal: key block kb sees the rows from its first key on, so the work falls with kb;
+    // when every XCD holds whole heads, it runs its heads' key blocks in order of kb (all
+    // first blocks, then all second ones, ...), longest first, so that the blocks of little
+    // work fill the end. Other masks: (b, h) major, key blocks of a head side by side.
+    int bh, kb;
+    {
+        const int per = (int)gridDim.x / kXcds;
+        if (MASK == 1 && (int)gridDim.x % kXcds == 0 && per % nkt == 0) {
+            const int hx = per / nkt, x = (int)blockIdx.x % kXcds, idx = (int)blockIdx.x / kXcds;
+            bh = x * hx + idx % hx;
+            kb = idx / hx;
+        } else {
+            const int L = xcd_remap(blockIdx.x, gridDim.x);
+            bh = L / nkt;
+            kb = L % nkt;
+        }
+    }
+    const int k0 = kb * KPB;
     const int kw = k0 + wave * 64;  // this wave's first key
     const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
     const int delta = Nkv - Nq;
