@@ -50,7 +50,8 @@ def kernels(lines):
 
 
 def loops(lines, name):
-    """Instruction lists of the loops (a label up to a branch back to it) of kernel `name`."""
+    """Instruction lists of the innermost loops (a label up to a branch back to it, holding no
+    other such span and no s_endpgm) of kernel `name`."""
     i = next(k for k, ln in enumerate(lines) if ln.startswith(name + ":"))
     j = next(k for k in range(i, len(lines)) if lines[k].startswith(".Lfunc_end"))
     seq, at = [], {}
@@ -60,12 +61,18 @@ def loops(lines, name):
             at[t[:-1]] = len(seq)
         elif t and not t.startswith("."):
             seq.append(t)
-    out = []
+    spans = []
     for k, t in enumerate(seq):
         m = re.match(r"s_c?branch\w*\s+(\.LBB\w+)$", t)
         if m and m.group(1) in at and at[m.group(1)] <= k:
-            out.append(seq[at[m.group(1)]:k + 1])
-    return out
+            a = at[m.group(1)]
+            # a backward jump over the program's end is a block placed after it (e.g. one arm
+            # of a branch jumping back to the join), not a loop
+            if not any(x.startswith("s_endpgm") for x in seq[a:k + 1]):
+                spans.append((a, k))
+    return [seq[a:k + 1] for a, k in spans] if not spans else [
+        seq[a:k + 1] for a, k in spans
+        if not any((a2, k2) != (a, k) and a <= a2 and k2 <= k for a2, k2 in spans)]
 
 
 def is_agpr_mfma(t):
