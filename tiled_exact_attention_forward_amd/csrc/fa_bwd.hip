@@ -313,14 +313,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, li = lane & 31;
-    // Causal: key block kb sees the rows from its first key on, so the work falls with kb;
-    // when every XCD holds whole heads, it runs its heads' key blocks in order of kb (all
-    // first blocks, then all second ones, ...), longest first, so that the blocks of little
-    // work fill the end. Other masks: (b, h) major, key blocks of a head side by side.
+    // Causal, window + global and prefix LM: the first key blocks see the most rows (causal:
+    // the rows from the block's first key on; the global or prefix keys: every row), so when
+    // every XCD holds whole heads, it runs its heads' key blocks in order of kb (all first
+    // blocks, then all second ones, ...), longest first, and the blocks of little work fill
+    // the end. Other masks: (b, h) major, the key blocks of a head side by side.
     int bh, kb;
     {
         const int per = (int)gridDim.x / kXcds;
-        if (MASK == 1 && (int)gridDim.x % kXcds == 0 && per % nkt == 0) {
+        if ((MASK == 1 || MASK == 2 || MASK == 4) && (int)gridDim.x % kXcds == 0 &&
+            per % nkt == 0) {
             const int hx = per / nkt, x = (int)blockIdx.x % kXcds, idx = (int)blockIdx.x / kXcds;
             bh = x * hx + idx % hx;
             kb = idx / hx;
