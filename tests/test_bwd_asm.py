@@ -11,7 +11,11 @@ compiler's hazard recognizer does not see. The source covers the two hazards its
 These tests compile the file with the library's flags and check, in every dK/dV
 instantiation, that the padding is where the source means it to be: before every
 AGPR-accumulating MFMA, between the last of them and the first instruction that reads an
-accumulator, and that the loop holds no copies between the register files.
+accumulator, and that the loop holds no copies between the register files. The compiler
+may also copy an accumulator on its own (a move between AGPRs when it splits a live range);
+placed right after an inline MFMA, such a copy reads the register before the MFMA has
+written it, so every instruction that reads an AGPR is checked against the last MFMA that
+writes it, in program order.
 """
 import os
 import re
@@ -75,6 +79,15 @@ def loops(lines, name):
         if not any((a2, k2) != (a, k) and a <= a2 and k2 <= k for a2, k2 in spans)]
 
 
+def agprs(operand):
+    """AGPR indices named by one operand (a5, a[0:15]); empty for anything else."""
+    m = re.fullmatch(r"a(\d+)", operand)
+    if m:
+        return {int(m.group(1))}
+    m = re.fullmatch(r"a\[(\d+):(\d+)\]", operand)
+    return set(range(int(m.group(1)), int(m.group(2)) + 1)) if m else set()
+
+
 def is_agpr_mfma(t):
     return re.match(r"v_mfma\S*\s+a\[", t) is not None
 
@@ -134,3 +147,30 @@ def test_no_register_file_copies_in_the_loop(asm):
             copies = [t for t in lp if t.startswith(("v_accvgpr_read", "v_accvgpr_write",
                                                      "v_accvgpr_mov"))]
             assert not copies, f"{name}: {len(copies)} AGPR copies in a loop, e.g. {copies[:3]}"
+
+
+def agpr_sources(t):
+    """AGPRs that a non-MFMA instruction reads."""
+    ops = t.split(None, 1)
+    if len(ops) < 2 or ops[0].startswith("v_mfma"):
+        return set()
+    srcs = [x.strip() for x in ops[1].split(",")]
+    if not ops[0].startswith(("global_store", "buffer_store", "ds_write", "flat_store",
+                              "scratch_store")):
+        srcs = srcs[1:]
+    return set().union(*(agprs(x) for x in srcs))
+
+
+def test_every_accumulator_read_waits_for_its_mfma(asm):
+    for name, body in kernels(asm):
+        written = {}  # AGPR -> index of the last inline MFMA that writes it
+        for i, t in enumerate(body):
+            if is_agpr_mfma(t):
+                for r in agprs(t.split(None, 1)[1].split(",")[0].strip()):
+                    written[r] = i
+                continue
+            for r in agpr_sources(t):
+                if r in written:
+                    ws = sum(wait_states(x) for x in body[written[r] + 1:i])
+                    assert ws >= MIN_WAIT_STATES, (
+                        f"{name}: {t!r} reads a{r} {ws} wait states after {body[written[r]]!r}")
