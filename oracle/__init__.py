@@ -12,7 +12,8 @@ invariants (rows sum to one, shift and permutation invariance, split-and-merge o
 one-hot edge probes of every mask boundary, and reductions between masks (a band or prefix
 covering every key is the unmasked case, an empty prefix is causal, an all-ones block layout
 is unmasked). The gradients are pinned to torch autograd in float64, central finite
-differences of the forward pass and the invariants of the softmax Jacobian.
+differences of the forward pass and the invariants of the softmax Jacobian, for the
+block-sparse layout as for the masks.
 """
 import ctypes
 import os
@@ -56,6 +57,11 @@ class Oracle:
             ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_long, ctypes.c_long, f64p,
             f64p, f64p]
         lib.oracle_attention_backward.restype = ctypes.c_int
+        lib.oracle_attention_backward_block_sparse.argtypes = [
+            f32p, f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_long,
+            ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_uint8), ctypes.c_long, f64p,
+            f64p, f64p]
+        lib.oracle_attention_backward_block_sparse.restype = ctypes.c_int
         lib.oracle_merge_lse.argtypes = [f32p, f32p, f32p, f32p, ctypes.c_long, ctypes.c_int,
                                          f64p, f64p]
         lib.oracle_merge_lse.restype = None
@@ -117,6 +123,27 @@ class Oracle:
             _p(dv, ctypes.c_double))
         if rc != 0:
             raise ValueError("oracle_attention_backward rejected its arguments")
+        return dq, dk, dv
+
+    def attention_backward_block_sparse(self, q, k, v, dout, scale, layout, block):
+        """Gradients (dq, dk, dv) of block-sparse attention (layout as in
+        attention_block_sparse) for upstream gradient dout, fp64."""
+        q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        assert k.shape == (B, H, Nkv, d) and v.shape == k.shape and g.shape == q.shape
+        lay = np.ascontiguousarray(np.asarray(layout).astype(np.uint8))
+        assert lay.shape == (H, -(-Nq // block), -(-Nkv // block)), lay.shape
+        dq = np.empty(q.shape, np.float64)
+        dk = np.empty(k.shape, np.float64)
+        dv = np.empty(k.shape, np.float64)
+        rc = self.lib.oracle_attention_backward_block_sparse(
+            _p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
+            _p(g, ctypes.c_float), B, H, Nq, Nkv, d, float(np.float32(scale)),
+            _p(lay, ctypes.c_uint8), int(block), _p(dq, ctypes.c_double),
+            _p(dk, ctypes.c_double), _p(dv, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_attention_backward_block_sparse rejected its arguments")
         return dq, dk, dv
 
     def attention_block_sparse(self, q, k, v, scale, layout, block, rows=None):
@@ -274,6 +301,10 @@ def attention(*args, **kw):
 
 def attention_block_sparse(*args, **kw):
     return default().attention_block_sparse(*args, **kw)
+
+
+def attention_backward_block_sparse(*args, **kw):
+    return default().attention_backward_block_sparse(*args, **kw)
 
 
 def attention_backward(*args, **kw):

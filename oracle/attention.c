@@ -241,16 +241,19 @@ int oracle_attention_block_sparse_rows(const float *q, const float *k, const flo
  *   dP_ij = sum_c dO_ic v_jc
  *   dS_ij = P_ij (dP_ij - D_i)                     (softmax Jacobian)
  *   dQ_i  = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i
- * Masks as oracle_attention_rows. All outputs [B,H,N,d] doubles. Parallel over (b, h).
+ * Masks as oracle_attention_rows, or (layout != NULL) the block layout of
+ * oracle_attention_block_sparse_rows. All outputs [B,H,N,d] doubles. Parallel over (b, h).
  */
-int oracle_attention_backward(const float *q, const float *k, const float *v, const float *dout,
-                              int B, int H, long Nq, long Nkv, int d, double scale, int mode,
-                              long window, long n_global, double *dq, double *dk, double *dv)
+static int attention_backward(const float *q, const float *k, const float *v,
+                              const float *dout, int B, int H, long Nq, long Nkv, int d,
+                              double scale, int mode, long window, long n_global,
+                              const uint8_t *layout, long block, double *dq, double *dk,
+                              double *dv)
 {
     int failed = 0;
     long bh;
-    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || mode < 0 || mode > 4)
-        return -1;
+    const long nqb = layout ? (Nq + block - 1) / block : 0;
+    const long nkb = layout ? (Nkv + block - 1) / block : 0;
     memset(dk, 0, sizeof(double) * (size_t)B * H * Nkv * d);
     memset(dv, 0, sizeof(double) * (size_t)B * H * Nkv * d);
 
@@ -274,9 +277,13 @@ int oracle_attention_backward(const float *q, const float *k, const float *v, co
                     const float *qi = qb + (size_t)i * d, *gi = gb + (size_t)i * d;
                     const long ip = i + (Nkv - Nq);
                     double m = -INFINITY, l = 0.0, D = 0.0;
+                    const uint8_t *lrow =
+                        layout ? layout + ((size_t)(bh % H) * nqb + (size_t)i / (size_t)block) * nkb
+                               : NULL;
                     for (j = 0; j < Nkv; ++j) {
                         double dot = 0.0;
-                        if (!key_visible(ip, j, mode, window, n_global)) {
+                        if (lrow ? lrow[j / block] == 0
+                                 : !key_visible(ip, j, mode, window, n_global)) {
                             p[j] = -INFINITY;
                             continue;
                         }
@@ -325,6 +332,30 @@ int oracle_attention_backward(const float *q, const float *k, const float *v, co
         free(orow);
     }
     return failed ? -1 : 0;
+}
+
+int oracle_attention_backward(const float *q, const float *k, const float *v, const float *dout,
+                              int B, int H, long Nq, long Nkv, int d, double scale, int mode,
+                              long window, long n_global, double *dq, double *dk, double *dv)
+{
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || mode < 0 || mode > 4)
+        return -1;
+    return attention_backward(q, k, v, dout, B, H, Nq, Nkv, d, scale, mode, window, n_global,
+                              NULL, 0, dq, dk, dv);
+}
+
+/* Gradients of block-sparse attention: layout [H, ceil(Nq/block), ceil(Nkv/block)], key j
+ * visible from query row i of head h when layout[h][i/block][j/block] != 0 (the reading of
+ * oracle_attention_block_sparse_rows); the arithmetic is the backward above. */
+int oracle_attention_backward_block_sparse(const float *q, const float *k, const float *v,
+                                           const float *dout, int B, int H, long Nq, long Nkv,
+                                           int d, double scale, const uint8_t *layout,
+                                           long block, double *dq, double *dk, double *dv)
+{
+    if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || d < 1 || block < 1 || layout == NULL)
+        return -1;
+    return attention_backward(q, k, v, dout, B, H, Nq, Nkv, d, scale, 0, 0, 0, layout, block,
+                              dq, dk, dv);
 }
 
 /*

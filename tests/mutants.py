@@ -29,6 +29,10 @@ MUTANTS = {
     "block_key_index": ("lrow[j / block] != 0", "lrow[(j + 1) / block] != 0"),
     "block_head": ("long h = bh % H;", "long h = 0;"),
     "bwd_no_rowterm": ("ds = p[j] * (dp - D);", "ds = p[j] * dp;"),
+    "bwd_block_key_index": ("lrow[j / block] == 0", "lrow[(j + 1) / block] == 0"),
+    "bwd_block_query_index": ("(size_t)i / (size_t)block) * nkb",
+                              "(size_t)(i + 1) / (size_t)block) * nkb"),
+    "bwd_block_head": ("layout + ((size_t)(bh % H) * nqb", "layout + ((size_t)(bh / H) * nqb"),
     "bwd_dk_no_scale": ("dkb[(size_t)j * d + c] += scale * ds", "dkb[(size_t)j * d + c] += ds"),
     "bwd_dv_from_ds": ("dvb[(size_t)j * d + c] += p[j] * (double)gi[c];",
                        "dvb[(size_t)j * d + c] += ds * (double)gi[c];"),

@@ -623,6 +623,62 @@ def pin_backward_invariants(orc):
         assert all(np.all(x == 0) for x in z), n
 
 
+def pin_backward_block_sparse(orc):
+    """Block-sparse gradients: torch autograd in float64 through a softmax masked by the layout
+    expanded with a Kronecker product (ragged edges, rows and keys that no tile reaches);
+    central differences of the oracle's block-sparse forward on tiny inputs; an all-ones
+    layout gives exactly the unmasked gradients; the softmax Jacobian's invariants."""
+    cases = [(1, 2, 13, 17, 8, 4), (2, 1, 20, 12, 4, 5), (1, 3, 9, 9, 8, 3), (2, 2, 16, 16, 8, 8)]
+    for n, (B, H, Nq, Nkv, d, blk) in enumerate(cases):
+        q = _rand((B, H, Nq, d), 4300 + 4 * n)
+        k = _rand((B, H, Nkv, d), 4301 + 4 * n)
+        v = _rand((B, H, Nkv, d), 4302 + 4 * n)
+        g = _rand((B, H, Nq, d), 4303 + 4 * n)
+        lay = _random_layout(H, -(-Nq // blk), -(-Nkv // blk), 4304 + n, density=0.5)
+        lay[0, -1, :] = 0  # a query block that sees nothing
+        scale = float(np.float32(1 / math.sqrt(d)))
+        got = orc.attention_backward_block_sparse(q, k, v, g, scale, lay, blk)
+        want = library_backward(q, k, v, g, scale, block_mask(lay, blk, Nq, Nkv))
+        for name, a, b in zip(("dq", "dk", "dv"), got, want):
+            assert np.allclose(a, b, rtol=1e-11, atol=1e-12), (n, name, np.abs(a - b).max())
+        # invariants: dK sums to zero over keys, dV sums to dO over the rows that see a key,
+        # rows that see nothing get dQ = 0
+        dq, dk, dv = got
+        seen = np.stack([block_mask(lay, blk, Nq, Nkv)[h].numpy().any(axis=1) for h in range(H)])
+        assert np.abs(dk.sum(axis=2)).max() < 1e-12, n
+        want_v = np.stack([g.astype(np.float64)[:, h, seen[h]].sum(axis=1) for h in range(H)], 1)
+        assert np.allclose(dv.sum(axis=2), want_v, rtol=1e-12, atol=1e-12), n
+        assert all(np.all(dq[:, h, ~seen[h]] == 0) for h in range(H)), n
+        ones = np.ones_like(lay)
+        dense = orc.attention_backward(q, k, v, g, scale, 0)
+        full = orc.attention_backward_block_sparse(q, k, v, g, scale, ones, blk)
+        assert all(np.array_equal(a, b) for a, b in zip(dense, full)), n
+    h = 2.0 ** -10
+    rng = np.random.default_rng(4350)
+    Nq, Nkv, d, blk = 6, 7, 2, 2
+    q, k, v, g = (np.round(rng.standard_normal(sh) * 64) / 64
+                  for sh in ((1, 2, Nq, d), (1, 2, Nkv, d), (1, 2, Nkv, d), (1, 2, Nq, d)))
+    q, k, v, g = (x.astype(np.float32) for x in (q, k, v, g))
+    lay = np.array([[[1, 0, 1, 0], [0, 1, 1, 0], [1, 1, 0, 1]],
+                    [[0, 1, 0, 1], [1, 0, 0, 0], [0, 0, 1, 1]]], np.uint8)
+    dq, dk, dv = orc.attention_backward_block_sparse(q, k, v, g, 0.5, lay, blk)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attention_block_sparse(qq, kk, vv, 0.5, lay, blk)
+        return float((o * g.astype(np.float64)).sum())
+
+    for which, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros(x.shape)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += np.float32(h)
+            xm[idx] -= np.float32(h)
+            args_p = [xp if w == which else y for w, y in (("q", q), ("k", k), ("v", v))]
+            args_m = [xm if w == which else y for w, y in (("q", q), ("k", k), ("v", v))]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-5, atol=2e-6), (which, np.abs(grad - num).max())
+
+
 def pin_prefill_paged(orc):
     """Chunked prefill against a paged cache: each sequence's newest q_lens[s] tokens attend
     to its seq_lens[s] keys with bottom-right masks. Pinned to torch SDPA in float64 on the
@@ -742,4 +798,5 @@ ALL_PINS = [pin_library, pin_mpmath, pin_q_zero, pin_causal_row0, pin_onehot_edg
             pin_mask_reductions, pin_empty_rows, pin_decode, pin_library_more_masks,
             pin_mpmath_more_masks, pin_q_zero_more_masks, pin_onehot_more_edges,
             pin_more_mask_reductions, pin_backward_library, pin_backward_finite_difference,
-            pin_backward_invariants, pin_prefill_paged, pin_merge_lse, pin_multimodal]
+            pin_backward_invariants, pin_backward_block_sparse, pin_prefill_paged,
+            pin_merge_lse, pin_multimodal]
