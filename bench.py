@@ -9,7 +9,8 @@ workload B=4 H=32 N=1024 d=128, the configuration the throughput metric is quote
 other workloads (fp16 dense, causal, sliding window + global keys, paged decode) are timed in
 the same run and reported under "workloads", with chunked prefill against the paged cache,
 multimodal attention (three calls merged by log-sum-exp, beside one prefix-LM call) and the
-backward pass (dQ, dK, dV) of the dense and causal workloads. Prints one JSON line.
+backward pass (dQ, dK, dV) of the dense, causal and block-sparse workloads. Prints one JSON
+line.
 
 Throughput counts 4*d FLOPs per visible (query, key) pair (QK^T and PV), with the exact pair
 count of the mask (not whole tiles); decode counts algorithmic HBM bytes (K and V of every
@@ -333,17 +334,28 @@ def bench_backward(name, steps, warmup, torch, fa, workloads, cold_calls=20):
     do = workloads.gen_dout(tuple(q.shape), w["dtype"], w["seed"] + 500).to(dev)
     scale = workloads.default_scale(w["d"])
     mask = (w["mask"], w["window"], w["n_global"])
-    o, lse = fa.fa_forward(q, k, v, scale, *mask)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty((fa.fa_backward_workspace_bytes(w["B"], w["H"], w["Nq"]),),
                      dtype=torch.uint8, device=dev)
+    layout = None
+    if w["mask"] == 5:  # block sparse: the forward's layout
+        layout = inp["layout"]
+        lay = layout.to(dev)
+        o, lse = fa.fa_forward_block_sparse(q, k, v, lay, w["block"], scale)
 
-    def step():
-        fa.fa_backward(q, k, v, o, lse, do, scale, *mask, dq=dq, dk=dk, dv=dv, workspace=ws)
+        def step():
+            fa.fa_backward_block_sparse(q, k, v, o, lse, do, lay, w["block"], scale, dq=dq,
+                                        dk=dk, dv=dv, workspace=ws)
+    else:
+        o, lse = fa.fa_forward(q, k, v, scale, *mask)
+
+        def step():
+            fa.fa_backward(q, k, v, o, lse, do, scale, *mask, dq=dq, dk=dk, dv=dv,
+                           workspace=ws)
 
     ms, wall = time_calls(step, steps, warmup, torch)
     cold = time_cold(step, cold_calls, torch) if cold_calls else (ms, ms, ms)
-    fwd_flops, pairs = prefill_flops(w)
+    fwd_flops, pairs = prefill_flops(w, layout)
     flops = fwd_flops // 4 * 10  # 10 d per visible pair: S, dP, dV, dK, dQ
     return dict(workload=name, w=w, ms=ms, wall_s=wall, flops=flops, pairs=pairs,
                 tflops=flops / (ms * 1e-3) / 1e12, cold_ms=cold,
@@ -511,7 +523,7 @@ def main():
               f"{r['ms_fused'] * 1e3:.1f} us, unified {r['ms_unified'] * 1e3:.1f} us",
               file=sys.stderr, flush=True)
         del r
-        for name in ("dense_bf16", "causal_bf16"):
+        for name in ("dense_bf16", "causal_bf16", "blocksparse_bf16"):
             r = bench_backward(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch,
                                fa, workloads)
             others["backward_" + name] = dict(

@@ -154,6 +154,26 @@ int fa_backward(const void *q, const void *k, const void *v, const void *o, cons
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fa_backward_block_sparse -- gradients of fa_forward_block_sparse: the recomputation of
+ * fa_backward (same passages) with the visible keys of each query row given by the block
+ * layout of fa_forward_block_sparse (the sparse variants of the "ascend-transformer-boost"
+ * article, 场景三).
+ *
+ *  q .. dv, B, H, Nq, Nkv, d, scale, dtype, workspace, workspace_bytes, stream: as
+ *          fa_backward; o and lse are fa_forward_block_sparse's outputs for the same layout.
+ *  layout, block: as fa_forward_block_sparse (DEVICE array [H, ceil(Nq/block),
+ *          ceil(Nkv/block)] uint8, one layout for every batch entry; block 128 only).
+ *  Supported: as fa_backward, with Nq and Nkv <= 262144 (each workgroup lists the visible
+ *  blocks of its row or column of the layout on chip). A key no query row sees gets dK = dV
+ *  = 0, a row that sees no key dQ = 0. The layout's contents are not checked on the host.
+ */
+int fa_backward_block_sparse(const void *q, const void *k, const void *v, const void *o,
+                             const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                             int B, int H, int Nq, int Nkv, int d, float scale,
+                             const uint8_t *layout, int block, int dtype, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * fa_merge_lse -- combine two attention results over disjoint key sets of the same query
  * rows: lse = ln(e^lse_a + e^lse_b), o = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b. This
  * is the step that lets the "ascend-transformer-boost" article (场景四) compute one

@@ -163,6 +163,27 @@ def test_backward_rejects_before_launch(kw, status):
     assert bwd(**kw) == status
 
 
+def bwd_bs(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=1, Nq=8, Nkv=8, d=64,
+           scale=0.125, layout=P, block=128, dtype=1, ws=P, wsb=None):
+    lib = fa.load_library()
+    if wsb is None:
+        wsb = lib.fa_backward_workspace_bytes(B, H, Nq)
+    return lib.fa_backward_block_sparse(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nkv, d, scale,
+                                        layout, block, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=N), fa.FA_ERR_NULL), (dict(q=N), fa.FA_ERR_NULL), (dict(dv=N), fa.FA_ERR_NULL),
+    (dict(block=64), fa.FA_ERR_UNSUPPORTED), (dict(Nkv=262145), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=262145), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(Nq=0), fa.FA_ERR_SHAPE),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE), (dict(ws=N), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=8 * 4), fa.FA_ERR_WORKSPACE), (dict(dq=ctypes.c_void_p(0x1004)), fa.FA_ERR_UNSUPPORTED),
+])
+def test_backward_block_sparse_rejects_before_launch(kw, status):
+    assert bwd_bs(**kw) == status
+
+
 def test_backward_workspace_bytes():
     lib = fa.load_library()
     # per 32-row tile of each (b, h): 32 log2-scaled LSE values and 32 values of D (floats)

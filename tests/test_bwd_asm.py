@@ -114,8 +114,8 @@ def reads_agpr(t):
 
 def test_every_dkdv_instantiation_found(asm):
     names = [n for n, _ in kernels(asm)]
-    # bf16 and fp16, d 64 and 128, masks 0-4
-    assert len(names) == 2 * 2 * 5, names
+    # bf16 and fp16, d 64 and 128, masks 0-4 and the block-sparse layout
+    assert len(names) == 2 * 2 * 6, names
 
 
 def test_operand_padding_before_each_inline_mfma(asm):

@@ -6,6 +6,7 @@ C ABI declared in include/fa.h. The functions carry the C names:
     fa_forward(q, k, v, ...)          tiled exact attention forward (O and LSE)
     fa_forward_block_sparse(...)      forward with a block-sparse layout of visible tiles
     fa_backward(q, k, v, o, lse, dout, ...)  gradients dQ, dK, dV
+    fa_backward_block_sparse(...)     gradients of the block-sparse forward
     fa_backward_workspace_bytes(...)
     fa_decode_paged(q, k_pages, ...)  single-token decode against a paged K/V cache
     fa_decode_paged_noalloc(...)      the same without a workspace (library's static scratch)
@@ -24,7 +25,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_bytes",
+__all__ = ["fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_block_sparse",
+           "fa_backward_workspace_bytes",
            "fa_decode_paged", "fa_decode_paged_noalloc", "fa_prefill_paged", "fa_merge_lse", "fa_multimodal_forward",
            "fa_multimodal_workspace_bytes", "fa_decode_paged_workspace_bytes",
            "fa_status_string", "fa_last_hip_error", "fa_version", "FaError", "library_path", "load_library",
@@ -39,7 +41,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_WINDOW_GLOBAL, FA_MASK_BAND, FA_MASK_PREFIX_LM = 0, 1, 2, 3, 4
 FA_MULTIMODAL_SPLIT_MERGE, FA_MULTIMODAL_FUSED = 0, 1
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_block_sparse", "fa_backward",
-                    "fa_backward_workspace_bytes", "fa_decode_paged", "fa_decode_paged_noalloc",
+                    "fa_backward_block_sparse", "fa_backward_workspace_bytes", "fa_decode_paged", "fa_decode_paged_noalloc",
                     "fa_prefill_paged",
                     "fa_merge_lse", "fa_multimodal_forward", "fa_multimodal_workspace_bytes",
                     "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_last_hip_error",
@@ -83,6 +85,9 @@ def load_library():
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i,
                                 vp, sz, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                             f, vp, i, i, vp, sz, vp]
+    lib.fa_backward_block_sparse.restype = i
     lib.fa_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_paged_workspace_bytes.restype = sz
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
@@ -230,10 +235,8 @@ def fa_backward_workspace_bytes(B, H, Nq):
     return int(load_library().fa_backward_workspace_bytes(int(B), int(H), int(Nq)))
 
 
-def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, window=0,
-                n_global=0, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV of fa_forward: q [B,H,Nq,d], k/v [B,H,Nkv,d] (f16/bf16), o and lse the
-    forward's outputs for the same arguments, dout like o. Returns (dq, dk, dv)."""
+def _backward_args(q, k, v, o, lse, dout, dq, dk, dv, workspace):
+    """Shape and device checks shared by the backward calls; allocates what is missing."""
     torch = _torch()
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
@@ -246,8 +249,6 @@ def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, windo
     _check_shape("dq", dq, q.shape)
     _check_shape("dk", dk, k.shape)
     _check_shape("dv", dv, v.shape)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -259,6 +260,18 @@ def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, windo
         _check_dev(name, t, q.dtype)
     _check_dev("lse", lse, torch.float32)
     _check_dev("workspace", workspace)
+    return dq, dk, dv, workspace
+
+
+def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, window=0,
+                n_global=0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of fa_forward: q [B,H,Nq,d], k/v [B,H,Nkv,d] (f16/bf16), o and lse the
+    forward's outputs for the same arguments, dout like o. Returns (dq, dk, dv)."""
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    dq, dk, dv, workspace = _backward_args(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
     rc = load_library().fa_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
         _ptr(dv), B, H, Nq, Nkv, d, float(scale), int(mask_mode), int(window), int(n_global),
@@ -266,6 +279,29 @@ def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, windo
         _stream(stream))
     if rc != FA_OK:
         raise FaError(rc, "fa_backward")
+    return dq, dk, dv
+
+
+def fa_backward_block_sparse(q, k, v, o, lse, dout, layout, block=128, scale=None, dq=None,
+                             dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of fa_forward_block_sparse (same layout and block); other arguments and
+    the result as fa_backward."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    want = (H, -(-Nq // block), -(-Nkv // block))
+    if tuple(layout.shape) != want or not layout.is_contiguous():
+        raise ValueError(f"layout must be a contiguous {want} tensor")
+    dq, dk, dv, workspace = _backward_args(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    _check_dev("layout", layout, torch.uint8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = load_library().fa_backward_block_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dv), B, H, Nq, Nkv, d, float(scale), _ptr(layout), int(block), _dtype_code(q),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_backward_block_sparse")
     return dq, dk, dv
 
 

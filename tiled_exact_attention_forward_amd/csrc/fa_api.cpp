@@ -194,19 +194,19 @@ size_t fa_backward_workspace_bytes(int B, int H, int Nq)
     return teaf::backward_workspace_floats(B, H, Nq) * sizeof(float);
 }
 
-int fa_backward(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                const void *dout, void *dq, void *dk, void *dv, int B, int H, int Nq, int Nkv,
-                int d, float scale, int mask_mode, int window, int n_global, int dtype,
-                void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the backward entry points (all but the mask arguments).
+int check_backward(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv, int B, int H, int Nq, int Nkv,
+                   int d, float scale, int dtype, void *workspace, size_t workspace_bytes)
 {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-    if (mask_mode < FA_MASK_NONE || mask_mode > FA_MASK_PREFIX_LM) return FA_ERR_UNSUPPORTED;
-    if (mask_mode == FA_MASK_WINDOW_GLOBAL && (window < 1 || n_global < 0)) return FA_ERR_SHAPE;
-    if (mask_mode == FA_MASK_BAND && window < 0) return FA_ERR_SHAPE;
-    if (mask_mode == FA_MASK_PREFIX_LM && n_global < 0) return FA_ERR_SHAPE;
     const long long bh = (long long)B * H;
     if (bh * ((Nq + 127) / 128) > (long long)INT_MAX || bh * ((Nkv + 127) / 128) > INT_MAX)
         return FA_ERR_SHAPE;
@@ -218,12 +218,49 @@ int fa_backward(const void *q, const void *k, const void *v, const void *o, cons
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
         return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_backward(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                const void *dout, void *dq, void *dk, void *dv, int B, int H, int Nq, int Nkv,
+                int d, float scale, int mask_mode, int window, int n_global, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int st = check_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nkv, d, scale,
+                                  dtype, workspace, workspace_bytes);
+    if (st != FA_OK) return st;
+    if (mask_mode < FA_MASK_NONE || mask_mode > FA_MASK_PREFIX_LM) return FA_ERR_UNSUPPORTED;
+    if (mask_mode == FA_MASK_WINDOW_GLOBAL && (window < 1 || n_global < 0)) return FA_ERR_SHAPE;
+    if (mask_mode == FA_MASK_BAND && window < 0) return FA_ERR_SHAPE;
+    if (mask_mode == FA_MASK_PREFIX_LM && n_global < 0) return FA_ERR_SHAPE;
     const bool uses_w = mask_mode == FA_MASK_WINDOW_GLOBAL || mask_mode == FA_MASK_BAND;
     const bool uses_g = mask_mode == FA_MASK_WINDOW_GLOBAL || mask_mode == FA_MASK_PREFIX_LM;
     const int wc = uses_w ? (int)std::min<long long>(window, (long long)Nq + Nkv) : 0;
     const int gc = uses_g ? std::min(n_global, Nkv) : 0;
     teaf::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, scale, mask_mode, wc,
-                    gc, dtype, workspace};
+                    gc, dtype, workspace, nullptr};
+    return hip_status(teaf::launch_backward(a, (hipStream_t)stream));
+}
+
+int fa_backward_block_sparse(const void *q, const void *k, const void *v, const void *o,
+                             const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                             int B, int H, int Nq, int Nkv, int d, float scale,
+                             const uint8_t *layout, int block, int dtype, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    const int st = check_backward(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nkv, d, scale,
+                                  dtype, workspace, workspace_bytes);
+    if (st != FA_OK) return st;
+    if (!layout) return FA_ERR_NULL;
+    if (block != teaf::kBlockSparseEdge) return FA_ERR_UNSUPPORTED;
+    const long long most = (long long)teaf::kBlockSparseMaxKeyBlocks * teaf::kBlockSparseEdge;
+    if ((long long)Nq > most || (long long)Nkv > most) return FA_ERR_UNSUPPORTED;
+    teaf::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, scale,
+                    teaf::kMaskBlockSparse, 0, 0, dtype, workspace, layout};
     return hip_status(teaf::launch_backward(a, (hipStream_t)stream));
 }
 

@@ -162,7 +162,8 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
                                           const s16x8 (&kf)[2][C::NKK],
                                           f32x16 (&dkt)[2][C::NDB], f32x16 (&dvt)[2][C::NDB],
                                           const int (&kofs)[C::NKK], const int (&tro)[2][C::NDB],
-                                          float c, int ip0, int kw, int li, int g, int W, int G)
+                                          float c, int ip0, int kw, int li, int g, int W, int G,
+                                          bool vis)
 {
     using Op = Ops16<T>;
     constexpr int BN = 32, NKK = C::NKK, NDB = C::NDB;
@@ -178,12 +179,20 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
             s[1] = Op::mma(a[kk], kf[1][kk], kk == 0 ? f32x16{} : s[1]);
         }
     }
-    const bool full = block_visible<MASK>(ip0, ip0 + BN - 1, kw, kw + 63, W, G);
+    // Block sparse: vis says whether the layout shows this wave's key block to the tile's
+    // query block (all or nothing); the other masks decide per element.
+    const bool full =
+        MASK == kBlockSparse ? vis : block_visible<MASK>(ip0, ip0 + BN - 1, kw, kw + 63, W, G);
     int lo[2] = {INT_MIN, INT_MIN}, hi[2] = {INT_MAX, INT_MAX};
     if (MASK != 0 && !full) {
+        if constexpr (MASK == kBlockSparse) {
+            lo[0] = lo[1] = 1;  // an empty range: P = 0 for every row
+            hi[0] = hi[1] = 0;
+        } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            key_row_range<MASK>(kw + 32 * h + li, ip0 + 4 * g, W, G, lo[h], hi[h]);
+            for (int h = 0; h < 2; ++h)
+                key_row_range<MASK>(kw + 32 * h + li, ip0 + 4 * g, W, G, lo[h], hi[h]);
+        }
     }
     // dP = dO V^T; P = 2^(c S - L) is formed alongside, two elements of each half per
     // step, so that one wave keeps its matrix and vector units busy together.
@@ -301,7 +310,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ ST, uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int Nq,
-    int Nkv, float c, float scale, int W, int G, int nkt, int nt32)
+    int Nkv, float c, float scale, int W, int G, int nkt, int nt32,
+    const uint8_t *__restrict__ layout, int H)
 {
     using C = CfgBD<D>;
     using Op = Ops16<T>;
@@ -394,10 +404,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         for (int db = 0; db < NDB; ++db) tro[h][db] = tr_ofs<D>(lane, h, db);
     const char *const vw = vl + wave * 64 * C::ROWB;  // this wave's V rows
 
-    int rlo, rhi;
-    rows_seeing<MASK>(k0, min(k0 + KPB - 1, Nkv - 1), Nq, Nkv, W, G, rlo, rhi);
-    const int t0 = rlo / BN;
-    const int ntl = rhi > rlo ? (rhi + BN - 1) / BN - t0 : 0;
+    // The 32-row tiles this workgroup visits: a range of tiles for masks 0-4; for the
+    // block-sparse layout, the query blocks that see either of its two 128-key blocks, listed
+    // in LDS after the V rows (each entry tagged with which of the two blocks it sees).
+    int t0 = 0, ntl = 0;
+    char *const lst = vl + 256 * C::ROWB;
+    const uint16_t *qlist = (const uint16_t *)(lst + 16);
+    if constexpr (MASK == kBlockSparse) {
+        const int nkb = (Nkv + kSparseBlock - 1) / kSparseBlock;
+        const int nqb = (Nq + kSparseBlock - 1) / kSparseBlock;
+        const int kb0 = k0 / kSparseBlock;
+        const uint8_t *lh = layout + (size_t)(bh % H) * nqb * nkb + kb0;
+        const int n = compact_list<C::NW>((int *)lst, (uint16_t *)qlist, nqb, tid, [&](int qb) {
+            const uint8_t *r = lh + (size_t)qb * nkb;
+            return (r[0] != 0 ? 1 : 0) | (kb0 + 1 < nkb && r[1] != 0 ? 2 : 0);
+        });
+        if (n > 0) {
+            const int last = __builtin_amdgcn_readfirstlane((int)(qlist[n - 1] & kListIndexMask));
+            ntl = 4 * (n - 1) + (last == nqb - 1 ? nt32 - 4 * last : 4);
+        }
+    } else {
+        int rlo, rhi;
+        rows_seeing<MASK>(k0, min(k0 + KPB - 1, Nkv - 1), Nq, Nkv, W, G, rlo, rhi);
+        t0 = rlo / BN;
+        ntl = rhi > rlo ? (rhi + BN - 1) / BN - t0 : 0;
+    }
+    // Tile n of the stream (n < ntl): its index among the 32-row tiles, and for the
+    // block-sparse layout the tag of its query block.
+    auto tile32 = [&](int n) {
+        if constexpr (MASK == kBlockSparse)
+            return __builtin_amdgcn_readfirstlane(
+                (int)(qlist[n / 4] & kListIndexMask) * 4 + n % 4);
+        else
+            return t0 + n;
+    };
     const char *qb = (const char *)(Q + qbase);
     const char *gb = (const char *)(dO + qbase);
     [[maybe_unused]] const float *stb = ST + (size_t)bh * nt32 * 64;  // device code only
@@ -411,11 +451,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // the slot of a tile already consumed) and touch no memory.
     auto load = [&](int n) {
         const bool real = n < ntl;
-        const int row0 = real ? (t0 + n) * BN : Nq;
+        const int tn = MASK == kBlockSparse ? (real ? tile32(n) : 0) : t0 + n;
+        const int row0 = real ? tn * BN : Nq;
         issue_kv<C>(qb, gb, off, row0, Nq, qslot(n), gslot(n), wave);
 #if defined(__HIP_DEVICE_COMPILE__)
         const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(stb + (real ? (size_t)(t0 + n) * 64 : 0)), (short)0,
+            const_cast<float *>(stb + (real ? (size_t)tn * 64 : 0)), (short)0,
             real ? kStatsBytes : 0, 0x00020000);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void *)sslot(n), 4, lane * 4, 0, 0, 0);
 #endif
@@ -431,9 +472,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         load(n + NS - 1);
         const char *qt = qslot(n), *gt = gslot(n);
         const float *st = (const float *)sslot(n);
-        const int ip0 = (t0 + n) * BN + delta;  // absolute position of the tile's row 0
+        const int ip0 = tile32(n) * BN + delta;  // absolute position of the tile's row 0
+        bool vis = true;
+        if constexpr (MASK == kBlockSparse)
+            vis = (__builtin_amdgcn_readfirstlane((int)qlist[n / 4]) >>
+                   (kListTagShift + (wave >> 1))) & 1;
 
-        dkdv_step<T, C, MASK>(qt, gt, vw, st, kf, dkt, dvt, kofs, tro, c, ip0, kw, li, g, W, G);
+        dkdv_step<T, C, MASK>(qt, gt, vw, st, kf, dkt, dvt, kofs, tro, c, ip0, kw, li, g, W, G,
+                              vis);
         // tile n + 1 resident (the NS - 2 tiles after it may still be in flight), then publish
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));
         ring_barrier();
@@ -552,9 +598,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ ST,
     uint16_t *__restrict__ dQ, int Nq, int Nkv, float c, float scale, int W, int G, int nqt,
-    int nt32)
+    int nt32, const uint8_t *__restrict__ layout, int H)
 {
     using C = CfgSP<D, kDqStages, 4>;
+    constexpr int SM = MASK == kBlockSparse ? 0 : MASK;  // element mask: the key tail only
     constexpr int BM = 128, BN = 32, NKK = C::NKK, NDB = C::NDB, NS = kDqStages, LPW = C::LPW;
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char *const lds = (char *)smem;
@@ -613,8 +660,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         ST[stats_index(bh, nt32, row) + 32] = -drow;
     }
 
-    const TileSchedule sch = make_schedule<MASK, BM, BN>(q0, Nq, Nkv, W, G);
-    const int ntl = sch.total, nint = sch.interior;
+    const TileSchedule sch = make_schedule<SM, BM, BN>(q0, Nq, Nkv, W, G);
+    int ntl = sch.total, nint = sch.interior;
+    // Block sparse: the key blocks this query block sees, listed in LDS after the ring as in
+    // the forward (key_block_list); only the key-tail tile is masked.
+    constexpr int TPB = kSparseBlock / BN;
+    const uint16_t *blist = (const uint16_t *)(lds + C::LDS_BYTES + 16);
+    if constexpr (MASK == kBlockSparse) {
+        const int nkb = (Nkv + kSparseBlock - 1) / kSparseBlock;
+        const uint8_t *lrow = layout + ((size_t)(bh % H) * nqt + q0 / kSparseBlock) * nkb;
+        key_block_list<C::NW, BN>(lds + C::LDS_BYTES, lrow, nkb, Nkv, tid, ntl, nint);
+    }
+    auto tile_at = [&](int p, const TileSchedule::Cursor &cu) {  // key tile at position p
+        if constexpr (MASK == kBlockSparse)
+            return __builtin_amdgcn_readfirstlane(
+                (int)(blist[p / TPB] & kListIndexMask) * TPB + p % TPB);
+        else
+            return cu.t;
+    };
     f32x16 dqt[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
@@ -643,7 +706,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     // (zero rows: it touches no memory and only writes zeros into a consumed slot).
     TileSchedule::Cursor ld = sch.begin(), cur = sch.begin();
     auto load = [&](int n) {
-        const int kv0 = n < ntl ? ld.t * BN : Nkv;
+        const int kv0 = n < ntl ? tile_at(n, ld) * BN : Nkv;
         issue_kv<C>(kb, vb, off, kv0, Nkv, kslot(n), vslot(n), wave);
         if (n < ntl) ld = sch.next(ld);
     };
@@ -658,9 +721,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     static_assert(NS == 4, "the steady loop is unrolled by the ring depth");
     auto steady = [&](int n) {
         const int p = n + NS - 1;
-        issue_kv<C>(kb, vb, off, sch.interior_tile(p) * BN, Nkv, kslot(p), vslot(p), wave);
-        dq_step<T, C, MASK>(kslot(n), vslot(n), qf, gf, dqt, kofs, tro, c, lrow, drow, false, 0,
-                            ip, Nkv, W, G, g);
+        const int tp = MASK == kBlockSparse ? tile_at(p, ld) : sch.interior_tile(p);
+        issue_kv<C>(kb, vb, off, tp * BN, Nkv, kslot(p), vslot(p), wave);
+        dq_step<T, C, SM>(kslot(n), vslot(n), qf, gf, dqt, kofs, tro, c, lrow, drow, false, 0,
+                          ip, Nkv, W, G, g);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile n + 1 resident
         ring_barrier();
     };
@@ -677,8 +741,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
     for (; n < ntl; ++n) {
         load(n + NS - 1);
-        dq_step<T, C, MASK>(kslot(n), vslot(n), qf, gf, dqt, kofs, tro, c, lrow, drow, n >= nint,
-                            cur.t * BN, ip, Nkv, W, G, g);
+        dq_step<T, C, SM>(kslot(n), vslot(n), qf, gf, dqt, kofs, tro, c, lrow, drow, n >= nint,
+                          tile_at(n, cur) * BN, ip, Nkv, W, G, g);
         cur = sch.next(cur);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));  // tile n + 1 resident
         ring_barrier();
@@ -701,26 +765,30 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s)
     // dQ first: it also writes the row statistics the dK/dV kernel reads.
     using CB = CfgSP<D, kDqStages, 4>;
     const int nqt = (a.Nq + 127) / 128;
+    // block sparse: wave counts and a list of up to kMaxKeyBlocks block ids after the ring
+    constexpr int list_bytes = MASK == kBlockSparse ? 16 + 2 * kMaxKeyBlocks : 0;
     auto kb = bwd_dq_kernel<T, D, MASK>;
+    const int lds_b = CB::LDS_BYTES + list_bytes;
     hipError_t e = hipFuncSetAttribute((const void *)kb,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, CB::LDS_BYTES);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_b);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kb, dim3((unsigned)((long)nqt * a.B * a.H)), dim3(256), CB::LDS_BYTES, s,
+    hipLaunchKernelGGL(kb, dim3((unsigned)((long)nqt * a.B * a.H)), dim3(256), lds_b, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        (const uint16_t *)a.dout, (const uint16_t *)a.o, a.lse, st,
-                       (uint16_t *)a.dq, a.Nq, a.Nkv, c, a.scale, a.window, a.n_global, nqt, nt32);
+                       (uint16_t *)a.dq, a.Nq, a.Nkv, c, a.scale, a.window, a.n_global, nqt, nt32,
+                       a.layout, a.H);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     using CA = CfgBD<D>;
     const int nkt = (a.Nkv + 255) / 256;
-    const int lds_a = CA::LDS_BYTES + kBwdStages * kStatsBytes + 256 * CA::ROWB;
+    const int lds_a = CA::LDS_BYTES + kBwdStages * kStatsBytes + 256 * CA::ROWB + list_bytes;
     auto ka = bwd_dkdv_kernel<T, D, MASK>;
     e = hipFuncSetAttribute((const void *)ka, hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ka, dim3((unsigned)((long)nkt * a.B * a.H)), dim3(256), lds_a, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        (const uint16_t *)a.dout, st, (uint16_t *)a.dk, (uint16_t *)a.dv, a.Nq,
-                       a.Nkv, c, a.scale, a.window, a.n_global, nkt, nt32);
+                       a.Nkv, c, a.scale, a.window, a.n_global, nkt, nt32, a.layout, a.H);
     return hipGetLastError();
 }
 
@@ -732,7 +800,8 @@ hipError_t launch_bwd_mask(const BwdArgs &a, hipStream_t s)
     case 1: return launch_bwd<T, D, 1>(a, s);
     case 2: return launch_bwd<T, D, 2>(a, s);
     case 3: return launch_bwd<T, D, 3>(a, s);
-    default: return launch_bwd<T, D, 4>(a, s);
+    case 4: return launch_bwd<T, D, 4>(a, s);
+    default: return launch_bwd<T, D, kBlockSparse>(a, s);
     }
 }
 

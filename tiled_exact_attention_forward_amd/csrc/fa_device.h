@@ -206,6 +206,68 @@ __device__ __forceinline__ TileSchedule make_schedule(int q0, int Nq, int Nkv, i
     return s;
 }
 
+// Block-sparse lists: the indices b < n (n <= kMaxKeyBlocks) whose 2-bit tag(b) is nonzero,
+// in ascending order, stored in LDS as b | tag(b) << 14 by the NW waves of a workgroup
+// (ballot and popcount per wave, the wave counts combined through wcnt[NW] in LDS).
+// Returns the number of entries, the same in every wave.
+constexpr int kListTagShift = 14, kListIndexMask = (1 << kListTagShift) - 1;
+template <int NW, typename Tag>
+__device__ __forceinline__ int compact_list(int *wcnt, uint16_t *list, int n, int tid, Tag tag)
+{
+    constexpr int CH = kMaxKeyBlocks / (64 * NW);
+    static_assert(kMaxKeyBlocks <= (1 << kListTagShift), "indices must fit below the tag");
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int f[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {  // every tag load first, one wait
+        const int b = u * 64 * NW + tid;
+        f[u] = b < n ? tag(b) : 0;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+        if (u * 64 * NW >= n) break;
+        const unsigned long long mk = __ballot(f[u] != 0);
+        if (lane == 0) wcnt[wave] = __popcll(mk);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int cw = wcnt[w];
+            before += w < wave ? cw : 0;
+            total += cw;
+        }
+        if (f[u] != 0)
+            list[cnt + before + __popcll(mk & ((1ull << lane) - 1))] =
+                (uint16_t)((u * 64 * NW + tid) | (f[u] << kListTagShift));
+        cnt += total;
+        __syncthreads();
+    }
+    return cnt;
+}
+
+// Key tiles of one query block under a block-sparse layout: lists the key blocks whose
+// entries in lrow (nkb of them) are set, at `at` + 16 in LDS (wave counts at `at`), and sets
+// the stream length ntl (position p holds key tile (kSparseBlock / BN) * list[p / (kSparseBlock
+// / BN)] + p % (kSparseBlock / BN); only the final key block can have fewer tiles, and it
+// comes last) and nint, the positions before the one tile with a key tail, if any.
+template <int NW, int BN>
+__device__ __forceinline__ void key_block_list(char *at, const uint8_t *lrow, int nkb, int Nkv,
+                                               int tid, int &ntl, int &nint)
+{
+    constexpr int TPB = kSparseBlock / BN;
+    uint16_t *list = (uint16_t *)(at + 16);
+    const int n = compact_list<NW>((int *)at, list, nkb, tid,
+                                   [&](int b) { return lrow[b] != 0 ? 1 : 0; });
+    ntl = nint = 0;
+    if (n > 0) {
+        const int lastb = __builtin_amdgcn_readfirstlane((int)(list[n - 1] & kListIndexMask));
+        const int all = (Nkv + BN - 1) / BN;
+        ntl = TPB * (n - 1) + (lastb == nkb - 1 ? all - TPB * lastb : TPB);
+        nint = ntl - (lastb == nkb - 1 && Nkv % BN != 0 ? 1 : 0);
+    }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Maximum that propagates NaN; it needs no quieting of its inputs, so a chain of them maps to

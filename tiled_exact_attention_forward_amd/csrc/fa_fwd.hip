@@ -286,51 +286,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     const int tail_kv0 = ((Nkv + BN - 1) / BN - 1) * BN;  // first key of the last key tile
     if constexpr (MASK == kBlockSparse) {
         static_assert(BM == kSparseBlock && kSparseBlock % BN == 0, "one query block per tile");
-        constexpr int TPB = kSparseBlock / BN, CH = kMaxKeyBlocks / (64 * NW);
         const int nkb = (Nkv + kSparseBlock - 1) / kSparseBlock;
         const uint8_t *lrow = layout + ((size_t)(bh % H) * nqt + q0 / kSparseBlock) * nkb;
-        int *wcnt = (int *)(lds + C::LDS_BYTES);
-        uint16_t *bl = (uint16_t *)(lds + C::LDS_BYTES + 16);
-        bool f[CH];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {  // all layout loads first, one wait
-            const int b = u * 64 * NW + tid;
-            f[u] = b < nkb && lrow[b] != 0;
-        }
-        int n = 0;
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            if (u * 64 * NW >= nkb) break;
-            const unsigned long long mk = __ballot(f[u]);
-            if (lane == 0) wcnt[wave] = __popcll(mk);
-            __syncthreads();
-            int before = 0, total = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const int cw = wcnt[w];
-                before += w < wave ? cw : 0;
-                total += cw;
-            }
-            if (f[u])
-                bl[n + before + __popcll(mk & ((1ull << lane) - 1))] =
-                    (uint16_t)(u * 64 * NW + tid);
-            n += total;
-            __syncthreads();
-        }
-        // stream position p holds tile TPB * blist[p / TPB] + p % TPB; only the final key
-        // block can have fewer tiles, and it comes last; only the key-tail tile is masked
-        if (n == 0) {
-            ntl = nint = 0;
-        } else {
-            const int lastb = __builtin_amdgcn_readfirstlane((int)bl[n - 1]);
-            const int all = (Nkv + BN - 1) / BN;
-            ntl = TPB * (n - 1) + (lastb == nkb - 1 ? all - TPB * lastb : TPB);
-            nint = ntl - (lastb == nkb - 1 && Nkv % BN != 0 ? 1 : 0);
-        }
+        key_block_list<NW, BN>(lds + C::LDS_BYTES, lrow, nkb, Nkv, tid, ntl, nint);
     }
     auto bs_tile = [&](int p) {
         constexpr int TPB = kSparseBlock / BN;
-        return __builtin_amdgcn_readfirstlane((int)blist[p / TPB] * TPB + p % TPB);
+        return __builtin_amdgcn_readfirstlane((int)(blist[p / TPB] & kListIndexMask) * TPB +
+                                              p % TPB);
     };
 
     float m = -INFINITY, nmu = 0.f, l = 0.f;

@@ -82,6 +82,7 @@ struct BwdArgs {
     float scale;
     int mask, window, n_global, dtype;
     void *workspace;  // backward_workspace_floats(B, H, Nq) floats of row statistics
+    const uint8_t *layout;  // block-sparse layout (mask 5), else null
 };
 
 // Row statistics of the backward: per 32-row tile of each (b, h), 32 log2-scaled LSE values
