@@ -68,3 +68,40 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
         assert e["lse_max_abs"] <= LSE_ABS, f"{label}: {e}"
         assert e["o_rel_l2"] <= REL_L2[dtype], f"{label}: {e}"
     return e
+
+
+# Unit roundoff of the 16-bit types, for the gradient tolerances below.
+U_GRAD = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def check_grads(got, ref, dtype, label, inputs, scale, vis):
+    """Gradients (dq, dk, dv) against the oracle's, with the backward's tolerance (stated in
+    test_backward_gpu's docstring): max-abs within 8u of each tensor's largest reference
+    value plus the float32 accumulation floor, rel-L2 within 4u, structural zeros exact.
+    inputs = (q, k, v, do) as given to both sides; vis = bool [Nq, Nkv] visibility, or the
+    pair (rows without a visible key, keys no row sees) already taken from it."""
+    u = U_GRAD[dtype]
+    q, k, v, do = (float(t.float().abs().max()) for t in inputs)
+    d = inputs[0].shape[-1]
+    fl = abs(scale) * 2 * d * 2.0 ** -20 * do * v * max(q, k)
+    if isinstance(vis, tuple):
+        zero_rows, zero_keys = vis
+    else:
+        zero_rows = ~vis.any(dim=1).numpy()  # [Nq]
+        zero_keys = ~vis.any(dim=0).numpy()  # [Nkv]
+    out = {}
+    for name, g, r, floor in zip(("dq", "dk", "dv"), got, ref, (fl, fl, 0.0)):
+        g = f64(g)
+        r = np.asarray(r, np.float64).reshape(g.shape)
+        assert not np.isnan(g).any(), f"{label}: NaN in {name}"
+        diff = np.abs(g - r)
+        rmax = float(np.abs(r).max()) if r.size else 0.0
+        mabs = float(diff.max()) if diff.size else 0.0
+        rl2 = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+        out[name] = (mabs, rmax, rl2)
+        assert mabs <= 8 * u * rmax + floor, f"{label}: {name} max-abs {mabs} ref max {rmax}"
+        if rmax > 64 * floor:
+            assert rl2 <= 4 * u, f"{label}: {name} rel-L2 {rl2}"
+        structural = zero_rows if name == "dq" else zero_keys
+        assert np.all(g[:, :, structural] == 0.0), f"{label}: {name} nonzero at a structural 0"
+    return out

@@ -29,13 +29,10 @@ import torch
 import oracle
 import tiled_exact_attention_forward_amd as fa
 import workloads
-from gpu_util import f64, to_dev
+from gpu_util import U_GRAD as U, check_grads, f64, to_dev
 from pins import band_mask
 
 pytestmark = pytest.mark.gpu
-
-U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
-
 
 def run_bwd(q, k, v, do, scale, mask=0, W=0, G=0):
     qd, kd, vd, gd = to_dev(q, k, v, do)
@@ -43,36 +40,6 @@ def run_bwd(q, k, v, do, scale, mask=0, W=0, G=0):
     dq, dk, dv = fa.fa_backward(qd, kd, vd, o, lse, gd, scale, mask, W, G)
     torch.cuda.synchronize()
     return dq, dk, dv
-
-
-def check_grads(got, ref, dtype, label, inputs, scale, vis):
-    """inputs = (q, k, v, do) as given to both sides; vis = bool [Nq, Nkv] visibility, or the
-    pair (rows without a visible key, keys no row sees) already taken from it."""
-    u = U[dtype]
-    q, k, v, do = (float(t.float().abs().max()) for t in inputs)
-    d = inputs[0].shape[-1]
-    fl = abs(scale) * 2 * d * 2.0 ** -20 * do * v * max(q, k)
-    if isinstance(vis, tuple):
-        zero_rows, zero_keys = vis
-    else:
-        zero_rows = ~vis.any(dim=1).numpy()  # [Nq]
-        zero_keys = ~vis.any(dim=0).numpy()  # [Nkv]
-    out = {}
-    for name, g, r, floor in zip(("dq", "dk", "dv"), got, ref, (fl, fl, 0.0)):
-        g = f64(g)
-        r = np.asarray(r, np.float64).reshape(g.shape)
-        assert not np.isnan(g).any(), f"{label}: NaN in {name}"
-        diff = np.abs(g - r)
-        rmax = float(np.abs(r).max()) if r.size else 0.0
-        mabs = float(diff.max()) if diff.size else 0.0
-        rl2 = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
-        out[name] = (mabs, rmax, rl2)
-        assert mabs <= 8 * u * rmax + floor, f"{label}: {name} max-abs {mabs} ref max {rmax}"
-        if rmax > 64 * floor:
-            assert rl2 <= 4 * u, f"{label}: {name} rel-L2 {rl2}"
-        structural = zero_rows if name == "dq" else zero_keys
-        assert np.all(g[:, :, structural] == 0.0), f"{label}: {name} nonzero at a structural 0"
-    return out
 
 
 MASKS = [(0, 0, 0), (1, 0, 0), (2, 40, 5), (2, 1, 0), (2, 100, 70), (2, 65, 63), (3, 0, 0),
