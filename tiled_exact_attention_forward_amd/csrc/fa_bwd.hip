@@ -407,6 +407,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // The 32-row tiles this workgroup visits: a range of tiles for masks 0-4; for the
     // block-sparse layout, the query blocks that see either of its two 128-key blocks, listed
     // in LDS after the V rows (each entry tagged with which of the two blocks it sees).
+    constexpr int TPQ = kSparseBlock / BN;  // 32-row tiles per query block
     int t0 = 0, ntl = 0;
     char *const lst = vl + 256 * C::ROWB;
     const uint16_t *qlist = (const uint16_t *)(lst + 16);
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         });
         if (n > 0) {
             const int last = __builtin_amdgcn_readfirstlane((int)(qlist[n - 1] & kListIndexMask));
-            ntl = 4 * (n - 1) + (last == nqb - 1 ? nt32 - 4 * last : 4);
+            ntl = TPQ * (n - 1) + (last == nqb - 1 ? nt32 - TPQ * last : TPQ);
         }
     } else {
         int rlo, rhi;
@@ -429,12 +430,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         t0 = rlo / BN;
         ntl = rhi > rlo ? (rhi + BN - 1) / BN - t0 : 0;
     }
-    // Tile n of the stream (n < ntl): its index among the 32-row tiles, and for the
-    // block-sparse layout the tag of its query block.
+    // Tile n of the stream (n < ntl): its index among the 32-row tiles (block sparse: tile
+    // n % TPQ of the listed query block n / TPQ).
     auto tile32 = [&](int n) {
         if constexpr (MASK == kBlockSparse)
             return __builtin_amdgcn_readfirstlane(
-                (int)(qlist[n / 4] & kListIndexMask) * 4 + n % 4);
+                (int)(qlist[n / TPQ] & kListIndexMask) * TPQ + n % TPQ);
         else
             return t0 + n;
     };
@@ -475,8 +476,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const int ip0 = tile32(n) * BN + delta;  // absolute position of the tile's row 0
         bool vis = true;
         if constexpr (MASK == kBlockSparse)
-            vis = (__builtin_amdgcn_readfirstlane((int)qlist[n / 4]) >>
-                   (kListTagShift + (wave >> 1))) & 1;
+            vis = (__builtin_amdgcn_readfirstlane((int)qlist[n / TPQ]) >>
+                   (kListTagShift + (wave >> 1))) & 1;  // waves 0-1: the first key block
 
         dkdv_step<T, C, MASK>(qt, gt, vw, st, kf, dkt, dvt, kofs, tro, c, ip0, kw, li, g, W, G,
                               vis);
