@@ -88,12 +88,12 @@ __device__ __forceinline__ void mma_agpr(f32x16 &acc, s16x8 a, s16x8 b)
 // 24 wait states after the last inline MFMA into acc[h][*] and before anything reads them:
 // the accumulators are the statement's operands, which orders it after their writers and
 // before their readers.
-template <int NDB>
-__device__ __forceinline__ void settle_agpr(f32x16 (&acc)[2][NDB])
+template <int NH, int NDB>
+__device__ __forceinline__ void settle_agpr(f32x16 (&acc)[NH][NDB])
 {
     static_assert(NDB == 2 || NDB == 4, "d 64 or 128");
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
         if constexpr (NDB == 4)
             __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                              : "+a"(acc[h][0]), "+a"(acc[h][1]), "+a"(acc[h][2]), "+a"(acc[h][3]));
@@ -151,23 +151,23 @@ __device__ __forceinline__ bool block_visible(int i0, int i1, int k0, int k1, in
     return k1 <= i0 || k1 < G;
 }
 
-// One 32-row tile of the dK/dV kernel for this wave's 64 keys: qt, gt and st are the tile's
+// One 32-row tile of the dK/dV kernel for this wave's 32 NH keys (NH halves of 32): qt, gt
+// and st are the tile's
 // Q, dO and statistics in LDS, vw the wave's V rows. The pointers are restrict-qualified:
 // nothing else in the step touches that memory, which also tells the compiler that the
 // loads of later tiles into other slots, still in flight, cannot overlap these reads.
-template <typename T, typename C, int MASK>
+template <typename T, typename C, int MASK, int NH>
 __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const char *__restrict__ gt,
                                           const char *__restrict__ vw,
                                           const float *__restrict__ st,
-                                          const s16x8 (&kf)[2][C::NKK],
-                                          f32x16 (&dkt)[2][C::NDB], f32x16 (&dvt)[2][C::NDB],
+                                          const s16x8 (&kf)[NH][C::NKK],
+                                          f32x16 (&dkt)[NH][C::NDB], f32x16 (&dvt)[NH][C::NDB],
                                           const int (&kofs)[C::NKK], const int (&tro)[2][C::NDB],
-                                          float c, int ip0, int kw, int li, int g, int W, int G,
-                                          bool vis)
+                                          float c, int ip0, int kw, int li, int g, int W, int G)
 {
     using Op = Ops16<T>;
     constexpr int BN = 32, NKK = C::NKK, NDB = C::NDB;
-    f32x16 s[2], dp[2];
+    f32x16 s[2], dp[2];  // per half (only [0] when NH = 1)
     {
         // all Q fragments first, then both halves' MFMAs, which share each fragment
         s16x8 a[NKK];
@@ -176,23 +176,18 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             s[0] = Op::mma(a[kk], kf[0][kk], kk == 0 ? f32x16{} : s[0]);
-            s[1] = Op::mma(a[kk], kf[1][kk], kk == 0 ? f32x16{} : s[1]);
+            if constexpr (NH == 2) s[1] = Op::mma(a[kk], kf[1][kk], kk == 0 ? f32x16{} : s[1]);
         }
     }
-    // Block sparse: vis says whether the layout shows this wave's key block to the tile's
-    // query block (all or nothing); the other masks decide per element.
-    const bool full =
-        MASK == kBlockSparse ? vis : block_visible<MASK>(ip0, ip0 + BN - 1, kw, kw + 63, W, G);
+    // Block sparse: the workgroup visits only query blocks that see its key block, whole;
+    // the other masks decide per element.
+    const bool full = MASK == kBlockSparse ||
+                      block_visible<MASK>(ip0, ip0 + BN - 1, kw, kw + 32 * NH - 1, W, G);
     int lo[2] = {INT_MIN, INT_MIN}, hi[2] = {INT_MAX, INT_MAX};
-    if (MASK != 0 && !full) {
-        if constexpr (MASK == kBlockSparse) {
-            lo[0] = lo[1] = 1;  // an empty range: P = 0 for every row
-            hi[0] = hi[1] = 0;
-        } else {
+    if (MASK != 0 && MASK != kBlockSparse && !full) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                key_row_range<MASK>(kw + 32 * h + li, ip0 + 4 * g, W, G, lo[h], hi[h]);
-        }
+        for (int h = 0; h < NH; ++h)
+            key_row_range<MASK>(kw + 32 * h + li, ip0 + 4 * g, W, G, lo[h], hi[h]);
     }
     // dP = dO V^T; P = 2^(c S - L) is formed alongside, two elements of each half per
     // step, so that one wave keeps its matrix and vector units busy together.
@@ -208,25 +203,28 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
             __builtin_shufflevector(nd4[0], nd4[1], 0, 1, 2, 3, 4, 5, 6, 7),
             __builtin_shufflevector(nd4[2], nd4[3], 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3, 4, 5,
             6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        // V fragments of the halves (rows 32 h + key; v1 unused when NH = 1)
         s16x8 a = *(const s16x8 *)(gt + kofs[0]);
         s16x8 v0 = *(const s16x8 *)(vw + kofs[0]);
-        s16x8 v1 = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[0]);
+        s16x8 v1 = NH == 2 ? *(const s16x8 *)(vw + 32 * C::ROWB + kofs[0]) : v0;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const int kn = (kk + 1) % NKK;
             const s16x8 an = *(const s16x8 *)(gt + kofs[kn]);
             const s16x8 v0n = *(const s16x8 *)(vw + kofs[kn]);
-            const s16x8 v1n = *(const s16x8 *)(vw + 32 * C::ROWB + kofs[kn]);
+            const s16x8 v1n = NH == 2 ? *(const s16x8 *)(vw + 32 * C::ROWB + kofs[kn]) : v0n;
             dp[0] = Op::mma(a, v0, kk == 0 ? nd : dp[0]);
-            dp[1] = Op::mma(a, v1, kk == 0 ? nd : dp[1]);
+            if constexpr (NH == 2) dp[1] = Op::mma(a, v1, kk == 0 ? nd : dp[1]);
 #pragma unroll
             for (int e = 16 * kk / NKK; e < 16 * (kk + 1) / NKK; ++e) {
                 const int r = 8 * (e >> 2) + (e & 3);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < NH; ++h) {
                     const float p =
                         fast_exp2(__builtin_fmaf(s[h][e], c, -lv[e >> 2][e & 3]));
-                    s[h][e] = (MASK == 0 || (r >= lo[h] && r <= hi[h])) ? p : 0.f;
+                    s[h][e] = (MASK == 0 || MASK == kBlockSparse || (r >= lo[h] && r <= hi[h]))
+                                  ? p
+                                  : 0.f;
                 }
             }
             a = an;
@@ -242,7 +240,7 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
             const int o8 = 8 * kc;
             s16x8 pf[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < NH; ++h)
                 pf[h] = Op::pack8(s[h][o8], s[h][o8 + 1], s[h][o8 + 2], s[h][o8 + 3],
                                   s[h][o8 + 4], s[h][o8 + 5], s[h][o8 + 6], s[h][o8 + 7]);
             const char *p0 = gt + kc * 16 * C::ROWB;
@@ -255,11 +253,11 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
                 const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
                 const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
                 mma_agpr<T>(dvt[0][db], ta, pf[0]);
-                mma_agpr<T>(dvt[1][db], ta, pf[1]);
+                if constexpr (NH == 2) mma_agpr<T>(dvt[1][db], ta, pf[1]);
 #pragma unroll
                 for (int e = o8 + 8 * db / NDB; e < o8 + 8 * (db + 1) / NDB; ++e)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < NH; ++h)
                         dp[h][e] = s[h][e] * dp[h][e];
                 tlo = lon;
                 thi = hin;
@@ -273,7 +271,7 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
         const int o8 = 8 * kc;
         s16x8 sf[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NH; ++h)
             sf[h] = Op::pack8(dp[h][o8], dp[h][o8 + 1], dp[h][o8 + 2], dp[h][o8 + 3],
                               dp[h][o8 + 4], dp[h][o8 + 5], dp[h][o8 + 6], dp[h][o8 + 7]);
         const char *p0 = qt + kc * 16 * C::ROWB;
@@ -286,7 +284,7 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
             const s16x4 hin = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + tro[1][dn]));
             const s16x8 ta = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
             mma_agpr<T>(dkt[0][db], ta, sf[0]);
-            mma_agpr<T>(dkt[1][db], ta, sf[1]);
+            if constexpr (NH == 2) mma_agpr<T>(dkt[1][db], ta, sf[1]);
             tlo = lon;
             thi = hin;
             __builtin_amdgcn_sched_barrier(0);
@@ -294,10 +292,12 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
     }
 }
 
-// dK and dV. A workgroup owns 256 keys, 64 per wave in two 32-key halves. K fragments stay in
-// registers and V rows in LDS (64 KB, loaded once; registers go to the dK/dV accumulators);
-// each Q or dO fragment read from LDS feeds both halves, which halves the LDS reads per
-// MFMA against 32 keys per wave. Per 32-row tile:
+// dK and dV. A workgroup owns 256 keys, 64 per wave in two 32-key halves (NH = 2). K fragments
+// stay in registers and V rows in LDS (64 KB, loaded once; registers go to the dK/dV
+// accumulators); each Q or dO fragment read from LDS feeds both halves, which halves the LDS
+// reads per MFMA against 32 keys per wave. Under a block-sparse layout a workgroup owns one
+// 128-key block, 32 keys per wave (NH = 1): with two blocks per workgroup, every query block
+// that sees only one of them would cost the other's products too. Per 32-row tile:
 //   S = Q K^T, dP = dO V^T           (lanes indexed by key: lane (g, key) holds rows
 //                                     8(e/4) + 4g + e%4 of each half)
 //   P = 2^(c S - L), dS = P (dP - D) (elementwise, fp32)
@@ -305,6 +305,9 @@ __device__ __forceinline__ void dkdv_step(const char *__restrict__ qt, const cha
 //                                     read transposed from LDS)
 // The MFMA order (S of both halves, then dP while the exponentials of P run, then dV while
 // dS is formed, then dK) lets one wave per SIMD overlap its vector and matrix work.
+template <int MASK>
+constexpr int dkdv_halves() { return MASK == kBlockSparse ? 1 : 2; }
+
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     using C = CfgBD<D>;
     using Op = Ops16<T>;
     constexpr int BN = 32, NKK = C::NKK, NDB = C::NDB, NS = kBwdStages, LPW = C::LPW;
-    constexpr int KPB = 256;  // keys per workgroup
+    constexpr int NH = dkdv_halves<MASK>();  // 32-key halves per wave
+    constexpr int KPB = 128 * NH;            // keys per workgroup
     extern __shared__ __attribute__((aligned(1024))) uint16_t smem[];
     char *const lds = (char *)smem;
 
@@ -343,14 +347,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         }
     }
     const int k0 = kb * KPB;
-    const int kw = k0 + wave * 64;  // this wave's first key
+    const int kw = k0 + wave * 32 * NH;  // this wave's first key
     const size_t qbase = (size_t)bh * Nq * D, kvbase = (size_t)bh * Nkv * D;
     const int delta = Nkv - Nq;
 
     // K rows of this lane's two keys as MFMA fragments (keys past Nkv read as zeros).
-    s16x8 kf[2][NKK];
+    s16x8 kf[NH][NKK];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
         const int key = kw + 32 * h + li;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
@@ -358,30 +362,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
                             ? *(const s16x8 *)(K + kvbase + (size_t)key * D + 16 * kk + 8 * g)
                             : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    // V rows of this wave's 64 keys go to LDS (after the ring and the statistics) with the
+    // V rows of this wave's 32 NH keys go to LDS (after the ring and the statistics) with the
     // same swizzle as the Q and dO tiles (they share the read offsets), each wave loading its
     // own rows, zero past Nkv.
     char *const vl = lds + C::LDS_BYTES + NS * kStatsBytes;
 #if defined(__HIP_DEVICE_COMPILE__)
     {
-        const int rows = min(max(Nkv - kw, 0), 64);
+        const int rows = min(max(Nkv - kw, 0), 32 * NH);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(V + kvbase + (size_t)min(kw, Nkv - 1) * D), (short)0,
             rows * C::ROWB, 0x00020000);
-        constexpr int VLOADS = 64 * C::ROWB / 1024;  // wave-wide 1 KB loads for 64 rows
+        constexpr int VLOADS = 32 * NH * C::ROWB / 1024;  // wave-wide 1 KB loads
 #pragma unroll
         for (int u = 0; u < VLOADS; ++u) {
             const int r = u * C::ROWS_PER_LOAD + lane / C::CHUNKS;
             const unsigned vo = r * C::ROWB + 16 * b_swz<D>(r, lane % C::CHUNKS);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vr, (lds_void *)(vl + (wave * 64 + u * C::ROWS_PER_LOAD) * C::ROWB), 16, vo, 0,
-                0, 0);
+                vr, (lds_void *)(vl + (wave * 32 * NH + u * C::ROWS_PER_LOAD) * C::ROWB), 16, vo,
+                0, 0, 0);
         }
     }
 #endif
-    f32x16 dkt[2][NDB], dvt[2][NDB];
+    f32x16 dkt[NH][NDB], dvt[NH][NDB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dkt[h][db] = dvt[h][db] = f32x16{};
 
@@ -402,26 +406,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) tro[h][db] = tr_ofs<D>(lane, h, db);
-    const char *const vw = vl + wave * 64 * C::ROWB;  // this wave's V rows
+    const char *const vw = vl + wave * 32 * NH * C::ROWB;  // this wave's V rows
 
     // The 32-row tiles this workgroup visits: a range of tiles for masks 0-4; for the
-    // block-sparse layout, the query blocks that see either of its two 128-key blocks, listed
-    // in LDS after the V rows (each entry tagged with which of the two blocks it sees).
+    // block-sparse layout, the query blocks that see its 128-key block, listed in LDS after
+    // the V rows.
     constexpr int TPQ = kSparseBlock / BN;  // 32-row tiles per query block
     int t0 = 0, ntl = 0;
-    char *const lst = vl + 256 * C::ROWB;
+    char *const lst = vl + KPB * C::ROWB;
     const uint16_t *qlist = (const uint16_t *)(lst + 16);
     if constexpr (MASK == kBlockSparse) {
         const int nkb = (Nkv + kSparseBlock - 1) / kSparseBlock;
         const int nqb = (Nq + kSparseBlock - 1) / kSparseBlock;
-        const int kb0 = k0 / kSparseBlock;
-        const uint8_t *lh = layout + (size_t)(bh % H) * nqb * nkb + kb0;
-        const int n = compact_list<C::NW>((int *)lst, (uint16_t *)qlist, nqb, tid, [&](int qb) {
-            const uint8_t *r = lh + (size_t)qb * nkb;
-            return (r[0] != 0 ? 1 : 0) | (kb0 + 1 < nkb && r[1] != 0 ? 2 : 0);
-        });
+        static_assert(KPB == kSparseBlock, "one key block per workgroup");
+        const uint8_t *lh = layout + (size_t)(bh % H) * nqb * nkb + k0 / kSparseBlock;
+        const int n = compact_list<C::NW>((int *)lst, (uint16_t *)qlist, nqb, tid,
+                                          [&](int qb) { return lh[(size_t)qb * nkb] != 0; });
         if (n > 0) {
-            const int last = __builtin_amdgcn_readfirstlane((int)(qlist[n - 1] & kListIndexMask));
+            const int last = __builtin_amdgcn_readfirstlane((int)qlist[n - 1]);
             ntl = TPQ * (n - 1) + (last == nqb - 1 ? nt32 - TPQ * last : TPQ);
         }
     } else {
@@ -434,8 +436,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // n % TPQ of the listed query block n / TPQ).
     auto tile32 = [&](int n) {
         if constexpr (MASK == kBlockSparse)
-            return __builtin_amdgcn_readfirstlane(
-                (int)(qlist[n / TPQ] & kListIndexMask) * TPQ + n % TPQ);
+            return __builtin_amdgcn_readfirstlane((int)qlist[n / TPQ] * TPQ + n % TPQ);
         else
             return t0 + n;
     };
@@ -474,13 +475,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const char *qt = qslot(n), *gt = gslot(n);
         const float *st = (const float *)sslot(n);
         const int ip0 = tile32(n) * BN + delta;  // absolute position of the tile's row 0
-        bool vis = true;
-        if constexpr (MASK == kBlockSparse)
-            vis = (__builtin_amdgcn_readfirstlane((int)qlist[n / TPQ]) >>
-                   (kListTagShift + (wave >> 1))) & 1;  // waves 0-1: the first key block
 
-        dkdv_step<T, C, MASK>(qt, gt, vw, st, kf, dkt, dvt, kofs, tro, c, ip0, kw, li, g, W, G,
-                              vis);
+        dkdv_step<T, C, MASK, NH>(qt, gt, vw, st, kf, dkt, dvt, kofs, tro, c, ip0, kw, li, g, W,
+                                  G);
         // tile n + 1 resident (the NS - 2 tiles after it may still be in flight), then publish
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAhead));
         ring_barrier();
@@ -503,8 +500,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // for a 16-pass MFMA; the inline MFMAs are invisible to the compiler's hazard checks).
     // The padding takes the accumulators as operands, so every MFMA that writes one comes
     // before it and every read of one after it, wherever the compiler places the reads.
-    settle_agpr<NDB>(dkt);
-    settle_agpr<NDB>(dvt);
+    settle_agpr<NH, NDB>(dkt);
+    settle_agpr<NH, NDB>(dvt);
 
     // dK^T / dV^T: lane (g, key) holds columns db*32 + 8(e/4) + 4g + e%4. Rows go out
     // through LDS (this wave's 64 rows, padded by 16 bytes against bank conflicts; the ring
@@ -512,14 +509,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // of 16 bytes per row, all waves of the chip finishing together, left partly written
     // lines for the L2 to evict and write back more than once.
     constexpr int RP = C::ROWB + 16;
-    static_assert(4 * 64 * RP <= C::LDS_BYTES + NS * kStatsBytes + 256 * C::ROWB, "staging");
-    char *const stg = lds + wave * 64 * RP;
+    static_assert(4 * 32 * NH * RP <= C::LDS_BYTES + NS * kStatsBytes + KPB * C::ROWB,
+                  "staging");
+    char *const stg = lds + wave * 32 * NH * RP;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // dK, then dV
         uint16_t *dst = (t == 0 ? dK : dV) + kvbase;
         const float f = t == 0 ? scale : 1.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -533,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         __asm__ volatile("" ::: "memory");
         constexpr int PER_ROW = C::ROWB / 16;  // 16-byte pieces of a row
 #pragma unroll
-        for (int it = 0; it < 64 * PER_ROW / 64; ++it) {
+        for (int it = 0; it < 32 * NH * PER_ROW / 64; ++it) {
             const int i = it * 64 + lane, r = i / PER_ROW, cpos = i % PER_ROW;
             const s16x8 val = *(const s16x8 *)(stg + r * RP + 16 * cpos);
             if (kw + r < Nkv) *(s16x8 *)(dst + (size_t)(kw + r) * D + 8 * cpos) = val;
@@ -674,8 +672,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
     auto tile_at = [&](int p, const TileSchedule::Cursor &cu) {  // key tile at position p
         if constexpr (MASK == kBlockSparse)
-            return __builtin_amdgcn_readfirstlane(
-                (int)(blist[p / TPB] & kListIndexMask) * TPB + p % TPB);
+            return __builtin_amdgcn_readfirstlane((int)blist[p / TPB] * TPB + p % TPB);
         else
             return cu.t;
     };
@@ -781,8 +778,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     using CA = CfgBD<D>;
-    const int nkt = (a.Nkv + 255) / 256;
-    const int lds_a = CA::LDS_BYTES + kBwdStages * kStatsBytes + 256 * CA::ROWB + list_bytes;
+    constexpr int KPB = 128 * dkdv_halves<MASK>();  // keys per dK/dV workgroup
+    const int nkt = (a.Nkv + KPB - 1) / KPB;
+    const int lds_a = CA::LDS_BYTES + kBwdStages * kStatsBytes + KPB * CA::ROWB + list_bytes;
     auto ka = bwd_dkdv_kernel<T, D, MASK>;
     e = hipFuncSetAttribute((const void *)ka, hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
     if (e != hipSuccess) return e;

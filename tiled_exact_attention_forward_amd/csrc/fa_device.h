@@ -206,28 +206,26 @@ __device__ __forceinline__ TileSchedule make_schedule(int q0, int Nq, int Nkv, i
     return s;
 }
 
-// Block-sparse lists: the indices b < n (n <= kMaxKeyBlocks) whose 2-bit tag(b) is nonzero,
-// in ascending order, stored in LDS as b | tag(b) << 14 by the NW waves of a workgroup
-// (ballot and popcount per wave, the wave counts combined through wcnt[NW] in LDS).
-// Returns the number of entries, the same in every wave.
-constexpr int kListTagShift = 14, kListIndexMask = (1 << kListTagShift) - 1;
-template <int NW, typename Tag>
-__device__ __forceinline__ int compact_list(int *wcnt, uint16_t *list, int n, int tid, Tag tag)
+// Block-sparse lists: the indices b < n (n <= kMaxKeyBlocks) for which pred(b) holds, in
+// ascending order, stored in LDS by the NW waves of a workgroup (ballot and popcount per wave,
+// the wave counts combined through wcnt[NW] in LDS). Returns the number of entries, the same
+// in every wave.
+template <int NW, typename Pred>
+__device__ __forceinline__ int compact_list(int *wcnt, uint16_t *list, int n, int tid, Pred pred)
 {
     constexpr int CH = kMaxKeyBlocks / (64 * NW);
-    static_assert(kMaxKeyBlocks <= (1 << kListTagShift), "indices must fit below the tag");
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int f[CH];
+    bool f[CH];
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {  // every tag load first, one wait
+    for (int u = 0; u < CH; ++u) {  // every layout load first, one wait
         const int b = u * 64 * NW + tid;
-        f[u] = b < n ? tag(b) : 0;
+        f[u] = b < n && pred(b);
     }
     int cnt = 0;
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
         if (u * 64 * NW >= n) break;
-        const unsigned long long mk = __ballot(f[u] != 0);
+        const unsigned long long mk = __ballot(f[u]);
         if (lane == 0) wcnt[wave] = __popcll(mk);
         __syncthreads();
         int before = 0, total = 0;
@@ -237,9 +235,9 @@ __device__ __forceinline__ int compact_list(int *wcnt, uint16_t *list, int n, in
             before += w < wave ? cw : 0;
             total += cw;
         }
-        if (f[u] != 0)
+        if (f[u])
             list[cnt + before + __popcll(mk & ((1ull << lane) - 1))] =
-                (uint16_t)((u * 64 * NW + tid) | (f[u] << kListTagShift));
+                (uint16_t)(u * 64 * NW + tid);
         cnt += total;
         __syncthreads();
     }
@@ -257,11 +255,10 @@ __device__ __forceinline__ void key_block_list(char *at, const uint8_t *lrow, in
 {
     constexpr int TPB = kSparseBlock / BN;
     uint16_t *list = (uint16_t *)(at + 16);
-    const int n = compact_list<NW>((int *)at, list, nkb, tid,
-                                   [&](int b) { return lrow[b] != 0 ? 1 : 0; });
+    const int n = compact_list<NW>((int *)at, list, nkb, tid, [&](int b) { return lrow[b] != 0; });
     ntl = nint = 0;
     if (n > 0) {
-        const int lastb = __builtin_amdgcn_readfirstlane((int)(list[n - 1] & kListIndexMask));
+        const int lastb = __builtin_amdgcn_readfirstlane((int)list[n - 1]);
         const int all = (Nkv + BN - 1) / BN;
         ntl = TPB * (n - 1) + (lastb == nkb - 1 ? all - TPB * lastb : TPB);
         nint = ntl - (lastb == nkb - 1 && Nkv % BN != 0 ? 1 : 0);

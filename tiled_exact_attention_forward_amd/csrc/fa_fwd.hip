@@ -292,8 +292,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(
     }
     auto bs_tile = [&](int p) {
         constexpr int TPB = kSparseBlock / BN;
-        return __builtin_amdgcn_readfirstlane((int)(blist[p / TPB] & kListIndexMask) * TPB +
-                                              p % TPB);
+        return __builtin_amdgcn_readfirstlane((int)blist[p / TPB] * TPB + p % TPB);
     };
 
     float m = -INFINITY, nmu = 0.f, l = 0.f;
