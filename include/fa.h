@@ -135,9 +135,11 @@ int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o
  *  dq             [B, H, Nq, d] dtype, written.
  *  dk, dv         [B, H, Nkv, d] dtype, written (zero for a key no query sees).
  *  B .. n_global  as fa_forward. A row with lse = -inf (no visible key) contributes nothing.
- *  dtype          FA_F16 or FA_BF16 only. Products take fp16/bf16 operands (P and dS are
+ *  dtype          FA_F16 or FA_BF16: products take fp16/bf16 operands (P and dS are
  *                 rounded to dtype) with float32 accumulation; the outputs are rounded
- *                 once at the end.
+ *                 once at the end. FA_F32: float32 operands and products throughout (the
+ *                 pages recommend fp32 or bf16 for training: ops-transformer article on
+ *                 gitcode.csdn.net, section 三.2); a plain, untuned pair of kernels.
  *  workspace      device buffer of at least fa_backward_workspace_bytes(B, H, Nq) bytes
  *                 (per-row D and log2-scaled LSE, grouped by 32-row tile); contents need no
  *                 initialisation; 16-byte aligned.

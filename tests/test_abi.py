@@ -151,7 +151,7 @@ def bwd(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=1, Nq=8, Nkv=8
     (dict(do=N), fa.FA_ERR_NULL), (dict(dq=N), fa.FA_ERR_NULL), (dict(dk=N), fa.FA_ERR_NULL),
     (dict(dv=N), fa.FA_ERR_NULL),
     (dict(B=0), fa.FA_ERR_SHAPE), (dict(Nkv=0), fa.FA_ERR_SHAPE),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=5), fa.FA_ERR_UNSUPPORTED), (dict(mask=5), fa.FA_ERR_UNSUPPORTED),
     (dict(mask=2, W=0), fa.FA_ERR_SHAPE), (dict(mask=3, W=-2), fa.FA_ERR_SHAPE),
     (dict(mask=4, G=-1), fa.FA_ERR_SHAPE), (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
@@ -176,7 +176,7 @@ def bwd_bs(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=1, Nq=8, Nk
     (dict(layout=N), fa.FA_ERR_NULL), (dict(q=N), fa.FA_ERR_NULL), (dict(dv=N), fa.FA_ERR_NULL),
     (dict(block=64), fa.FA_ERR_UNSUPPORTED), (dict(Nkv=262145), fa.FA_ERR_UNSUPPORTED),
     (dict(Nq=262145), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(Nq=0), fa.FA_ERR_SHAPE),
+    (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED), (dict(Nq=0), fa.FA_ERR_SHAPE),
     (dict(scale=float("nan")), fa.FA_ERR_SHAPE), (dict(ws=N), fa.FA_ERR_WORKSPACE),
     (dict(wsb=8 * 4), fa.FA_ERR_WORKSPACE), (dict(dq=ctypes.c_void_p(0x1004)), fa.FA_ERR_UNSUPPORTED),
 ])

@@ -61,7 +61,7 @@ SHAPES = [(1, 1, 1, 1), (1, 2, 300, 300), (2, 1, 200, 457), (1, 2, 513, 129), (1
           (1, 3, 1000, 1000), (1, 2, 129, 640)]
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("density", [0.3, 0.7])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -78,7 +78,7 @@ def test_backward_block_sparse_small(dtype, d, density, shape):
                    lay)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_all_ones_layout_equals_unmasked_bitwise(dtype):
     q, k, v = workloads.gen_prefill(2, 2, 300, 420, 128, dtype, 31)
     do = workloads.gen_dout((2, 2, 300, 128), dtype, 32)

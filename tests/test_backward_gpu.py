@@ -8,7 +8,8 @@ prefix LM, window and band at N = 32768) run in the benchmark's launch configura
 compare every gradient element, head by head.
 
 Tolerance (gradients are sums of many products whose operands P and dS are rounded to the
-16-bit type, u = 2^-8 for bf16 and 2^-11 for fp16, and D_i uses the forward's rounded O):
+16-bit type, u = 2^-8 for bf16 and 2^-11 for fp16, and D_i uses the forward's rounded O; the
+float32 backward rounds nothing to 16 bits and takes u = 2^-16, derived in gpu_util):
   * max |g_gpu - g_ref| <= 8u * max |g_ref| + F over each gradient tensor, and
     ||g_gpu - g_ref||_2 <= 4u * ||g_ref||_2 (three roundings of relative size <= u/2 each);
   * F is the float32 accumulation floor of dS = P (dP - D): both dP_ij and D_i are d-term
@@ -48,7 +49,7 @@ SHAPES = [(1, 1, 1, 1), (1, 2, 17, 17), (2, 3, 100, 100), (1, 2, 129, 129), (1, 
           (1, 2, 64, 200), (1, 2, 200, 64), (1, 1, 1, 333), (1, 2, 257, 513)]
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", MASKS, ids=lambda m: f"m{m[0]}w{m[1]}g{m[2]}")
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -265,7 +265,7 @@ def _backward_args(q, k, v, o, lse, dout, dq, dk, dv, workspace):
 
 def fa_backward(q, k, v, o, lse, dout, scale=None, mask_mode=FA_MASK_NONE, window=0,
                 n_global=0, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV of fa_forward: q [B,H,Nq,d], k/v [B,H,Nkv,d] (f16/bf16), o and lse the
+    """dQ, dK, dV of fa_forward: q [B,H,Nq,d], k/v [B,H,Nkv,d] (f32/f16/bf16), o and lse the
     forward's outputs for the same arguments, dout like o. Returns (dq, dk, dv)."""
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]

@@ -6,6 +6,7 @@
 #include <algorithm>
 
 #include "fa.h"
+#include "fa_bwd32.h"
 #include "fa_launch.h"
 
 namespace {
@@ -206,7 +207,7 @@ int check_backward(const void *q, const void *k, const void *v, const void *o, c
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     const long long bh = (long long)B * H;
     if (bh * ((Nq + 127) / 128) > (long long)INT_MAX || bh * ((Nkv + 127) / 128) > INT_MAX)
         return FA_ERR_SHAPE;
@@ -219,6 +220,12 @@ int check_backward(const void *q, const void *k, const void *v, const void *o, c
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
         return FA_ERR_UNSUPPORTED;
     return FA_OK;
+}
+
+// The float32 backward has kernels of its own (fp32 products throughout).
+hipError_t launch_backward_any(const teaf::BwdArgs &a, hipStream_t s)
+{
+    return a.dtype == FA_F32 ? teaf::launch_backward32(a, s) : teaf::launch_backward(a, s);
 }
 
 }  // namespace
@@ -243,7 +250,7 @@ int fa_backward(const void *q, const void *k, const void *v, const void *o, cons
     const int gc = uses_g ? std::min(n_global, Nkv) : 0;
     teaf::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, scale, mask_mode, wc,
                     gc, dtype, workspace, nullptr};
-    return hip_status(teaf::launch_backward(a, (hipStream_t)stream));
+    return hip_status(launch_backward_any(a, (hipStream_t)stream));
 }
 
 int fa_backward_block_sparse(const void *q, const void *k, const void *v, const void *o,
@@ -261,7 +268,7 @@ int fa_backward_block_sparse(const void *q, const void *k, const void *v, const 
     if ((long long)Nq > most || (long long)Nkv > most) return FA_ERR_UNSUPPORTED;
     teaf::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, scale,
                     teaf::kMaskBlockSparse, 0, 0, dtype, workspace, layout};
-    return hip_status(teaf::launch_backward(a, (hipStream_t)stream));
+    return hip_status(launch_backward_any(a, (hipStream_t)stream));
 }
 
 int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
