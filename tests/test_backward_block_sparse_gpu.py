@@ -20,6 +20,7 @@ import tiled_exact_attention_forward_amd as fa
 import workloads
 from gpu_util import check_grads, f64, to_dev
 from pins import block_mask
+from test_block_sparse_gpu import NMAX, longest_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +128,27 @@ def test_backward_block_sparse_full_size():
                                                  lay.numpy(), w["block"])
     check_per_head(got, ref, w["dtype"], "blocksparse_bf16", (inp["q"], inp["k"], inp["v"], do),
                    scale, lay)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("long_side", ["keys", "queries"])
+def test_longest_block_lists(dtype, long_side):
+    """2048 x 128 - 77 keys (the dQ kernel lists up to 2048 key blocks per query block) or
+    query rows (the dK/dV kernel lists up to 2048 query blocks per key block) against 200 on
+    the other side, every element; heads whose short-side block sees nothing must give zero
+    gradients there."""
+    Nq, Nkv = (200, NMAX) if long_side == "keys" else (NMAX, 200)
+    q, k, v = workloads.gen_prefill(1, 2, Nq, Nkv, 64, dtype, 38)
+    do = workloads.gen_dout((1, 2, Nq, 64), dtype, 39)
+    lay = longest_layout(2, 2048, 40, transpose=long_side == "queries")
+    got = run_bwd_bs(q, k, v, do, 0.125, lay)
+    ref = oracle.attention_backward_block_sparse(q, k, v, do, 0.125, lay.numpy(), 128)
+    ln = lay.numpy().astype(bool)
+    for h in range(2):
+        zero_rows = np.repeat(~ln[h].any(axis=1), 128)[:Nq]
+        zero_keys = np.repeat(~ln[h].any(axis=0), 128)[:Nkv]
+        sl = lambda t: t[:, h:h + 1]  # noqa: E731
+        e = check_grads([sl(g) for g in got], [sl(np.asarray(r)) for r in ref], dtype,
+                        f"longest lists {long_side} {dtype} head {h}",
+                        tuple(sl(t) for t in (q, k, v, do)), 0.125, (zero_rows, zero_keys))
+        print("longest lists", long_side, dtype, h, e)

@@ -100,3 +100,36 @@ def test_full_size_every_element():
                                            inp["layout"].numpy(), w["block"])
     e = check(o, lse, ro, rl, w["dtype"], "blocksparse_bf16")
     print("blocksparse_bf16", e)
+
+
+# The longest sequence the block-sparse entry points take is 2048 blocks of 128 positions;
+# 77 short of it, the last key block is partial.
+NMAX = 2048 * 128 - 77
+
+
+def longest_layout(nqb, nkb, seed, transpose=False):
+    """Layout [2, nqb, nkb] for one short side (2 blocks) against 2048 blocks on the other.
+    Head 0: one short-side block sees every long-side block (a full 2048-entry block list on
+    chip), the other a 3 % spread that includes the first and the last (partial) block.
+    Head 1: one short-side block sees nothing, the other only the last block."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    n = max(nqb, nkb)
+    lay = torch.zeros((2, 2, n), dtype=torch.uint8)
+    lay[0, 0] = (torch.rand(n, generator=g) < 0.03).to(torch.uint8)
+    lay[0, 0, 0] = lay[0, 0, n - 1] = 1
+    lay[0, 1] = 1
+    lay[1, 1, n - 1] = 1
+    return lay.transpose(1, 2).contiguous() if transpose else lay
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_longest_key_block_list(dtype):
+    """Nkv = 2048 x 128 - 77, every element: the query tiles' key-block lists fill every
+    compaction chunk, and rows that see no block give O = 0, LSE = -inf."""
+    q, k, v = workloads.gen_prefill(1, 2, 200, NMAX, 64, dtype, 24)
+    lay = longest_layout(2, 2048, 25)
+    o, lse = run_bs(q, k, v, lay, 0.125)
+    ro, rl = oracle.attention_block_sparse(q, k, v, 0.125, lay.numpy(), 128)
+    e = check(o, lse, ro, rl, dtype, f"longest key-block list {dtype}")
+    assert np.all(f64(o)[0, 1, :128] == 0) and np.all(np.isneginf(f64(lse)[0, 1, :128]))
+    print("longest key-block list", dtype, e)
