@@ -246,7 +246,9 @@ int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_im
  *  lse         [S, H] float32, written; may be NULL.
  *  workspace   device buffer of at least fa_decode_paged_workspace_bytes(...) bytes for
  *              the per-split partial results (split-KV); contents need no initialisation.
- *  Supported: page_size == 256, d == 128, dtype FA_F16 or FA_BF16, H a multiple of 8.
+ *  Supported: page_size == 256, d == 128, dtype FA_F16 or FA_BF16, H a multiple of 8;
+ *  S, H and max_pages_per_seq at most 65535 each (so up to 16,776,960 tokens a sequence:
+ *  these are launch-grid dimensions), else FA_ERR_SHAPE.
  *  The kernels never read page slots at or past seq_lens[s], nor unused table entries.
  *  Page ids outside [0, num_pages) are clamped into the pool (wrong values, never a read
  *  outside it); a length past max_pages_per_seq*page_size counts as that maximum, and a

@@ -83,6 +83,9 @@ def dec(q=P, kp=P, vp=P, pt=P, sl=P, o=P, lse=N, page=256, S=8, H=32, d=128, max
     (dict(page=128), fa.FA_ERR_UNSUPPORTED), (dict(d=64), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
     (dict(H=12), fa.FA_ERR_UNSUPPORTED),
+    # launch-grid dimensions: splits (one per page when there are many), sequences, heads
+    (dict(maxp=65536), fa.FA_ERR_SHAPE), (dict(S=65536), fa.FA_ERR_SHAPE),
+    (dict(H=65536), fa.FA_ERR_SHAPE),
     (dict(ws=N), fa.FA_ERR_WORKSPACE), (dict(wsb=16), fa.FA_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x1004)), fa.FA_ERR_WORKSPACE),
     (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
@@ -102,7 +105,7 @@ def dec_noalloc(q=P, kp=P, vp=P, pt=P, sl=P, o=P, lse=N, page=256, S=8, H=32, d=
     (dict(S=0), fa.FA_ERR_SHAPE), (dict(maxp=0), fa.FA_ERR_SHAPE),
     (dict(page=128), fa.FA_ERR_UNSUPPORTED), (dict(d=64), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(H=12), fa.FA_ERR_UNSUPPORTED),
-    (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
+    (dict(scale=float("nan")), fa.FA_ERR_SHAPE), (dict(maxp=65536), fa.FA_ERR_SHAPE),
     # partials beyond the 16 MiB static array, even at the longest split (256 tokens), which
     # these sizes pick: 64 x 64 x 64 pages take 135 MB, 32 x 32 x 64 pages 33.8 MB
     (dict(S=64, H=64, maxp=64), fa.FA_ERR_SCRATCH),

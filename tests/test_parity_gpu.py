@@ -134,3 +134,27 @@ def test_decode_ragged_lengths(dtype, lens, max_len):
     ro, rl = oracle.decode_paged(inp["q"], inp["k_pages"], inp["v_pages"], inp["page_table"],
                                  inp["seq_lens"], scale)
     check(o, lse, ro, rl, dtype, f"decode {dtype} {lens}")
+
+
+@pytest.mark.timeout(600)
+def test_decode_longest_sequence():
+    """The longest sequence decode takes: 65535 pages of 256 tokens, so 65535 splits in the
+    split pass's launch grid and 65535 partial results per head in the combine. The table
+    maps its pages at random onto the 97 full pages of a cache drawn by the usual recipe
+    (pages shared between positions, as a prefix cache shares them), so the pool stays
+    small; a short sequence shares the launch."""
+    maxp = 65535
+    _, inp = workloads.gen_workload("decode_f16", dtype="f16", lens=[97 * 256, 300], S=2, H=8,
+                                    max_len=97 * 256)
+    g = torch.Generator("cpu").manual_seed(72)
+    full = inp["page_table"][0, :97]
+    pt = torch.full((2, maxp), -1, dtype=torch.int32)
+    pt[0] = full[torch.randint(0, 97, (maxp,), generator=g)]
+    pt[1, :2] = inp["page_table"][1, :2]
+    inp = dict(inp, page_table=pt, seq_lens=torch.tensor([maxp * 256, 300], dtype=torch.int32))
+    scale = workloads.default_scale(128)
+    o, lse = run_decode(inp, scale)
+    ro, rl = oracle.decode_paged(inp["q"], inp["k_pages"], inp["v_pages"], pt, inp["seq_lens"],
+                                 scale)
+    e = check(o, lse, ro, rl, "f16", "decode, longest sequence")
+    print("decode longest sequence", e)

@@ -328,7 +328,11 @@ int check_decode(const void *q, const void *k_pages, const void *v_pages,
     if (page_size != 256 || d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (H % teaf::kDecodeHeads != 0) return FA_ERR_UNSUPPORTED;
-    if (num_seqs > 65535 || H / teaf::kDecodeHeads > 65535) return FA_ERR_SHAPE;
+    // Launch grids: the split pass is (H / heads, splits, num_seqs), where the splits of the
+    // longest sequence the table allows number max_pages_per_seq whenever there are more
+    // than 2048 of them (one per 256-token page); the combine pass is (num_seqs, H). A grid
+    // dimension past x takes at most 65535.
+    if (num_seqs > 65535 || H > 65535 || max_pages_per_seq > 65535) return FA_ERR_SHAPE;
     if ((long long)num_pages * page_size * H * d > (long long)1 << 40) return FA_ERR_SHAPE;
     if ((long long)max_pages_per_seq * page_size > (1ll << 30)) return FA_ERR_SHAPE;
     if (!(scale == scale)) return FA_ERR_SHAPE;
