@@ -92,7 +92,10 @@ typedef enum {
  *              accumulator are float32 for every dtype; for fp16/bf16 the probabilities
  *              are rounded to the input dtype before the product with V.
  *  Supported: d in {64, 128}; any B, H, Nq, Nkv >= 1 (no padding needed; tails are
- *  masked inside the kernel); B*H < 2^31 and every tensor < 2^31 elements per (b, h).
+ *  masked inside the kernel); B*H*ceil(Nq/128) < 2^24 (workgroups of 256 threads, whose
+ *  count a dispatch holds in 32 bits of work-items; the backward also needs
+ *  B*H*ceil(Nkv/128) < 2^24, chunked prefill num_seqs*H*ceil(Qmax/128) < 2^24) and every
+ *  tensor < 2^31 elements per (b, h); else FA_ERR_SHAPE.
  *  q, k, v, o need 16-byte alignment.
  */
 int fa_forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
@@ -184,7 +187,8 @@ int fa_backward_block_sparse(const void *q, const void *k, const void *v, const 
  *
  *  o_a, o_b, o   [rows, d] dtype (o may alias o_a or o_b)
  *  lse_a, lse_b, lse  [rows] float32, natural log (lse may alias lse_a or lse_b)
- *  Supported: d in {64, 128}; dtype FA_F32, FA_F16, FA_BF16; rows >= 1; o_a, o_b, o
+ *  Supported: d in {64, 128}; dtype FA_F32, FA_F16, FA_BF16; rows >= 1 and
+ *  rows * d * sizeof(dtype) / 16 <= 2^32 - 256 (one thread per 16 bytes of a row); o_a, o_b, o
  *  16-byte aligned. Arithmetic in float32; o is rounded to dtype once.
  */
 int fa_merge_lse(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b,

@@ -61,6 +61,8 @@ def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nkv=8, d=64, scale=0.125, mas
     (dict(scale=float("nan")), fa.FA_ERR_SHAPE),
     (dict(q=ctypes.c_void_p(0x1008)), fa.FA_ERR_UNSUPPORTED),
     (dict(B=1 << 16, H=1 << 16), fa.FA_ERR_SHAPE),
+    # 2^24 workgroups of 256 threads: one work-item past a dispatch's 32-bit grid
+    (dict(B=1 << 16, H=256, Nq=128, Nkv=128), fa.FA_ERR_SHAPE),
 ])
 def test_forward_rejects_before_launch(kw, status):
     assert fwd(**kw) == status
@@ -225,6 +227,7 @@ def mrg(oa=P, la=P, ob=P, lb=P, o=P, l=P, rows=10, d=128, dtype=2):
     (dict(oa=N), fa.FA_ERR_NULL), (dict(lb=N), fa.FA_ERR_NULL), (dict(o=N), fa.FA_ERR_NULL),
     (dict(l=N), fa.FA_ERR_NULL), (dict(rows=0), fa.FA_ERR_SHAPE),
     (dict(rows=1 << 41), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(rows=1 << 28), fa.FA_ERR_SHAPE),  # bf16 d 128: 16 threads a row, 2^24 workgroups
     (dict(dtype=4), fa.FA_ERR_UNSUPPORTED), (dict(ob=ctypes.c_void_p(0x1004)),
                                              fa.FA_ERR_UNSUPPORTED),
 ])

@@ -13,6 +13,16 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workgroups of a one-dimensional launch of 256-thread workgroups: a dispatch counts its
+// grid in work-items with 32 bits.
+constexpr long long kMaxWorkgroups1D = (1ll << 32) / 256 - 1;
+
+// Workgroups of the merge launch: 16 bytes of a row per thread.
+long long merge_workgroups(long long rows, int d, int elem)
+{
+    return (rows * (d * elem / 16) + 255) / 256;
+}
+
 thread_local hipError_t g_last_hip = hipSuccess;
 
 int hip_status(hipError_t e)
@@ -64,7 +74,7 @@ int check_forward(const void *q, const void *k, const void *v, void *o, float *l
     if (mask_mode == FA_MASK_PREFIX_LM && n_global < 0) return FA_ERR_SHAPE;
     const long long bh = (long long)B * H;
     const long long nqt = (Nq + 127) / 128;
-    if (bh * nqt > (long long)INT_MAX) return FA_ERR_SHAPE;
+    if (bh * nqt > kMaxWorkgroups1D) return FA_ERR_SHAPE;
     if ((long long)Nq * d > (long long)INT_MAX || (long long)Nkv * d > (long long)INT_MAX)
         return FA_ERR_SHAPE;
     if (!(scale == scale)) return FA_ERR_SHAPE;  // NaN scale
@@ -106,8 +116,7 @@ int fa_merge_lse(const void *o_a, const float *lse_a, const void *o_b, const flo
     if (rows < 1 || rows > (1ll << 40)) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-    if (rows * (d / (16 / (long long)elem_bytes(dtype))) / 256 >= (long long)UINT_MAX)
-        return FA_ERR_SHAPE;
+    if (merge_workgroups(rows, d, (int)elem_bytes(dtype)) > kMaxWorkgroups1D) return FA_ERR_SHAPE;
     if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
     teaf::MergeArgs a{o_a, lse_a, o_b, lse_b, o, lse, (long)rows, d, dtype};
     return hip_status(teaf::launch_merge(a, (hipStream_t)stream));
@@ -152,6 +161,8 @@ int fa_multimodal_forward(const void *q_img, const void *k_img, const void *v_im
         !aligned16(workspace))
         return FA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * H * n_txt;
+    if (merge_workgroups((long long)rows, d, (int)elem_bytes(dtype)) > kMaxWorkgroups1D)
+        return FA_ERR_SHAPE;
     char *ws = (char *)workspace;
     float *lse_x = (float *)(ws + align256(rows * d * elem_bytes(dtype)));
     st = check_forward(q_txt, k_img, v_img, ws, lse_x, B, H, n_txt, n_img, d, scale,
@@ -178,7 +189,7 @@ int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o
         return FA_ERR_UNSUPPORTED;
     const long long bh = (long long)B * H;
     const long long nqt = (Nq + 127) / 128;
-    if (bh * nqt > (long long)INT_MAX) return FA_ERR_SHAPE;
+    if (bh * nqt > kMaxWorkgroups1D) return FA_ERR_SHAPE;
     if ((long long)Nq * d > (long long)INT_MAX || (long long)Nkv * d > (long long)INT_MAX)
         return FA_ERR_SHAPE;
     if (!(scale == scale)) return FA_ERR_SHAPE;  // NaN scale
@@ -209,7 +220,7 @@ int check_backward(const void *q, const void *k, const void *v, const void *o, c
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     const long long bh = (long long)B * H;
-    if (bh * ((Nq + 127) / 128) > (long long)INT_MAX || bh * ((Nkv + 127) / 128) > INT_MAX)
+    if (bh * ((Nq + 127) / 128) > kMaxWorkgroups1D || bh * ((Nkv + 127) / 128) > kMaxWorkgroups1D)
         return FA_ERR_SHAPE;
     if ((long long)Nq * d > (long long)INT_MAX || (long long)Nkv * d > (long long)INT_MAX)
         return FA_ERR_SHAPE;
@@ -289,7 +300,7 @@ int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
     if (mask_mode == FA_MASK_BAND && window < 0) return FA_ERR_SHAPE;
     if (mask_mode == FA_MASK_PREFIX_LM && n_global < 0) return FA_ERR_SHAPE;
     if (H > 65535 || (long long)max_pages_per_seq * page_size > (1ll << 30)) return FA_ERR_SHAPE;
-    if ((long long)num_seqs * H * ((Qmax + 127) / 128) > (long long)INT_MAX) return FA_ERR_SHAPE;
+    if ((long long)num_seqs * H * ((Qmax + 127) / 128) > kMaxWorkgroups1D) return FA_ERR_SHAPE;
     if (!(scale == scale)) return FA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
         return FA_ERR_UNSUPPORTED;
