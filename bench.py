@@ -32,6 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PAGES_F32_TFLOPS = 0.57     # pages' Ascend 910 fp32 time for the dense shape, as TFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PAGES_BF16_TFLOPS = 1.25    # pages' Ascend 910 bf16 time for this workload, as TFLOP/s
 CSRC = "tiled_exact_attention_forward_amd/csrc/"
@@ -205,6 +207,16 @@ def time_cold(fn, calls, torch, flush_bytes=1 << 30):
     del scratch
     t = np.sort(np.asarray(times))
     return float(np.median(t)), float(t[0]), float(t[min(len(t) - 1, int(0.9 * len(t)))])
+
+
+def peak_fraction(r):
+    """Rate against the datasheet MFMA peak of the workload's own dtype (fp32 inputs run
+    fp32 MFMAs; the pages time the same dense shape in fp32 too)."""
+    if r["w"]["dtype"] == "f32":
+        return dict(frac_f32_peak=round(r["tflops"] / PEAK_F32_TFLOPS, 4),
+                    pages_f32_tflops=PAGES_F32_TFLOPS,
+                    note_f32="fp32 kernels are a plain, untuned path (fp32 products throughout)")
+    return dict(frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4))
 
 
 def bench_prefill(name, steps, warmup, torch, fa, workloads, cold_calls=20):
@@ -481,17 +493,17 @@ def main():
     others = {}
     if not args.only_headline:
         for name in ("dense_f16", "dense_bf16", "causal_bf16", "window_bf16", "band_bf16",
-                     "prefix_bf16", "blocksparse_bf16"):
+                     "prefix_bf16", "blocksparse_bf16", "dense_f32"):
             if name == args.workload:
                 continue
             r = bench_prefill(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch, fa,
                               workloads)
             others[name] = dict(us=round(r["ms"] * 1e3, 2), tflops=round(r["tflops"], 2),
-                                frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
                                 visible_pairs=r["pairs"],
                                 cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
                                 cold_tflops=round(r["cold_tflops"], 2),
                                 tile_count=r["tile_count"])
+            others[name].update(peak_fraction(r))
             print(f"[bench] {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
             del r
@@ -523,16 +535,17 @@ def main():
               f"{r['ms_fused'] * 1e3:.1f} us, unified {r['ms_unified'] * 1e3:.1f} us",
               file=sys.stderr, flush=True)
         del r
-        for name in ("dense_bf16", "causal_bf16", "blocksparse_bf16"):
+        for name in ("dense_bf16", "causal_bf16", "blocksparse_bf16", "dense_f32"):
             r = bench_backward(name, max(10, args.steps // 4), max(3, args.warmup // 4), torch,
                                fa, workloads)
             others["backward_" + name] = dict(
                 us=round(r["ms"] * 1e3, 2), tflops=round(r["tflops"], 2),
-                frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4), visible_pairs=r["pairs"],
+                visible_pairs=r["pairs"],
                 cold_us_median_min_p90=[round(x * 1e3, 2) for x in r["cold_ms"]],
                 cold_tflops=round(r["cold_tflops"], 2),
                 traffic=backward_traffic(name),
                 note="fa_backward (2 kernels); 10*d FLOPs per visible pair")
+            others["backward_" + name].update(peak_fraction(r))
             print(f"[bench] backward {name}: {r['ms'] * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
             del r
@@ -562,6 +575,8 @@ def main():
 
     w = head["w"]
     achieved = head["flops"] / (head["ms"] * 1e-3) / 1e12
+    f32 = w["dtype"] == "f32"
+    peak = PEAK_F32_TFLOPS if f32 else PEAK_BF16_TFLOPS
     kernel_key = f"fwd16_{w['dtype']}_d{w['d']}_mask{w['mask']}_{args.workload}"
     mask_name = {0: "none", 1: "causal", 2: "window+global", 3: "band", 4: "prefix LM",
                  5: "block sparse"}[w["mask"]]
@@ -577,7 +592,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(head["tflops"] / PAGES_BF16_TFLOPS, 2)
-        if args.workload == "dense_bf16" else None,
+        if args.workload == "dense_bf16" else
+        round(head["tflops"] / PAGES_F32_TFLOPS, 2) if args.workload == "dense_f32" else None,
         "dtype": w["dtype"],
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: B={w['B']} H={w['H']} Nq={w['Nq']} "
@@ -586,15 +602,16 @@ def main():
         "cold_cache": {"us_median_min_p90": [round(x * 1e3, 2) for x in head["cold_ms"]],
                        "tflops_median": round(head["cold_tflops"], 3),
                        "note": "L2 and MALL flushed (1 GiB fill) before each timed call"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic(kernel_key),
-                     "kernel": f"fwd16_kernel<{w['dtype']}, d={w['d']}, mask {mask_name}>",
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None if f32 else load_traffic(kernel_key),
+                     "kernel": f"fwd32_kernel<d={w['d']}, mask {mask_name}>" if f32 else
+                     f"fwd16_kernel<{w['dtype']}, d={w['d']}, mask {mask_name}>",
                      "flops_per_launch": head["flops"],
                      "algorithmic_bytes_per_launch": head["bytes"],
                      # the same kernel with L2 and MALL flushed before each call (median)
                      "achieved_cold": round(head["cold_tflops"], 3),
-                     "frac_cold": round(head["cold_tflops"] / PEAK_BF16_TFLOPS, 4)},
+                     "frac_cold": round(head["cold_tflops"] / peak, 4)},
         "cpu_baseline": None if base is None else {
             k: (round(v, 6) if isinstance(v, float) else v) for k, v in base.items()},
         "workloads": others,

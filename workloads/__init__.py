@@ -38,6 +38,8 @@ WORKLOADS = {
                       mask=0, window=0, n_global=0, input_scale=1.0, seed=2),
     "dense_bf16": dict(kind="prefill", B=4, H=32, Nq=1024, Nkv=1024, d=128, dtype="bf16",
                        mask=0, window=0, n_global=0, input_scale=1.0, seed=2),
+    "dense_f32": dict(kind="prefill", B=4, H=32, Nq=1024, Nkv=1024, d=128, dtype="f32",
+                      mask=0, window=0, n_global=0, input_scale=1.0, seed=2),
     "causal_bf16": dict(kind="prefill", B=4, H=32, Nq=4096, Nkv=4096, d=128, dtype="bf16",
                         mask=1, window=0, n_global=0, input_scale=0.5, seed=3),
     "window_bf16": dict(kind="prefill", B=1, H=32, Nq=32768, Nkv=32768, d=128, dtype="bf16",
