@@ -4,7 +4,8 @@ memset, no host synchronisation), so a serving loop can capture them into a HIP 
 paged decode and a chunked prefill against the same cache; every replay is compared bit for
 bit with the eager results on the same inputs, with eager library calls and synchronisations
 between the replays, and with the inputs rewritten in place between replays (the graph must
-read the current contents of its buffers).
+read the current contents of its buffers). A second graph holds the fp32 forward and backward
+and the block-sparse forward and backward.
 """
 import pytest
 import torch
@@ -87,3 +88,58 @@ def test_capture_and_replay():
         torch.cuda.synchronize()
         q.copy_(q2 if rep % 2 == 0 else q_orig)
         want = eager()
+
+
+def test_capture_fp32_and_block_sparse():
+    """The fp32 forward and backward and the block-sparse forward and backward in one graph,
+    replayed against eager results as above."""
+    dev = require_gpu()
+    scale = workloads.default_scale(64)
+    q, k, v = (t.to(dev) for t in workloads.gen_prefill(2, 2, 300, 450, 64, "f32", 55))
+    do = workloads.gen_dout((2, 2, 300, 64), "f32", 56).to(dev)
+    bq, bk, bv = (t.to(dev) for t in workloads.gen_prefill(1, 2, 300, 450, 128, "bf16", 57))
+    bdo = workloads.gen_dout((1, 2, 300, 128), "bf16", 58).to(dev)
+    g = torch.Generator("cpu").manual_seed(59)
+    lay = (torch.rand((2, 3, 4), generator=g) < 0.5).to(torch.uint8).to(dev)
+
+    o, lse = torch.empty_like(q), torch.empty((2, 2, 300), dtype=torch.float32, device=dev)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((fa.fa_backward_workspace_bytes(2, 2, 300),), dtype=torch.uint8,
+                     device=dev)
+    bo, blse = torch.empty_like(bq), torch.empty((1, 2, 300), dtype=torch.float32, device=dev)
+    bgq, bgk, bgv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+    bws = torch.empty((fa.fa_backward_workspace_bytes(1, 2, 300),), dtype=torch.uint8,
+                      device=dev)
+
+    def calls():
+        fa.fa_forward(q, k, v, scale, fa.FA_MASK_BAND, 40, out=o, lse=lse)
+        fa.fa_backward(q, k, v, o, lse, do, scale, fa.FA_MASK_BAND, 40, dq=gq, dk=gk, dv=gv,
+                       workspace=ws)
+        fa.fa_forward_block_sparse(bq, bk, bv, lay, 128, scale, out=bo, lse=blse)
+        fa.fa_backward_block_sparse(bq, bk, bv, bo, blse, bdo, lay, 128, scale, dq=bgq, dk=bgk,
+                                    dv=bgv, workspace=bws)
+
+    outs = (o, lse, gq, gk, gv, bo, blse, bgq, bgk, bgv)
+    calls()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(3.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (got, ref) in enumerate(zip(outs, want)):
+            assert torch.equal(got, ref), (rep, i)
+        fa.fa_forward(q, k, v, scale, fa.FA_MASK_NONE)  # eager work between replays
+        torch.cuda.synchronize()
