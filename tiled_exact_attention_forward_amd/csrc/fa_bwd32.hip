@@ -34,7 +34,7 @@ template <int MASK>
 __device__ __forceinline__ bool block_sees(int ip0, int ip1, int k0, int k1, int W, int G)
 {
     if (MASK == 1) return ip1 >= k0;
-    if (MASK == 2) return (k0 < G && ip1 >= k0) || (ip1 >= k0 && ip0 - k1 < W);
+    if (MASK == 2) return ip1 >= k0 && (k0 < G || ip0 - k1 < W);  // global or window key
     if (MASK == 3) return ip1 + W >= k0 && ip0 - W <= k1;
     if (MASK == 4) return k0 < G || ip1 >= k0;
     return true;
