@@ -426,8 +426,20 @@ def cpu_baseline(res, budget_s):
     what = (f"the whole workload ({total_rows} query rows), run {reps} times" if n == total_rows
             else f"{n} of {total_rows} query rows (evenly spaced over batch, head, row)")
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
-                kind="oracle", seconds=dt * reps,
+                kind="oracle", seconds=dt * reps, cpu_model=host_cpu_model(),
                 sample=f"{what} of {res['workload']}, fp64 C oracle with OpenMP")
+
+
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
