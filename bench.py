@@ -468,7 +468,7 @@ def main():
     MIN_WARM_S = args.warm_seconds
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the attention path has no multi-GPU sharding in this build)", file=sys.stderr)
+              "(the library has no multi-GPU sharding)", file=sys.stderr)
         sys.exit(2)
 
     import torch

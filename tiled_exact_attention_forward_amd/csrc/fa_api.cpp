@@ -46,7 +46,7 @@ const char *fa_status_string(int status)
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "a size argument is out of range";
-    case FA_ERR_UNSUPPORTED: return "valid arguments that this build does not support";
+    case FA_ERR_UNSUPPORTED: return "valid arguments that the library does not support";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "the HIP runtime rejected a launch";
     case FA_ERR_SCRATCH:
