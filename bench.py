@@ -215,7 +215,7 @@ def peak_fraction(r):
     if r["w"]["dtype"] == "f32":
         return dict(frac_f32_peak=round(r["tflops"] / PEAK_F32_TFLOPS, 4),
                     pages_f32_tflops=PAGES_F32_TFLOPS,
-                    note_f32="fp32 kernels are a plain, untuned path (fp32 products throughout)")
+                    note_f32="fp32 kernels are a plain path (fp32 products throughout)")
     return dict(frac_bf16_peak=round(r["tflops"] / PEAK_BF16_TFLOPS, 4))
 
 

@@ -142,7 +142,7 @@ int fa_forward_block_sparse(const void *q, const void *k, const void *v, void *o
  *                 rounded to dtype) with float32 accumulation; the outputs are rounded
  *                 once at the end. FA_F32: float32 operands and products throughout (the
  *                 pages recommend fp32 or bf16 for training: ops-transformer article on
- *                 gitcode.csdn.net, section 三.2); a plain, untuned pair of kernels.
+ *                 gitcode.csdn.net, section 三.2); a plain pair of kernels.
  *  workspace      device buffer of at least fa_backward_workspace_bytes(B, H, Nq) bytes
  *                 (per-row D and log2-scaled LSE, grouped by 32-row tile); contents need no
  *                 initialisation; 16-byte aligned.

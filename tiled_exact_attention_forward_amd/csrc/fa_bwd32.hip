@@ -8,7 +8,8 @@
 // The pages recommend fp32 or bf16 for training (ops-transformer article on
 // gitcode.csdn.net, section 三.2 "精度与性能平衡"). These kernels take fp32 operands
 // throughout (v_mfma_f32_32x32x2f32: true fp32 products, no rounding of P or dS) and, like
-// the fp32 forward, are a plain single-buffered form: a parity path, not tuned.
+// the fp32 forward, are plain kernels: a parity path, not tuned beyond loading each tile
+// one tile ahead (through registers into the second of two LDS stages).
 //  * bwd32_dq_kernel runs first: a workgroup owns 128 query rows (4 waves x 32) with Q and
 //    dO in registers, forms the row statistics (L_i = LSE_i log2 e, +inf for a row without
 //    a visible key; D_i) and stores them per 32-row tile as [32 L, 32 -D] (the 16-bit
@@ -40,23 +41,6 @@ __device__ __forceinline__ bool block_sees(int ip0, int ip1, int k0, int k1, int
     return true;
 }
 
-// Copies rows [r0, r0 + 32) of a [rows, D] fp32 matrix into LDS (row pitch D + 1 floats);
-// rows at or past n read as zero.
-template <int D>
-__device__ __forceinline__ void tile_to_lds(float *dst, const float *__restrict__ src, int r0,
-                                            int n, int tid)
-{
-    constexpr int KP = D + 1, RC = D / 4, CPT = 32 * RC / 256;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-        const int id = tid + u * 256, r = id / RC, cc = id % RC;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (r0 + r < n) x = *(const f32x4 *)(src + (size_t)(r0 + r) * D + 4 * cc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[r * KP + 4 * cc + e] = x[e];
-    }
-}
-
 // Stores a 32 x D result held as D/32 transposed 32 x 32 fragments (lane (g, i): row i,
 // columns db*32 + mfma32_pos(e, g)) times f into the row at out.
 template <int D>
@@ -81,8 +65,9 @@ __global__ __launch_bounds__(256) void bwd32_dq_kernel(
     int W, int G, int nqt, const uint8_t *__restrict__ layout, int H)
 {
     constexpr int BM = 128, BN = 32, KP = D + 1, NKK = D / 2, NDB = D / 32;
-    __shared__ float ks[BN * KP];
-    __shared__ float vs[BN * KP];
+    constexpr int RC = D / 4, CPT = BN * RC / 256;  // 16-byte pieces of a tile per thread
+    constexpr int STAGE = 2 * BN * KP;              // one stage: the K rows, then the V rows
+    extern __shared__ float stages[];               // two stages
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
@@ -120,44 +105,84 @@ __global__ __launch_bounds__(256) void bwd32_dq_kernel(
         const int nkb = (Nkv + kSparseBlock - 1) / kSparseBlock;
         lrow = layout + ((size_t)(bh % H) * nqt + q0 / kSparseBlock) * nkb;
     }
-    for (int n = 0; n < ntiles; ++n) {
-        const int kv0 = (n < na ? tr.a0 + n : tr.b0 + (n - na)) * BN;
-        if (MASK == kBlockSparse && lrow[kv0 / kSparseBlock] == 0) continue;  // whole workgroup
-        __syncthreads();  // the previous tile's readers are done
-        tile_to_lds<D>(ks, K + kvbase, kv0, Nkv, tid);
-        tile_to_lds<D>(vs, V + kvbase, kv0, Nkv, tid);
-        __syncthreads();
-        if (wrow0 >= Nq) continue;
-        if (MASK != 0 && MASK != kBlockSparse &&
-            !block_sees<MASK>(wrow0 + delta, wrow0 + 31 + delta, kv0, kv0 + BN - 1, W, G))
-            continue;
-
-        f32x16 s, dp;
+    auto tile_of = [&](int n) { return n < na ? tr.a0 + n : tr.b0 + (n - na); };
+    // The first tile position at or after n that the workgroup visits (block sparse: the
+    // key blocks its layout row marks visible).
+    auto next_tile = [&](int n) {
+        if (MASK == kBlockSparse)
+            while (n < ntiles && lrow[tile_of(n) * BN / kSparseBlock] == 0) ++n;
+        return n;
+    };
+    // A tile's K and V rows go to registers one tile ahead (their loads in flight during the
+    // current tile's products), then into the other LDS stage; keys at or past Nkv are zero.
+    f32x4 kpre[CPT], vpre[CPT];
+    auto fetch = [&](int n) {
+        const int kv0 = tile_of(n) * BN;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[li * KP + 2 * kk + g], qf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[li * KP + 2 * kk + g], gf[kk], dp, 0, 0,
-                                                      0);
+        for (int u = 0; u < CPT; ++u) {
+            const int id = tid + u * 256, r = id / RC, cc = id % RC;
+            const size_t at = kvbase + (size_t)(kv0 + r) * D + 4 * cc;
+            const bool in = kv0 + r < Nkv;
+            kpre[u] = in ? *(const f32x4 *)(K + at) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vpre[u] = in ? *(const f32x4 *)(V + at) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        // dS^T in place of S^T: lane (g, i) holds keys kv0 + mfma32_pos(e, g) of row i.
+    };
+    auto stash = [&](float *st) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int key = kv0 + mfma32_pos(e, g);
-            const bool vis = key < Nkv && key_visible<MASK>(ip, key, W, G);
-            const float p = vis ? fast_exp2(s[e] * c - Lrow) : 0.f;
-            s[e] = p * (dp[e] - Drow);
+        for (int u = 0; u < CPT; ++u) {
+            const int id = tid + u * 256, r = id / RC, cc = id % RC;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                st[r * KP + 4 * cc + e] = kpre[u][e];
+                st[BN * KP + r * KP + 4 * cc + e] = vpre[u][e];
+            }
         }
-        // dQ^T += K^T dS^T, one key per lane half and step.
+    };
+    int n = next_tile(0), stage = 0;
+    if (n < ntiles) {
+        fetch(n);
+        stash(stages);
+    }
+    __syncthreads();
+    while (n < ntiles) {
+        const int kv0 = tile_of(n) * BN, nn = next_tile(n + 1);
+        if (nn < ntiles) fetch(nn);
+        const float *ks = stages + stage * STAGE, *vs = ks + BN * KP;
+        if (wrow0 < Nq &&
+            (MASK == 0 || MASK == kBlockSparse ||
+             block_sees<MASK>(wrow0 + delta, wrow0 + 31 + delta, kv0, kv0 + BN - 1, W, G))) {
+            f32x16 s, dp;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int kr = mfma32_pos(e, g);
+            for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[kr * KP + db * 32 + li], s[e],
-                                                              dq[db], 0, 0, 0);
+            for (int kk = 0; kk < NKK; ++kk) {
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[li * KP + 2 * kk + g], qf[kk], s, 0,
+                                                         0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[li * KP + 2 * kk + g], gf[kk], dp,
+                                                          0, 0, 0);
+            }
+            // dS^T in place of S^T: lane (g, i) holds keys kv0 + mfma32_pos(e, g) of row i.
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = kv0 + mfma32_pos(e, g);
+                const bool vis = key < Nkv && key_visible<MASK>(ip, key, W, G);
+                const float p = vis ? fast_exp2(s[e] * c - Lrow) : 0.f;
+                s[e] = p * (dp[e] - Drow);
+            }
+            // dQ^T += K^T dS^T, one key per lane half and step.
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int kr = mfma32_pos(e, g);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[kr * KP + db * 32 + li],
+                                                                  s[e], dq[db], 0, 0, 0);
+            }
         }
+        if (nn < ntiles) stash(stages + (stage ^ 1) * STAGE);
+        __syncthreads();  // the next stage is written, this one's readers are done
+        stage ^= 1;
+        n = nn;
     }
     if (live) store_row<D>(dQ + qbase + (size_t)row * D, dq, scale, g);
 }
@@ -171,9 +196,9 @@ __global__ __launch_bounds__(256) void bwd32_dkdv_kernel(
 {
     constexpr int BK = 128, KP = D + 1, NKK = D / 2, NDB = D / 32;
     static_assert(BK == kSparseBlock, "a workgroup's keys are one block of the sparse layout");
-    __shared__ float qs[32 * KP];
-    __shared__ float gs[32 * KP];
-    __shared__ float stat[64];  // the tile's L values, then its -D values
+    constexpr int RC = D / 4, CPT = 32 * RC / 256;  // 16-byte pieces of a tile per thread
+    constexpr int STAGE = 2 * 32 * KP + 64;  // Q rows, dO rows, the tile's L then -D values
+    extern __shared__ float stages[];        // two stages
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
@@ -206,51 +231,93 @@ __global__ __launch_bounds__(256) void bwd32_dkdv_kernel(
         lcol = layout + (size_t)(bh % H) * nqb * nkb + k0 / kSparseBlock;
     }
     const int kend = min(k0 + BK, Nkv) - 1;
-    for (int t = 0; t < nt32; ++t) {
+    // Whether the workgroup visits 32-row tile t, and the first such tile at or after t.
+    auto visits = [&](int t) {
         const int r0 = 32 * t;
-        if (MASK == kBlockSparse) {
-            if (lcol[(size_t)(r0 / kSparseBlock) * nkb] == 0) continue;  // whole workgroup
-        } else if (MASK != 0 &&
-                   !block_sees<MASK>(r0 + delta, min(r0 + 31, Nq - 1) + delta, k0, kend, W, G)) {
-            continue;
+        if (MASK == kBlockSparse) return lcol[(size_t)(r0 / kSparseBlock) * nkb] != 0;
+        return MASK == 0 ||
+               block_sees<MASK>(r0 + delta, min(r0 + 31, Nq - 1) + delta, k0, kend, W, G);
+    };
+    auto next_tile = [&](int t) {
+        while (t < nt32 && !visits(t)) ++t;
+        return t;
+    };
+    // A tile's Q and dO rows and its statistics go to registers one tile ahead (their loads in
+    // flight during the current tile's products), then into the other LDS stage; rows at or
+    // past Nq are zero.
+    f32x4 qpre[CPT], gpre[CPT];
+    float spre = 0.f;
+    auto fetch = [&](int t) {
+        const int r0 = 32 * t;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int id = tid + u * 256, r = id / RC, cc = id % RC;
+            const size_t at = qbase + (size_t)(r0 + r) * D + 4 * cc;
+            const bool in = r0 + r < Nq;
+            qpre[u] = in ? *(const f32x4 *)(Q + at) : f32x4{0.f, 0.f, 0.f, 0.f};
+            gpre[u] = in ? *(const f32x4 *)(dO + at) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();  // the previous tile's readers are done
-        tile_to_lds<D>(qs, Q + qbase, r0, Nq, tid);
-        tile_to_lds<D>(gs, dO + qbase, r0, Nq, tid);
-        if (tid < 64) stat[tid] = st[((size_t)bh * nt32 + t) * 64 + tid];
-        __syncthreads();
-        if (wk0 >= Nkv) continue;
-
-        f32x16 s, dp;
+        if (tid < 64) spre = st[((size_t)bh * nt32 + t) * 64 + tid];
+    };
+    auto stash = [&](float *sg) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+        for (int u = 0; u < CPT; ++u) {
+            const int id = tid + u * 256, r = id / RC, cc = id % RC;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[li * KP + 2 * kk + g], kf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[li * KP + 2 * kk + g], vf[kk], dp, 0, 0,
-                                                      0);
-        }
-        // P and dS: lane (g, i) holds rows r0 + mfma32_pos(e, g) of key i.
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = mfma32_pos(e, g), rw = r0 + r;
-            const bool vis = live && rw < Nq && key_visible<MASK>(rw + delta, key, W, G);
-            const float p = vis ? fast_exp2(s[e] * c - stat[r]) : 0.f;
-            s[e] = p;
-            dp[e] = p * (dp[e] + stat[32 + r]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS, one row per lane half and step.
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = mfma32_pos(e, g);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[r * KP + db * 32 + li], s[e],
-                                                              dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[r * KP + db * 32 + li], dp[e],
-                                                              dk[db], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+                sg[r * KP + 4 * cc + e] = qpre[u][e];
+                sg[32 * KP + r * KP + 4 * cc + e] = gpre[u][e];
             }
         }
+        if (tid < 64) sg[2 * 32 * KP + tid] = spre;
+    };
+    int t = next_tile(0), stage = 0;
+    if (t < nt32) {
+        fetch(t);
+        stash(stages);
+    }
+    __syncthreads();
+    while (t < nt32) {
+        const int r0 = 32 * t, tn = next_tile(t + 1);
+        if (tn < nt32) fetch(tn);
+        const float *qs = stages + stage * STAGE, *gs = qs + 32 * KP, *stat = gs + 32 * KP;
+        if (wk0 < Nkv) {
+            f32x16 s, dp;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[li * KP + 2 * kk + g], kf[kk], s, 0,
+                                                         0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[li * KP + 2 * kk + g], vf[kk], dp,
+                                                          0, 0, 0);
+            }
+            // P and dS: lane (g, i) holds rows r0 + mfma32_pos(e, g) of key i.
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = mfma32_pos(e, g), rw = r0 + r;
+                const bool vis = live && rw < Nq && key_visible<MASK>(rw + delta, key, W, G);
+                const float p = vis ? fast_exp2(s[e] * c - stat[r]) : 0.f;
+                s[e] = p;
+                dp[e] = p * (dp[e] + stat[32 + r]);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS, one row per lane half and step.
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = mfma32_pos(e, g);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[r * KP + db * 32 + li],
+                                                                  s[e], dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[r * KP + db * 32 + li],
+                                                                  dp[e], dk[db], 0, 0, 0);
+                }
+            }
+        }
+        if (tn < nt32) stash(stages + (stage ^ 1) * STAGE);
+        __syncthreads();  // the next stage is written, this one's readers are done
+        stage ^= 1;
+        t = tn;
     }
     if (live) {
         store_row<D>(dK + kvbase + (size_t)key * D, dk, scale, g);
@@ -263,16 +330,27 @@ hipError_t launch_bwd32(const BwdArgs &a, hipStream_t s)
 {
     const float c = a.scale * kLog2e;
     const int nqt = (a.Nq + 127) / 128, nkt = (a.Nkv + 127) / 128;
-    // dQ first: it also writes the row statistics the dK/dV kernel reads.
-    hipLaunchKernelGGL((bwd32_dq_kernel<D, MASK>), dim3((unsigned)((long)nqt * a.B * a.H)),
-                       dim3(256), 0, s, (const float *)a.q, (const float *)a.k,
+    // dQ first: it also writes the row statistics the dK/dV kernel reads. Its two LDS stages
+    // of K and V rows take 66 KB at d 128.
+    constexpr int lds_dq = 2 * 2 * 32 * (D + 1) * (int)sizeof(float);
+    auto kq = bwd32_dq_kernel<D, MASK>;
+    hipError_t e = hipFuncSetAttribute((const void *)kq,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_dq);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kq, dim3((unsigned)((long)nqt * a.B * a.H)),
+                       dim3(256), lds_dq, s, (const float *)a.q, (const float *)a.k,
                        (const float *)a.v, (const float *)a.dout, (const float *)a.o, a.lse,
                        (float *)a.workspace, (float *)a.dq, a.Nq, a.Nkv, c, a.scale, a.window,
                        a.n_global, nqt, a.layout, a.H);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd32_dkdv_kernel<D, MASK>), dim3((unsigned)((long)nkt * a.B * a.H)),
-                       dim3(256), 0, s, (const float *)a.q, (const float *)a.k,
+    constexpr int lds_dkdv = 2 * (2 * 32 * (D + 1) + 64) * (int)sizeof(float);
+    auto kkv = bwd32_dkdv_kernel<D, MASK>;
+    e = hipFuncSetAttribute((const void *)kkv, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lds_dkdv);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kkv, dim3((unsigned)((long)nkt * a.B * a.H)),
+                       dim3(256), lds_dkdv, s, (const float *)a.q, (const float *)a.k,
                        (const float *)a.v, (const float *)a.dout, (const float *)a.workspace,
                        (float *)a.dk, (float *)a.dv, a.Nq, a.Nkv, c, a.scale, a.window,
                        a.n_global, nkt, a.layout, a.H);
