@@ -8,34 +8,25 @@ compiler's hazard recognizer does not see. The source covers the two hazards its
   * an MFMA's result must be complete before other instructions read it (up to 18 wait
     states for 16 passes): the accumulators go through padding of 24 wait states after the
     loop, in statements that take them as operands.
-These tests compile the file with the library's flags and check, in every dK/dV
-instantiation, that the padding is where the source means it to be: before every
-AGPR-accumulating MFMA, between the last of them and the first instruction that reads an
-accumulator, and that the loop holds no copies between the register files. The compiler
-may also copy an accumulator on its own (a move between AGPRs when it splits a live range);
-placed right after an inline MFMA, such a copy reads the register before the MFMA has
-written it, so every instruction that reads an AGPR is checked against the last MFMA that
-writes it, in program order.
+These tests read the file's assembly (compiled with the library's flags,
+conftest.device_asm) and check, in every dK/dV instantiation, that the padding is where the
+source means it to be: before every AGPR-accumulating MFMA, between the last of them and the
+first instruction that reads an accumulator, and that the loop holds no copies between the
+register files. The compiler may also copy an accumulator on its own (a move between AGPRs
+when it splits a live range); placed right after an inline MFMA, such a copy reads the
+register before the MFMA has written it, so every instruction that reads an AGPR is checked
+against the last MFMA that writes it, in program order.
 """
-import os
 import re
-import subprocess
 
 import pytest
-
-from tiled_exact_attention_forward_amd import build as b
 
 MIN_WAIT_STATES = 19
 
 
 @pytest.fixture(scope="module")
-def asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("bwd_asm") / "fa_bwd.s"
-    cmd = ["hipcc", *b.FLAGS, *b.EXTRA.get("fa_bwd.hip", []), "--cuda-device-only", "-S",
-           os.path.join(b.CSRC, "fa_bwd.hip"), "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-3000:]
-    return out.read_text().split("\n")
+def asm(device_asm):
+    return device_asm["fa_bwd.hip"]
 
 
 def kernels(lines):
