@@ -127,14 +127,14 @@ __global__ __launch_bounds__(256) void bwd32_dq_kernel(
             vpre[u] = in ? *(const f32x4 *)(V + at) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
-    auto stash = [&](float *st) {
+    auto stash = [&](float *sk) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int id = tid + u * 256, r = id / RC, cc = id % RC;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                st[r * KP + 4 * cc + e] = kpre[u][e];
-                st[BN * KP + r * KP + 4 * cc + e] = vpre[u][e];
+                sk[r * KP + 4 * cc + e] = kpre[u][e];
+                sk[BN * KP + r * KP + 4 * cc + e] = vpre[u][e];
             }
         }
     };
